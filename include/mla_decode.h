@@ -1,0 +1,256 @@
+/*
+ * mla_decode.h - C ABI of a gfx950 (MI355X) library for weight-absorbed
+ * Multi-head Latent Attention (MLA) decode over a paged latent KV cache.
+ *
+ * What is computed (each entry point below cites the passage it implements):
+ *
+ *   For query row n of request b and head h, with cache rows c_t of the
+ *   request's tokens t < L_b (each row: 512 latent values, then 64 rope values):
+ *     s_t   = sm_scale * (q_nope[n,h,:] . c_t[0:512] + q_rope[n,h,:] . c_t[512:576])
+ *     out   = sum_t softmax(s)_t * c_t[0:512]        (the latent is also the value)
+ *     lse   = ln sum_t exp(s_t)                      (natural log)
+ *   q_nope is the absorbed query: the per-head no-rope query already multiplied
+ *   by W_UK, as in section 2.1 of the sglang-jax MLA gap page and the forward
+ *   path of the SGLang v0.3 MLA page. The two-path score, the online softmax
+ *   and the latent-as-value product are the core loop of the MLA kernel in
+ *   section 2.4 of the gap page.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer named *_d is device memory; *_h is host memory. The caller
+ *     owns all memory. The library allocates nothing and never synchronises
+ *     the device; all device work is enqueued on the caller's stream, passed as
+ *     a hipStream_t cast to void* (NULL = the null stream).
+ *   - Arguments are validated on the host before anything is enqueued. A
+ *     non-zero return means nothing was enqueued (MLA_ERR_HIP aside: a launch
+ *     the runtime rejected).
+ *   - The library holds no state besides a cached device-property query.
+ *   - Calls that share a workspace and overlap on different streams race.
+ */
+#ifndef MLA_DECODE_H_
+#define MLA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1,         /* NULL pointer, bad size, malformed CSR arrays */
+    MLA_ERR_UNSUPPORTED = 2,         /* a shape or dtype this build does not implement */
+    MLA_ERR_WORKSPACE_TOO_SMALL = 3, /* a caller buffer is smaller than required */
+    MLA_ERR_HIP = 4,                 /* the HIP runtime reported an error */
+    MLA_ERR_PLAN_MISMATCH = 5        /* the plan was built for other parameters */
+} mla_status;
+
+typedef enum {
+    MLA_DTYPE_BF16 = 0,
+    MLA_DTYPE_FP32 = 1,
+    MLA_DTYPE_FP8_E4M3FN = 2 /* OCP e4m3fn: bias 7, max 448, no infinities */
+} mla_dtype;
+
+typedef struct {
+    int32_t num_heads;        /* H query heads: 16, 32, 64 or 128 */
+    int32_t kv_lora_rank;     /* must be 512 */
+    int32_t qk_rope_head_dim; /* must be 64 */
+    int32_t page_size;        /* tokens per cache page, >= 1 */
+    int32_t kv_dtype;         /* MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3FN */
+    int32_t out_dtype;        /* MLA_DTYPE_BF16, or MLA_DTYPE_FP32 for the fp32 mode:
+                                 the softmax probabilities and the output are never
+                                 rounded to bf16 */
+    int32_t num_cus;          /* compute units to balance over; 0 = ask the device */
+    int32_t max_splits;       /* cap on KV chunks per query row; 0 = library default,
+                                 1 = never split */
+} mla_decode_params;
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_string(int32_t status);
+
+/*
+ * Plan layout. The plan is built on the host and copied verbatim to the start
+ * of the device workspace. It is plain data: tests may read it.
+ */
+#define MLA_PLAN_MAGIC 0x504C4D41u /* "AMLP" */
+#define MLA_PLAN_VERSION 1
+
+typedef struct {
+    uint32_t magic;
+    int32_t version;
+    int32_t num_heads, page_size, kv_dtype, out_dtype;
+    int32_t batch;          /* requests */
+    int32_t num_rows;       /* query rows (qo_indptr[batch]) */
+    int32_t num_items;      /* decode work items = workgroups of the decode launch */
+    int32_t num_merges;     /* query rows whose KV was split into several chunks */
+    int32_t num_partials;   /* partial (out, lse) slots written by split chunks */
+    int32_t chunk_tokens;   /* target chunk length the plan used */
+    int64_t num_page_entries; /* kv_indptr[batch]: entries of kv_indices the batch uses */
+    int64_t items_offset;   /* byte offset of mla_work_item[num_items] */
+    int64_t merges_offset;  /* byte offset of mla_merge_item[num_merges] */
+    int64_t plan_bytes;     /* bytes of the plan itself (header + items + merges) */
+    int64_t partial_out_offset; /* workspace offset of float[num_partials][H][512] */
+    int64_t partial_lse_offset; /* workspace offset of float[num_partials][H] */
+    int64_t workspace_bytes;    /* workspace bytes this plan needs */
+} mla_plan_header;
+
+typedef struct {
+    int32_t row;       /* query row n */
+    int32_t request;   /* request b */
+    int32_t page_base; /* kv_indptr[b]: first entry of b's page list in kv_indices */
+    int32_t kv_begin;  /* first token of the chunk */
+    int32_t kv_end;    /* one past the last token (the request's length for the last chunk) */
+    int32_t partial;   /* -1: write out/lse directly; else the partial slot */
+    int32_t head_begin;
+    int32_t num_heads;
+} mla_work_item;
+
+typedef struct {
+    int32_t row;           /* query row n */
+    int32_t partial_begin; /* its chunks are partial slots [partial_begin, +num_partials) */
+    int32_t num_partials;
+    int32_t reserved;
+} mla_merge_item;
+
+/*
+ * Upper bounds on the host plan buffer and the device workspace for a batch of
+ * up to `batch` requests and `num_rows` query rows with these parameters.
+ * Returns MLA_OK, MLA_ERR_INVALID_ARG or MLA_ERR_UNSUPPORTED.
+ */
+int32_t mla_decode_workspace_size(const mla_decode_params* params, int32_t batch, int32_t num_rows,
+                                  size_t* plan_bytes, size_t* workspace_bytes);
+
+/*
+ * mla_decode_plan - split-KV chunking and balance across compute units.
+ *
+ * The CSR description of a paged, ragged batch and the per-batch plan() that
+ * picks the split-KV chunking and balances long and short requests across the
+ * chip are from the "Paged, ragged batches" paragraph of the SGLang
+ * attention-backends page; splitting the keys of one query across workgroups
+ * and merging by rescaling is Flash-Decoding, in the FlashAttention paragraph
+ * of the same page. A plan is built once per batch and reused by every layer
+ * (the PR 49477 analysis, section 1, reuses its metadata across layers).
+ *
+ *   qo_indptr_h       [batch+1] query rows of each request, or NULL for one row
+ *                     per request (plain decode).
+ *   kv_indptr_h       [batch+1] offsets of each request's page list in kv_indices.
+ *   kv_last_page_len_h [batch] valid tokens in each request's last page, in
+ *                     [1, page_size]; NULL means the last page is full. A request
+ *                     with no pages has length 0 (its output is 0, lse -inf).
+ *   plan_h            caller-owned host buffer (pinned memory is best) of
+ *                     plan_h_bytes; receives mla_plan_header + items + merges.
+ *   workspace_d       device workspace of workspace_bytes, or NULL to build the
+ *                     host plan only. When given, the plan is copied to its
+ *                     start with an asynchronous copy on `stream`: plan_h must
+ *                     stay unchanged until that copy has completed.
+ * The lengths here are upper bounds: mla_decode may clip them further with
+ * kv_lens_d. Returns MLA_OK, MLA_ERR_INVALID_ARG (NULL arrays, decreasing
+ * indptr, last_page_len out of range), MLA_ERR_UNSUPPORTED,
+ * MLA_ERR_WORKSPACE_TOO_SMALL or MLA_ERR_HIP.
+ */
+int32_t mla_decode_plan(const mla_decode_params* params, int32_t batch, const int32_t* qo_indptr_h,
+                        const int32_t* kv_indptr_h, const int32_t* kv_last_page_len_h,
+                        void* plan_h, size_t plan_h_bytes, void* workspace_d,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode - absorbed-MLA attention of every query row over its request's
+ * paged latent tokens, with split-KV partials merged by log-sum-exp.
+ *
+ * Formulas: see the top of this header (two-path score and latent reused as
+ * value: sglang-jax MLA gap page, sections 2.1 and 2.4; the MLA paragraph of the
+ * SGLang attention-backends page; online softmax and split-KV merge: its
+ * FlashAttention paragraph). Returns (out, lse) as the fixed-length FA4 path of
+ * the PR 49477 analysis, section 4, returns them together.
+ *
+ *   plan_h, workspace_d  the plan from mla_decode_plan with the same params, and
+ *                        the workspace it was copied into.
+ *   q_nope_d   bf16 [N, H, 512] absorbed query; element (n, h, d) at
+ *              n*q_nope_stride_n + h*q_nope_stride_h + d (strides in elements,
+ *              multiples of 8, base 16-byte aligned).
+ *   q_rope_d   bf16 [N, H, 64], same conventions. A concatenated [N, H, 576]
+ *              query is passed as q_rope_d = q_nope_d + 512 with equal strides.
+ *   kv_cache_d [num_pages, page_size, 576] of kv_dtype, rows contiguous
+ *              (latent 512, then rope 64); 16-byte aligned.
+ *   kv_scale   fp8 dequantisation scale (cache value = code * kv_scale); must be
+ *              1 for bf16 caches.
+ *   kv_indices_d  int32 page numbers, the CSR column array of the plan's batch.
+ *   kv_lens_d  int32 [batch] token counts known only on the device, or NULL.
+ *              Request b then attends to min(kv_lens_d[b], planned length)
+ *              tokens. This is how the tree-verify suffix uses the compacted
+ *              table: its lengths come from mla_tree_suffix_compact.
+ *   sm_scale   softmax scale applied to the raw scores.
+ *   out_d      [N, H, 512] contiguous, out_dtype.
+ *   lse_d      float [N, H] contiguous (natural log), or NULL.
+ * The library never reads cache rows past a request's length, nor pool rows
+ * outside its page list. Returns MLA_OK, MLA_ERR_INVALID_ARG,
+ * MLA_ERR_UNSUPPORTED, MLA_ERR_PLAN_MISMATCH, MLA_ERR_WORKSPACE_TOO_SMALL or
+ * MLA_ERR_HIP.
+ */
+int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const void* workspace_d,
+                   size_t workspace_bytes, const void* q_nope_d, int64_t q_nope_stride_n,
+                   int64_t q_nope_stride_h, const void* q_rope_d, int64_t q_rope_stride_n,
+                   int64_t q_rope_stride_h, const void* kv_cache_d, float kv_scale,
+                   const int32_t* kv_indices_d, const int32_t* kv_lens_d, float sm_scale,
+                   void* out_d, float* lse_d, void* stream);
+
+/*
+ * mla_merge_states - merge two attention states over disjoint token sets:
+ *   s = ln(e^{s_a} + e^{s_b}),  v = e^{s_a - s} v_a + e^{s_b - s} v_b.
+ * This is the LSE merge of the prefix and suffix results in the cascade of the
+ * PR 49477 analysis (introduction), and the Flash-Decoding rescaling of the
+ * attention-backends page. A state with s = -inf (no tokens) drops out; two
+ * empty states give v = 0, s = -inf.
+ *
+ *   v_a_d, v_b_d, v_out_d  [num_rows, head_dim] of v_dtype (BF16 or FP32, all
+ *                          three the same), rows contiguous, 16-byte aligned.
+ *   s_a_d, s_b_d, s_out_d  float [num_rows], natural-log LSE.
+ *   head_dim               multiple of 8, at most 4096.
+ * v_out_d may alias v_a_d or v_b_d (and s_out_d s_a_d or s_b_d).
+ * Returns MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED or MLA_ERR_HIP.
+ */
+int32_t mla_merge_states(const void* v_a_d, const float* s_a_d, const void* v_b_d,
+                         const float* s_b_d, void* v_out_d, float* s_out_d, int64_t num_rows,
+                         int32_t head_dim, int32_t v_dtype, void* stream);
+
+/*
+ * mla_tree_suffix_compact - suffix page table of tree-verify attention by a
+ * scan-based stable compaction, in one launch (PR 49477 analysis, section 1).
+ *
+ * For query row r < num_actual_rows, request req = r / width:
+ *   valid[c] = tree_mask_d[r*mask_stride + c] != 0          (c < width)
+ *   rank[c]  = inclusive prefix sum of valid; count = sum of valid
+ *   dest[c]  = valid[c] ? rank[c]-1 : count + c - rank[c]
+ *   page_table_d[r*table_stride + dest[c]] =
+ *            req_to_token_d[req*req_stride + prefix_lens_d[req] + c]
+ *   cache_seqlens_d[r] = count
+ * i.e. visible draft slots first and then the hidden ones, each group in its
+ * original order. Rows num_actual_rows <= r < num_rows are graph padding: no
+ * mask is read, the table row is zeroed and the length is 0. Because the
+ * visible slots come first, attending to the first cache_seqlens_d[r] entries
+ * of each row is the truncation to max_tree_depth of section 2 (pass
+ * cache_seqlens_d as kv_lens_d to mla_decode).
+ *   tree_mask_d  uint8 [num_actual_rows, mask_stride], mask_stride >= width
+ *   req_to_token_d int32 [*, req_stride]; prefix_lens_d int32 [num_actual_rows/width rounded up]
+ *   page_table_d int32 [num_rows, table_stride], table_stride >= width
+ *   width in [1, 1024]
+ * Returns MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED or MLA_ERR_HIP.
+ */
+int32_t mla_tree_suffix_compact(const uint8_t* tree_mask_d, int64_t mask_stride,
+                                const int32_t* req_to_token_d, int64_t req_stride,
+                                const int32_t* prefix_lens_d, int32_t width, int32_t num_rows,
+                                int32_t num_actual_rows, int32_t* page_table_d,
+                                int64_t table_stride, int32_t* cache_seqlens_d, void* stream);
+
+/*
+ * Name of the decode kernel instantiation these parameters select (static
+ * storage), e.g. "mla_decode<hw32,hs4,kv_bf16,out_bf16>"; NULL if unsupported.
+ * Tests use it to prove which branch ran.
+ */
+const char* mla_decode_variant(const mla_decode_params* params);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H_ */

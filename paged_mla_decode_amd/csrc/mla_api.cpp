@@ -1,0 +1,193 @@
+// C-ABI entry points of the MLA decode library: argument validation on the
+// host, then launches on the caller's stream. See include/mla_decode.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "mla_decode.h"
+#include "mla_internal.h"
+
+using namespace mla;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_cu_mutex;
+int g_cu_count[kMaxDevices] = {0};
+
+// Compute units of the current device (cached per device).
+int32_t device_cus(int32_t requested, int32_t* out) {
+    if (requested > 0) {
+        *out = requested;
+        return MLA_OK;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    if (g_cu_count[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return MLA_ERR_HIP;
+        g_cu_count[dev] = n;
+    }
+    *out = g_cu_count[dev];
+    return MLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int32_t status) {
+    switch (status) {
+        case MLA_OK: return "MLA_OK";
+        case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+        case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+        case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
+        case MLA_ERR_HIP: return "MLA_ERR_HIP";
+        case MLA_ERR_PLAN_MISMATCH: return "MLA_ERR_PLAN_MISMATCH";
+        default: return "MLA_ERR_UNKNOWN";
+    }
+}
+
+const char* mla_decode_variant(const mla_decode_params* params) { return variant_name(params); }
+
+int32_t mla_decode_workspace_size(const mla_decode_params* params, int32_t batch, int32_t num_rows,
+                                  size_t* plan_bytes, size_t* workspace_bytes) {
+    if (!params || (!plan_bytes && !workspace_bytes)) return MLA_ERR_INVALID_ARG;
+    Variant v;
+    if (!select_variant(params, &v)) return MLA_ERR_UNSUPPORTED;
+    int32_t cus = 0;
+    const int32_t st = device_cus(params->num_cus, &cus);
+    if (st != MLA_OK) return st;
+    return plan_bounds(params, cus, batch, num_rows, plan_bytes, workspace_bytes);
+}
+
+int32_t mla_decode_plan(const mla_decode_params* params, int32_t batch, const int32_t* qo_indptr_h,
+                        const int32_t* kv_indptr_h, const int32_t* kv_last_page_len_h,
+                        void* plan_h, size_t plan_h_bytes, void* workspace_d,
+                        size_t workspace_bytes, void* stream) {
+    if (!params || !kv_indptr_h || !plan_h || batch < 0) return MLA_ERR_INVALID_ARG;
+    Variant v;
+    if (!select_variant(params, &v)) return MLA_ERR_UNSUPPORTED;
+    int32_t cus = 0;
+    int32_t st = device_cus(params->num_cus, &cus);
+    if (st != MLA_OK) return st;
+    st = plan_build(params, cus, batch, qo_indptr_h, kv_indptr_h, kv_last_page_len_h, plan_h,
+                    plan_h_bytes);
+    if (st != MLA_OK) return st;
+    const mla_plan_header* h = static_cast<const mla_plan_header*>(plan_h);
+    if (workspace_d) {
+        if ((size_t)h->workspace_bytes > workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+        if (hipMemcpyAsync(workspace_d, plan_h, (size_t)h->plan_bytes, hipMemcpyHostToDevice,
+                           (hipStream_t)stream) != hipSuccess)
+            return MLA_ERR_HIP;
+    }
+    return MLA_OK;
+}
+
+int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const void* workspace_d,
+                   size_t workspace_bytes, const void* q_nope_d, int64_t q_nope_stride_n,
+                   int64_t q_nope_stride_h, const void* q_rope_d, int64_t q_rope_stride_n,
+                   int64_t q_rope_stride_h, const void* kv_cache_d, float kv_scale,
+                   const int32_t* kv_indices_d, const int32_t* kv_lens_d, float sm_scale,
+                   void* out_d, float* lse_d, void* stream) {
+    if (!params || !plan_h || !workspace_d) return MLA_ERR_INVALID_ARG;
+    Variant v;
+    if (!select_variant(params, &v)) return MLA_ERR_UNSUPPORTED;
+    const mla_plan_header* h = static_cast<const mla_plan_header*>(plan_h);
+    if (h->magic != MLA_PLAN_MAGIC || h->version != MLA_PLAN_VERSION) return MLA_ERR_INVALID_ARG;
+    if (h->num_heads != params->num_heads || h->page_size != params->page_size ||
+        h->kv_dtype != params->kv_dtype || h->out_dtype != params->out_dtype)
+        return MLA_ERR_PLAN_MISMATCH;
+    if ((size_t)h->workspace_bytes > workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    if (h->num_items == 0) return MLA_OK;
+    if (!q_nope_d || !q_rope_d || !kv_cache_d || !kv_indices_d || !out_d) return MLA_ERR_INVALID_ARG;
+    if (!aligned16(q_nope_d) || !aligned16(q_rope_d) || !aligned16(kv_cache_d) || !aligned16(out_d) ||
+        !aligned16(workspace_d))
+        return MLA_ERR_INVALID_ARG;
+    if (q_nope_stride_n < 0 || q_nope_stride_h < 0 || q_rope_stride_n < 0 || q_rope_stride_h < 0 ||
+        (q_nope_stride_n | q_nope_stride_h | q_rope_stride_n | q_rope_stride_h) % 8 != 0)
+        return MLA_ERR_INVALID_ARG;
+    if (!std::isfinite(sm_scale) || !std::isfinite(kv_scale) || kv_scale <= 0.f) return MLA_ERR_INVALID_ARG;
+    if (params->kv_dtype == MLA_DTYPE_BF16 && kv_scale != 1.f) return MLA_ERR_INVALID_ARG;
+
+    const char* ws = static_cast<const char*>(workspace_d);
+    DecodeArgs a{};
+    a.items = reinterpret_cast<const mla_work_item*>(ws + h->items_offset);
+    a.q_nope = static_cast<const uint16_t*>(q_nope_d);
+    a.qn_sn = q_nope_stride_n;
+    a.qn_sh = q_nope_stride_h;
+    a.q_rope = static_cast<const uint16_t*>(q_rope_d);
+    a.qr_sn = q_rope_stride_n;
+    a.qr_sh = q_rope_stride_h;
+    a.cache = static_cast<const uint8_t*>(kv_cache_d);
+    a.kv_indices = kv_indices_d;
+    a.num_indices = h->num_page_entries;
+    a.kv_lens = kv_lens_d;
+    a.out = out_d;
+    a.lse = lse_d;
+    a.part_out = reinterpret_cast<float*>(const_cast<char*>(ws) + h->partial_out_offset);
+    a.part_lse = reinterpret_cast<float*>(const_cast<char*>(ws) + h->partial_lse_offset);
+    a.num_heads = params->num_heads;
+    a.page_size = params->page_size;
+    a.scale_log2 = (float)((double)sm_scale * (double)kv_scale * 1.4426950408889634);
+    a.out_scale = kv_scale;
+    int err = launch_decode(v, params->kv_dtype, params->out_dtype, a, h->num_items, stream);
+    if (err != 0) return MLA_ERR_HIP;
+    if (h->num_merges > 0) {
+        MergePartialsArgs m{};
+        m.merges = reinterpret_cast<const mla_merge_item*>(ws + h->merges_offset);
+        m.part_out = a.part_out;
+        m.part_lse = a.part_lse;
+        m.out = out_d;
+        m.lse = lse_d;
+        m.num_heads = params->num_heads;
+        err = launch_merge_partials(params->out_dtype, m, h->num_merges, stream);
+        if (err != 0) return MLA_ERR_HIP;
+    }
+    return MLA_OK;
+}
+
+int32_t mla_merge_states(const void* v_a_d, const float* s_a_d, const void* v_b_d,
+                         const float* s_b_d, void* v_out_d, float* s_out_d, int64_t num_rows,
+                         int32_t head_dim, int32_t v_dtype, void* stream) {
+    if (num_rows < 0 || head_dim <= 0 || head_dim % 8 != 0) return MLA_ERR_INVALID_ARG;
+    if (head_dim > 4096) return MLA_ERR_UNSUPPORTED;
+    if (v_dtype != MLA_DTYPE_BF16 && v_dtype != MLA_DTYPE_FP32) return MLA_ERR_UNSUPPORTED;
+    if (num_rows == 0) return MLA_OK;
+    if (!v_a_d || !s_a_d || !v_b_d || !s_b_d || !v_out_d || !s_out_d) return MLA_ERR_INVALID_ARG;
+    if (!aligned16(v_a_d) || !aligned16(v_b_d) || !aligned16(v_out_d)) return MLA_ERR_INVALID_ARG;
+    if (num_rows > (int64_t)INT32_MAX * 4) return MLA_ERR_UNSUPPORTED;
+    return launch_merge_states(v_a_d, s_a_d, v_b_d, s_b_d, v_out_d, s_out_d, num_rows, head_dim,
+                               v_dtype, stream) == 0
+               ? MLA_OK
+               : MLA_ERR_HIP;
+}
+
+int32_t mla_tree_suffix_compact(const uint8_t* tree_mask_d, int64_t mask_stride,
+                                const int32_t* req_to_token_d, int64_t req_stride,
+                                const int32_t* prefix_lens_d, int32_t width, int32_t num_rows,
+                                int32_t num_actual_rows, int32_t* page_table_d,
+                                int64_t table_stride, int32_t* cache_seqlens_d, void* stream) {
+    if (width < 1 || num_rows < 0 || num_actual_rows < 0 || num_actual_rows > num_rows)
+        return MLA_ERR_INVALID_ARG;
+    if (width > 1024) return MLA_ERR_UNSUPPORTED;
+    if (num_rows == 0) return MLA_OK;
+    if (!page_table_d || !cache_seqlens_d || table_stride < width) return MLA_ERR_INVALID_ARG;
+    if (num_actual_rows > 0 &&
+        (!tree_mask_d || !req_to_token_d || !prefix_lens_d || mask_stride < width || req_stride < width))
+        return MLA_ERR_INVALID_ARG;
+    return launch_tree_compact(tree_mask_d, mask_stride, req_to_token_d, req_stride, prefix_lens_d,
+                               width, num_rows, num_actual_rows, page_table_d, table_stride,
+                               cache_seqlens_d, stream) == 0
+               ? MLA_OK
+               : MLA_ERR_HIP;
+}
+
+}  // extern "C"

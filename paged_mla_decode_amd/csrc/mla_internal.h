@@ -1,0 +1,80 @@
+// Internal declarations shared by the C-ABI layer, the host planner and the
+// gfx950 kernels. Not part of the public interface.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mla_decode.h"
+
+namespace mla {
+
+constexpr int kLatent = 512;           // kv_lora_rank: the value width
+constexpr int kRope = 64;              // qk_rope_head_dim
+constexpr int kRow = kLatent + kRope;  // values per cached token
+constexpr int kTile = 32;              // tokens per LDS tile in the decode kernel
+
+// One decode kernel instantiation: HW heads per wave (MFMA N width), HS waves
+// (head blocks) per workgroup, and how many such workgroups fit on one CU.
+struct Variant {
+    int hw;
+    int hs;
+    int wgs_per_cu;
+    int min_chunk;  // shortest chunk worth a partial (tokens)
+};
+
+// Selects the kernel instantiation for these parameters. Returns false when the
+// parameters are outside what this build implements.
+bool select_variant(const mla_decode_params* p, Variant* v);
+const char* variant_name(const mla_decode_params* p);
+
+// Host planner (pure host code, no HIP calls).
+int32_t plan_bounds(const mla_decode_params* p, int32_t num_cus, int32_t batch, int32_t num_rows,
+                    size_t* plan_bytes, size_t* workspace_bytes);
+int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
+                   const int32_t* qo_indptr, const int32_t* kv_indptr,
+                   const int32_t* kv_last_page_len, void* plan_h, size_t plan_h_bytes);
+
+struct DecodeArgs {
+    const mla_work_item* items;
+    const uint16_t* q_nope;  // bf16 bits
+    int64_t qn_sn, qn_sh;
+    const uint16_t* q_rope;
+    int64_t qr_sn, qr_sh;
+    const uint8_t* cache;
+    const int32_t* kv_indices;
+    int64_t num_indices;     // entries of kv_indices (range of the scalar loads)
+    const int32_t* kv_lens;  // may be null
+    void* out;
+    float* lse;  // may be null
+    float* part_out;
+    float* part_lse;
+    int32_t num_heads;
+    int32_t page_size;
+    float scale_log2;  // sm_scale * kv_scale * log2(e)
+    float out_scale;   // kv_scale (fp8 cache) or 1
+};
+
+struct MergePartialsArgs {
+    const mla_merge_item* merges;
+    const float* part_out;
+    const float* part_lse;
+    void* out;
+    float* lse;  // may be null
+    int32_t num_heads;
+};
+
+// Kernel launchers (device code lives in mla_kernels.hip). Return hipError_t as int.
+int launch_decode(const Variant& v, int kv_dtype, int out_dtype, const DecodeArgs& a,
+                  int num_items, void* stream);
+int launch_merge_partials(int out_dtype, const MergePartialsArgs& a, int num_merges,
+                          void* stream);
+int launch_merge_states(const void* v_a, const float* s_a, const void* v_b, const float* s_b,
+                        void* v_out, float* s_out, int64_t num_rows, int32_t head_dim,
+                        int32_t v_dtype, void* stream);
+int launch_tree_compact(const uint8_t* mask, int64_t mask_stride, const int32_t* req_to_token,
+                        int64_t req_stride, const int32_t* prefix_lens, int32_t width,
+                        int32_t num_rows, int32_t num_actual_rows, int32_t* page_table,
+                        int64_t table_stride, int32_t* seqlens, void* stream);
+
+}  // namespace mla

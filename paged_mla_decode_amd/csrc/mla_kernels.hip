@@ -1,0 +1,690 @@
+// gfx950 (CDNA4, MI355X) kernels for weight-absorbed MLA decode over a paged
+// latent cache, the log-sum-exp merge and the tree-suffix stable compaction.
+//
+// Decode kernel design (one workgroup per plan work item: a query row and a
+// token chunk, all heads):
+//   * Latent tiles of 32 tokens stream from HBM into LDS with 16-byte direct
+//     global->LDS loads (no VGPR staging), double-buffered, with the page-table
+//     lookups for tile i+2 and the loads of tile i+1 in flight while tile i is
+//     computed. Unused rows of a partial last tile are redirected to a valid
+//     row, so no load ever leaves the request's pages.
+//   * The score is computed transposed, S^T[token, head] = C . Q^T, as an MFMA
+//     with the absorbed query as the register-resident operand. The
+//     accumulator then holds, per lane, one head and eight consecutive tokens:
+//     exactly the operand layout the P . latent contraction needs, so the
+//     probabilities never leave registers.
+//   * The P . latent product reads the latent tile through the LDS transpose
+//     load (ds_read_b64_tr_b16 / _b8), which hands each lane one latent column
+//     over four (eight) consecutive tokens.
+//   * Softmax in base 2 against a fixed reference point per head: the first
+//     tile's max. The sum and O accumulate exp2(s - reference) and are never
+//     rescaled, so O is only touched by MFMAs. Should a later score exceed the
+//     reference by more than 2^64 (possible only for extreme score spreads),
+//     the chunk is recomputed once with the true max as the reference. Either
+//     way the result is the exact softmax, normalised at the end.
+//   * Row max / sum across the lanes that share a head use v_permlane16/32_swap.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "mla_internal.h"
+#include "mla_tile_layout.h"
+
+namespace mla {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kOverflowSlack = 64.0f;  // log2 units: probabilities stay below 2^64
+
+// ---------------------------------------------------------------------------
+// Small device helpers
+// ---------------------------------------------------------------------------
+
+// Barriers written as inline assembly with a memory clobber, so that the
+// compiler neither moves memory operations across them nor adds waits of its
+// own. Direct-to-LDS loads complete in issue order with the other vector
+// memory loads, so "vmcnt <= N" means everything but the N most recent loads
+// has landed in LDS.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// All of this wave's LDS accesses are complete, then a workgroup barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-byte direct global->LDS load: lane l's 16 bytes land at lds + 16 l.
+// Issued as inline assembly so that the compiler's wait-count model never sees
+// these LDS writes (it would otherwise drain every load before each LDS read);
+// wait_vmcnt_barrier() orders them instead. M0 holds the wave-uniform LDS
+// address; one wait state separates its write from the load.
+__device__ __forceinline__ void dma16(const void* src, LDS_AS void* dst) {
+    const uint32_t lds = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(src)
+                 : "memory", "m0");
+}
+
+// Value held by lane ^ 32 / lane ^ 16, combined with the own value.
+__device__ __forceinline__ float max_xor32(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Eight e4m3fn codes (two dwords) -> eight bf16 values, exact.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned lo, unsigned hi) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return r;
+}
+
+typedef int i32x4s __attribute__((ext_vector_type(4)));
+typedef int i32x8s __attribute__((ext_vector_type(8)));
+typedef int i32x16s __attribute__((ext_vector_type(16)));
+// Scalar buffer loads (SMEM, tracked by lgkmcnt, range-checked by the buffer
+// descriptor: dwords past num_records read as 0).
+__device__ i32x8s sbuffer_load_x8(i32x4s rsrc, int byte_off, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v8i32");
+__device__ i32x16s sbuffer_load_x16(i32x4s rsrc, int byte_off, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v16i32");
+
+// Raw buffer descriptor for a dword array of n entries (gfx9 family dword 3).
+__device__ __forceinline__ i32x4s make_rsrc(const void* base, int64_t n_dwords) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t bytes = (uint64_t)n_dwords * 4u;
+    i32x4s r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)(uint32_t)((a >> 32) & 0xFFFFu);  // stride 0
+    r[2] = (int)(uint32_t)(bytes > 0xFFFFFFFFull ? 0xFFFFFFFFull : bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// v[off] for a per-lane off in [0, N), from a wave-uniform (SGPR) vector.
+template <int N, class V>
+__device__ __forceinline__ int select_lane(const V& v, int off) {
+    int x = v[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) x = off == j ? v[j] : x;
+    return x;
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// The decode kernel
+// ---------------------------------------------------------------------------
+template <int HW, int HS, bool KV8, bool OUT32>
+__global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
+    using L = TileLayout<KV8>;
+    using SA = ScoreAddr<HW, KV8>;
+    using PA = PvAddr<HW, KV8>;
+    constexpr int NV = HW == 32 ? 16 : 8;                        // score values per lane per tile
+    constexpr int kLoadsMax = (L::kNB + HS - 1) / HS;            // direct loads per wave per tile
+    constexpr int kLoadsMin = L::kNB / HS;
+    constexpr int kNTok = HS >= L::kNTB ? 1 : L::kNTB / HS;      // distinct tokens a lane loads
+    constexpr int kSteps = SA::kSteps;
+    constexpr int kDBlocks = PA::kDBlocks;
+    static_assert(kLoadsMax + kNTok < 64, "vmcnt budget");
+    // The scheduler may not hoist LDS reads more than this many MFMA steps
+    // ahead: unbounded hoisting costs four VGPRs per operand in flight.
+    constexpr int kSchedStep = 2;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * L::kTileBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const mla_work_item it = a.items[blockIdx.x];
+    const int ps = a.page_size;
+    const int kv_begin = it.kv_begin;
+    int kv_end = it.kv_end;
+    if (a.kv_lens) kv_end = min(kv_end, a.kv_lens[it.request]);
+    const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + kTile - 1) / kTile : 0;
+
+    // Lane roles. hq: head (MFMA N index); gq: lane group along the K dim.
+    const int hq = HW == 32 ? (lane & 31) : (lane & 15);
+    const int gq = HW == 32 ? (lane >> 5) : (lane >> 4);
+    const int head = it.head_begin + w * HW + hq;
+
+    // ---- absorbed query -> registers (B operand of the score MFMA) ----
+    bf16x8 q[kSteps];
+    {
+        const uint16_t* qn = a.q_nope + (int64_t)it.row * a.qn_sn + (int64_t)head * a.qn_sh;
+        const uint16_t* qr = a.q_rope + (int64_t)it.row * a.qr_sn + (int64_t)head * a.qr_sh;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            const int k0 = (HW == 32 ? 16 : 32) * s + 8 * gq;
+            q[s] = (s < kSteps * 8 / 9) ? load_bf16x8(qn + k0) : load_bf16x8(qr + (k0 - kLatent));
+        }
+        // Let the query land before any tile load is issued: the compiler does not
+        // see the tile loads, so its own waits for these registers inside the
+        // loop would otherwise also drain the tiles in flight.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+
+    // ---- per-lane LDS bases (see mla_tile_layout.h) ----
+    int sbase[SA::kBases], pbase[PA::kBases];
+#pragma unroll
+    for (int i = 0; i < SA::kBases; ++i) sbase[i] = SA::base(lane, i);
+#pragma unroll
+    for (int i = 0; i < PA::kBases; ++i) pbase[i] = PA::base(lane, i);
+    // Global byte offset of the chunk this lane loads, within its row (chunk group 0).
+    const int dma_lane_off = L::block_chunk(0, lane) * 16;
+
+    // ---- page-table lookups for the tokens this lane loads ----
+    // A wave's lanes load TPB consecutive tokens per token block, which span at
+    // most TPB consecutive page-table entries: one scalar buffer load fetches
+    // them, and each lane picks its own. Tail tokens are clamped to the last
+    // valid token, so no load ever leaves the request's pages.
+    using IdxVec = typename std::conditional<L::kTPB == 8, i32x8s, i32x16s>::type;
+    const i32x4s idx_rsrc = make_rsrc(a.kv_indices, a.num_indices);
+    IdxVec sidx[kNTok];
+    int p0[kNTok];
+    auto fetch_idx = [&](int tile) {  // issue the scalar loads for a tile
+        const int tstart = kv_begin + tile * kTile;
+#pragma unroll
+        for (int k = 0; k < kNTok; ++k) {
+            const int tb = HS >= L::kNTB ? (w % L::kNTB) : (w + HS * k);
+            const int first = min(tstart + tb * L::kTPB, kv_end - 1);
+            p0[k] = first / ps;
+            const int off = (it.page_base + p0[k]) * 4;
+            if constexpr (L::kTPB == 8)
+                sidx[k] = sbuffer_load_x8(idx_rsrc, off, 0);
+            else
+                sidx[k] = sbuffer_load_x16(idx_rsrc, off, 0);
+        }
+    };
+    auto resolve_rows = [&](int tile, const uint8_t** rowp) {  // lane row pointers of a tile
+        const int tstart = kv_begin + tile * kTile;
+#pragma unroll
+        for (int k = 0; k < kNTok; ++k) {
+            const int tb = HS >= L::kNTB ? (w % L::kNTB) : (w + HS * k);
+            const int tau = min(tstart + L::block_token(tb, lane), kv_end - 1);
+            const int pi = tau / ps;
+            const int page = select_lane<L::kTPB>(sidx[k], pi - p0[k]);
+            rowp[k] = a.cache + ((int64_t)page * ps + (tau - pi * ps)) * L::kRowBytes + dma_lane_off;
+        }
+    };
+    auto issue_tile = [&](LDS_AS char* base, const uint8_t* const* rowp) {
+#pragma unroll
+        for (int i = 0; i < kLoadsMax; ++i) {
+            const int b = w + HS * i;
+            if (L::kNB % HS != 0 && b >= L::kNB) break;
+            const int k = HS >= L::kNTB ? 0 : i % (L::kNTB / HS);
+            const int cg = b / L::kNTB;
+            dma16(rowp[k] + cg * L::kCG * 16, base + b * 1024);
+        }
+    };
+
+    // ---- accumulators ----
+    f32x16 O32[HW == 32 ? kDBlocks : 1];
+    f32x4 O16[HW == 16 ? kDBlocks : 1];
+    // Softmax reference point (log2 units) per head: the first tile's max. The
+    // running true max is tracked; if it ever exceeds the reference by more
+    // than kOverflowSlack the chunk is recomputed with the true max as the
+    // reference (which then bounds every probability by 1). O is only ever
+    // touched by MFMAs inside the loop.
+    float m_ref = -INFINITY, m_true = -INFINITY;
+    float l_part = 0.f;
+    __shared__ int rerun_flag[HS];
+
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int i = 0; i < (HW == 32 ? kDBlocks : 1); ++i) O32[i] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < (HW == 16 ? kDBlocks : 1); ++i) O16[i] = f32x4{};
+    l_part = 0.f;
+
+    if (ntiles > 0) {
+        // One tile step. T is the buffer computed, N the one being filled;
+        // distinct restrict-qualified parameters tell the compiler the two
+        // never alias, so it adds no waits of its own for the direct-to-LDS
+        // loads: the explicit vmcnt waits order them. Step i = -1 only starts
+        // the pipeline (loads of tile 0). Every vector memory load in flight
+        // here is a tile load: the page table is read through the scalar path.
+        fetch_idx(0);
+        auto tile_step = [&](const LDS_AS char* __restrict__ T, LDS_AS char* __restrict__ N, int i) {
+            const int tstart = kv_begin + i * kTile;
+            if (i + 1 < ntiles) {
+                const uint8_t* rowp[kNTok];
+                resolve_rows(i + 1, rowp);
+                if (i + 2 < ntiles) fetch_idx(i + 2);
+                issue_tile(N, rowp);
+            }
+            if (i < 0) return;
+            // Outstanding after tile i's loads: those of tile i+1, if any.
+            if (i + 1 < ntiles)
+                wait_vmcnt_barrier<kLoadsMin>();
+            else
+                wait_vmcnt_barrier<0>();
+
+            const int nvalid = min(kTile, kv_end - tstart);
+
+            // ---- score: S^T = C . Q^T ----
+            float sv[NV];
+            if constexpr (HW == 32) {
+                f32x16 S = {};
+#pragma unroll
+                for (int s = 0; s < kSteps; ++s) {
+                    const int off = sbase[SA::base_index(s, 0)] + SA::delta(s);
+                    bf16x8 A;
+                    if constexpr (KV8) {
+                        const i32x2 raw = *(const LDS_AS i32x2*)(T + off);
+                        A = fp8x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]);
+                    } else {
+                        A = *(const LDS_AS bf16x8*)(T + off);
+                    }
+                    S = mfma32(A, q[s], S);
+                    if ((s + 1) % kSchedStep == 0) __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sv[r] = S[r];
+            } else {
+                f32x4 S0 = {}, S1 = {};
+#pragma unroll
+                for (int s = 0; s < kSteps; ++s) {
+                    const int off0 = sbase[SA::base_index(s, 0)] + SA::delta(s);
+                    const int off1 = sbase[SA::base_index(s, 1)] + SA::delta(s);
+                    bf16x8 A0, A1;
+                    if constexpr (KV8) {
+                        const i32x2 r0 = *(const LDS_AS i32x2*)(T + off0);
+                        const i32x2 r1 = *(const LDS_AS i32x2*)(T + off1);
+                        A0 = fp8x8_to_bf16((unsigned)r0[0], (unsigned)r0[1]);
+                        A1 = fp8x8_to_bf16((unsigned)r1[0], (unsigned)r1[1]);
+                    } else {
+                        A0 = *(const LDS_AS bf16x8*)(T + off0);
+                        A1 = *(const LDS_AS bf16x8*)(T + off1);
+                    }
+                    S0 = mfma16(A0, q[s], S0);
+                    S1 = mfma16(A1, q[s], S1);
+                    if ((s + 1) % kSchedStep == 0) __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sv[r] = S0[r];
+                    sv[4 + r] = S1[r];
+                }
+            }
+
+            // ---- scale, mask the tail, tile max ----
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < NV; ++r) {
+                // token of value r: HW32: 16*(r/8) + 8*g + r%8; HW16: 8*g + r
+                const int tok = HW == 32 ? (16 * (r >> 3) + 8 * gq + (r & 7)) : (8 * gq + r);
+                float v = sv[r] * a.scale_log2;
+                v = tok < nvalid ? v : -INFINITY;
+                sv[r] = v;
+                tmax = fmaxf(tmax, v);
+            }
+            if (HW == 16) tmax = max_xor16(tmax);
+            tmax = max_xor32(tmax);
+            if (pass == 0 && i == 0) m_ref = tmax;
+            m_true = fmaxf(m_true, tmax);
+
+            // ---- probabilities relative to the reference ----
+            float p[NV];
+#pragma unroll
+            for (int r = 0; r < NV; ++r) {
+                p[r] = fast_exp2(sv[r] - m_ref);
+                l_part += p[r];
+            }
+
+            // ---- O^T += C^T . P^T ----
+            constexpr int kKK = HW == 32 ? 2 : 1;
+#pragma unroll
+            for (int kk = 0; kk < kKK; ++kk) {
+                bf16x8 P, Plo;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    P[e] = (__bf16)p[8 * kk + e];
+                    if (OUT32) Plo[e] = (__bf16)(p[8 * kk + e] - (float)P[e]);
+                }
+#pragma unroll
+                for (int md = 0; md < kDBlocks; ++md) {
+                    const int pb = pbase[PA::base_index(md)];
+                    bf16x8 A;
+                    if constexpr (KV8) {
+                        const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                            (LDS_AS i32x2*)(T + pb + PA::delta(md, kk, 0)));
+                        A = fp8x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]);
+                    } else {
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (LDS_AS i16x4*)(T + pb + PA::delta(md, kk, 0)));
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (LDS_AS i16x4*)(T + pb + PA::delta(md, kk, 1)));
+                        A = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
+                    if constexpr (HW == 32) {
+                        O32[md] = mfma32(A, P, O32[md]);
+                        if (OUT32) O32[md] = mfma32(A, Plo, O32[md]);
+                    } else {
+                        O16[md] = mfma16(A, P, O16[md]);
+                        if (OUT32) O16[md] = mfma16(A, Plo, O16[md]);
+                    }
+                    if ((md + 1) % kSchedStep == 0) __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            lds_barrier();  // everyone is done with this buffer before it is refilled
+        };
+        for (int i = -1; i < ntiles; ++i) {
+            const int cur = (i & 1) * L::kTileBytes;  // i = -1 computes nothing and fills buffer 0
+            tile_step((const LDS_AS char*)smem + cur, (LDS_AS char*)smem + (L::kTileBytes - cur), i);
+        }
+    }
+    // Did any head of the workgroup outgrow its reference? All waves must agree,
+    // since the tiles are loaded cooperatively.
+    const bool over = __builtin_amdgcn_ballot_w64(m_true > m_ref + kOverflowSlack) != 0;
+    if (lane == 0) rerun_flag[w] = over ? 1 : 0;
+    lds_barrier();
+    int any = 0;
+#pragma unroll
+    for (int k = 0; k < HS; ++k) any |= rerun_flag[k];
+    lds_barrier();
+    if (!any) break;
+    m_ref = m_true;  // second pass: every probability is at most 1
+    }
+
+    // ---- finalize: l across the lanes of a head, normalise, write ----
+    const float m_run = m_ref;
+    float l = l_part;
+    if (HW == 16) l = sum_xor16(l);
+    l = sum_xor32(l);
+    const bool empty = !(l > 0.f);
+    const float inv = empty ? 0.f : (a.out_scale / l);
+    const float lse = empty ? -INFINITY : (m_run + __log2f(l)) * kLn2;
+    const int nh = a.num_heads;
+
+    if (it.partial >= 0) {
+        float* po = a.part_out + ((int64_t)it.partial * nh + head) * kLatent;
+        if constexpr (HW == 32) {
+#pragma unroll
+            for (int md = 0; md < kDBlocks; ++md)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int d = 32 * md + 8 * r4 + 4 * gq;
+                    f32x4 v = {O32[md][4 * r4] * inv, O32[md][4 * r4 + 1] * inv,
+                               O32[md][4 * r4 + 2] * inv, O32[md][4 * r4 + 3] * inv};
+                    *reinterpret_cast<f32x4*>(po + d) = v;
+                }
+        } else {
+#pragma unroll
+            for (int md = 0; md < kDBlocks; ++md) {
+                const int d = 16 * md + 4 * gq;
+                *reinterpret_cast<f32x4*>(po + d) = O16[md] * inv;
+            }
+        }
+        if (gq == 0) a.part_lse[(int64_t)it.partial * nh + head] = lse;
+    } else {
+        if constexpr (OUT32) {
+            float* o = reinterpret_cast<float*>(a.out) + ((int64_t)it.row * nh + head) * kLatent;
+            if constexpr (HW == 32) {
+#pragma unroll
+                for (int md = 0; md < kDBlocks; ++md)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int d = 32 * md + 8 * r4 + 4 * gq;
+                        f32x4 v = {O32[md][4 * r4] * inv, O32[md][4 * r4 + 1] * inv,
+                                   O32[md][4 * r4 + 2] * inv, O32[md][4 * r4 + 3] * inv};
+                        *reinterpret_cast<f32x4*>(o + d) = v;
+                    }
+            } else {
+#pragma unroll
+                for (int md = 0; md < kDBlocks; ++md)
+                    *reinterpret_cast<f32x4*>(o + 16 * md + 4 * gq) = O16[md] * inv;
+            }
+        } else {
+            __bf16* o = reinterpret_cast<__bf16*>(a.out) + ((int64_t)it.row * nh + head) * kLatent;
+            if constexpr (HW == 32) {
+#pragma unroll
+                for (int md = 0; md < kDBlocks; ++md)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int d = 32 * md + 8 * r4 + 4 * gq;
+                        bf16x4 v = {(__bf16)(O32[md][4 * r4] * inv), (__bf16)(O32[md][4 * r4 + 1] * inv),
+                                    (__bf16)(O32[md][4 * r4 + 2] * inv), (__bf16)(O32[md][4 * r4 + 3] * inv)};
+                        *reinterpret_cast<bf16x4*>(o + d) = v;
+                    }
+            } else {
+#pragma unroll
+                for (int md = 0; md < kDBlocks; ++md) {
+                    const f32x4 x = O16[md] * inv;
+                    bf16x4 v = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+                    *reinterpret_cast<bf16x4*>(o + 16 * md + 4 * gq) = v;
+                }
+            }
+        }
+        if (a.lse && gq == 0) a.lse[(int64_t)it.row * nh + head] = lse;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of split-KV partials (one wave per (row, head)).
+// ---------------------------------------------------------------------------
+template <bool OUT32>
+__global__ __launch_bounds__(256) void merge_partials_kernel(const MergePartialsArgs a) {
+    const mla_merge_item mi = a.merges[blockIdx.x];
+    const int lane = threadIdx.x & 63;
+    const int nh = a.num_heads;
+    for (int h = blockIdx.y * 4 + (threadIdx.x >> 6); h < nh; h += gridDim.y * 4) {
+        float m = -INFINITY;
+        for (int p = 0; p < mi.num_partials; ++p)
+            m = fmaxf(m, a.part_lse[(int64_t)(mi.partial_begin + p) * nh + h]);
+        f32x8 acc = {};
+        float wsum = 0.f;
+        if (m != -INFINITY) {
+            for (int p = 0; p < mi.num_partials; ++p) {
+                const int64_t slot = (int64_t)(mi.partial_begin + p) * nh + h;
+                const float wp = fast_exp2((a.part_lse[slot] - m) * kLog2e);
+                wsum += wp;
+                const f32x8 v = *reinterpret_cast<const f32x8*>(a.part_out + slot * kLatent + 8 * lane);
+                acc += wp * v;
+            }
+        }
+        const bool empty = !(wsum > 0.f);
+        const float inv = empty ? 0.f : 1.f / wsum;
+        const int64_t orow = (int64_t)mi.row * nh + h;
+        if constexpr (OUT32) {
+            *reinterpret_cast<f32x8*>(reinterpret_cast<float*>(a.out) + orow * kLatent + 8 * lane) = acc * inv;
+        } else {
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (__bf16)(acc[e] * inv);
+            *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(a.out) + orow * kLatent + 8 * lane) = v;
+        }
+        if (a.lse && lane == 0) a.lse[orow] = empty ? -INFINITY : m + __logf(wsum);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Two-state LSE merge (one wave per row, 8 elements per lane per step).
+// ---------------------------------------------------------------------------
+template <bool F32>
+__global__ __launch_bounds__(256) void merge_states_kernel(const void* va, const float* sa,
+                                                           const void* vb, const float* sb,
+                                                           void* vo, float* so, int64_t rows,
+                                                           int d) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const float a = sa[row], b = sb[row];
+    float wa = 0.f, wb = 0.f, s = -INFINITY;
+    if (!(a == -INFINITY && b == -INFINITY)) {
+        const float m = fmaxf(a, b);
+        const float ea = __expf(a - m), eb = __expf(b - m);
+        const float sum = ea + eb;
+        wa = ea / sum;
+        wb = eb / sum;
+        s = m + __logf(sum);
+    }
+    for (int c = 8 * lane; c < d; c += 512) {
+        const int64_t off = row * d + c;
+        if constexpr (F32) {
+            const f32x8 x = *reinterpret_cast<const f32x8*>(reinterpret_cast<const float*>(va) + off);
+            const f32x8 y = *reinterpret_cast<const f32x8*>(reinterpret_cast<const float*>(vb) + off);
+            *reinterpret_cast<f32x8*>(reinterpret_cast<float*>(vo) + off) = wa * x + wb * y;
+        } else {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(va) + off);
+            const bf16x8 y = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(vb) + off);
+            bf16x8 r;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r[e] = (__bf16)(wa * (float)x[e] + wb * (float)y[e]);
+            *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(vo) + off) = r;
+        }
+    }
+    if (lane == 0) so[row] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Tree-suffix stable compaction (one wave per query row).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tree_compact_kernel(
+    const uint8_t* __restrict__ mask, int64_t mask_stride, const int32_t* __restrict__ req_to_token,
+    int64_t req_stride, const int32_t* __restrict__ prefix_lens, int width, int num_rows,
+    int num_actual_rows, int32_t* __restrict__ table, int64_t table_stride,
+    int32_t* __restrict__ seqlens) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= num_rows) return;
+    const int lane = threadIdx.x & 63;
+    int32_t* trow = table + (int64_t)row * table_stride;
+    if (row >= num_actual_rows) {  // graph padding: read no mask
+        for (int c = lane; c < width; c += 64) trow[c] = 0;
+        if (lane == 0) seqlens[row] = 0;
+        return;
+    }
+    const int req = row / width;
+    const int32_t* slots = req_to_token + (int64_t)req * req_stride + prefix_lens[req];
+    const uint8_t* mrow = mask + (int64_t)row * mask_stride;
+    int count = 0;
+    for (int seg = 0; seg < width; seg += 64) {
+        const int c = seg + lane;
+        const bool v = c < width && mrow[c] != 0;
+        count += __popcll(__builtin_amdgcn_ballot_w64(v));
+    }
+    const uint64_t le = (uint64_t(2) << lane) - 1;  // lanes 0..lane
+    int before = 0;
+    for (int seg = 0; seg < width; seg += 64) {
+        const int c = seg + lane;
+        const bool v = c < width && mrow[c] != 0;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(v);
+        const int rank = before + __popcll(bal & le);  // inclusive count of visible columns
+        if (c < width) {
+            const int dest = v ? rank - 1 : count + c - rank;
+            trow[dest] = slots[c];
+        }
+        before += __popcll(bal);
+    }
+    if (lane == 0) seqlens[row] = count;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <int HW, int HS>
+static int launch_decode_hs(int kv_dtype, int out_dtype, const DecodeArgs& a, int n, hipStream_t s) {
+    const dim3 grid(n), block(64 * HS);
+    const bool kv8 = kv_dtype == MLA_DTYPE_FP8_E4M3FN;
+    const bool o32 = out_dtype == MLA_DTYPE_FP32;
+    if (kv8 && o32)
+        decode_kernel<HW, HS, true, true><<<grid, block, 0, s>>>(a);
+    else if (kv8)
+        decode_kernel<HW, HS, true, false><<<grid, block, 0, s>>>(a);
+    else if (o32)
+        decode_kernel<HW, HS, false, true><<<grid, block, 0, s>>>(a);
+    else
+        decode_kernel<HW, HS, false, false><<<grid, block, 0, s>>>(a);
+    return (int)hipGetLastError();
+}
+
+int launch_decode(const Variant& v, int kv_dtype, int out_dtype, const DecodeArgs& a, int num_items,
+                  void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (num_items <= 0) return 0;
+    if (v.hw == 32 && v.hs == 4) return launch_decode_hs<32, 4>(kv_dtype, out_dtype, a, num_items, s);
+    if (v.hw == 16 && v.hs == 1) return launch_decode_hs<16, 1>(kv_dtype, out_dtype, a, num_items, s);
+    if (v.hw == 16 && v.hs == 2) return launch_decode_hs<16, 2>(kv_dtype, out_dtype, a, num_items, s);
+    if (v.hw == 16 && v.hs == 4) return launch_decode_hs<16, 4>(kv_dtype, out_dtype, a, num_items, s);
+    return (int)hipErrorInvalidValue;
+}
+
+int launch_merge_partials(int out_dtype, const MergePartialsArgs& a, int num_merges, void* stream) {
+    if (num_merges <= 0) return 0;
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 grid(num_merges, (a.num_heads + 3) / 4), block(256);
+    if (out_dtype == MLA_DTYPE_FP32)
+        merge_partials_kernel<true><<<grid, block, 0, s>>>(a);
+    else
+        merge_partials_kernel<false><<<grid, block, 0, s>>>(a);
+    return (int)hipGetLastError();
+}
+
+int launch_merge_states(const void* v_a, const float* s_a, const void* v_b, const float* s_b,
+                        void* v_out, float* s_out, int64_t num_rows, int32_t head_dim,
+                        int32_t v_dtype, void* stream) {
+    if (num_rows <= 0) return 0;
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 grid((unsigned)((num_rows + 3) / 4)), block(256);
+    if (v_dtype == MLA_DTYPE_FP32)
+        merge_states_kernel<true><<<grid, block, 0, s>>>(v_a, s_a, v_b, s_b, v_out, s_out, num_rows, head_dim);
+    else
+        merge_states_kernel<false><<<grid, block, 0, s>>>(v_a, s_a, v_b, s_b, v_out, s_out, num_rows, head_dim);
+    return (int)hipGetLastError();
+}
+
+int launch_tree_compact(const uint8_t* mask, int64_t mask_stride, const int32_t* req_to_token,
+                        int64_t req_stride, const int32_t* prefix_lens, int32_t width,
+                        int32_t num_rows, int32_t num_actual_rows, int32_t* page_table,
+                        int64_t table_stride, int32_t* seqlens, void* stream) {
+    if (num_rows <= 0) return 0;
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 grid((num_rows + 3) / 4), block(256);
+    tree_compact_kernel<<<grid, block, 0, s>>>(mask, mask_stride, req_to_token, req_stride,
+                                               prefix_lens, width, num_rows, num_actual_rows,
+                                               page_table, table_stride, seqlens);
+    return (int)hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,151 @@
+// LDS layout of a decode tile and the per-lane address decompositions the
+// decode kernel uses. Host and device code share this header: a CPU test
+// checks every decomposition against chunk_offset() for every lane.
+//
+// A tile holds 32 cache rows (tokens). A row is split into 16-byte chunks
+// (72 for bf16, 36 for fp8). The tile is stored as 1 KiB blocks, each holding
+// TPB tokens x CG chunks: one direct-to-LDS load instruction of a wave writes
+// its 64 lanes' 16 bytes contiguously, i.e. exactly one block. Inside a block,
+// chunk c of token t sits in slot c ^ (t % CG): an XOR swizzle that spreads the
+// same chunk of consecutive tokens over different LDS banks. Blocks are
+// ordered chunk-group-major: block = (chunk / CG) * NTB + token / TPB.
+//
+// Every LDS read address of the kernel is (a per-lane base register) + (a
+// compile-time immediate). The swizzle mixes lane bits and compile-time bits,
+// so each read type keeps a handful of bases, one per value of the
+// compile-time bits that interact with the lane bits.
+#pragma once
+
+#if defined(__HIPCC__)
+#define MLA_HD __host__ __device__ __forceinline__
+#else
+#define MLA_HD inline
+#endif
+
+namespace mla {
+
+template <bool KV8>
+struct TileLayout {
+    static constexpr int kTile = 32;
+    static constexpr int kRowBytes = KV8 ? 576 : 1152;
+    static constexpr int kCPT = kRowBytes / 16;  // chunks per token: 36 | 72
+    static constexpr int kCG = KV8 ? 4 : 8;      // chunks per token in one block
+    static constexpr int kTPB = 64 / kCG;        // tokens per block: 16 | 8
+    static constexpr int kNCG = kCPT / kCG;      // chunk groups: 9
+    static constexpr int kNTB = kTile / kTPB;    // token blocks: 2 | 4
+    static constexpr int kNB = kNCG * kNTB;      // blocks per tile: 18 | 36
+    static constexpr int kTileBytes = kNB * 1024;
+
+    // Byte offset of chunk j of token t.
+    static MLA_HD int chunk_offset(int t, int j) {
+        const int b = (j / kCG) * kNTB + t / kTPB;
+        return b * 1024 + ((t % kTPB) * kCG + ((j % kCG) ^ (t % kCG))) * 16;
+    }
+    // Which chunk lane `lane` of a block loads (the inverse swizzle), and the
+    // token of the block it belongs to.
+    static MLA_HD int block_token(int tb, int lane) { return tb * kTPB + lane / kCG; }
+    static MLA_HD int block_chunk(int cg, int lane) {
+        const int t_mod = (lane / kCG) % kCG;  // = token % CG, for every token block
+        return cg * kCG + ((lane % kCG) ^ t_mod);
+    }
+};
+
+// ---- Score operand (A of S^T = C . Q^T): lane reads 8 latent values of one token ----
+//
+// HW=32 (32x32x16 MFMA): lane holds token perm(lane % 32) and k = 16 s + 8 (lane / 32).
+// The token permutation swaps bits 2 and 3, so that the accumulator rows a lane
+// owns are eight consecutive tokens (what the P . latent operand needs).
+// HW=16 (16x16x32 MFMA, two 16-token blocks): lane holds token
+// 8 (m / 4) + m % 4 + 4 blk (m = lane % 16) and k = 32 s + 8 (lane / 16).
+template <int HW, bool KV8>
+struct ScoreAddr {
+    using L = TileLayout<KV8>;
+    static constexpr int kSteps = HW == 32 ? 36 : 18;
+    static constexpr int kBlocks = HW == 32 ? 1 : 2;
+    static constexpr int kBases = 4;
+
+    static MLA_HD int token(int lane, int blk) {
+        if (HW == 32) {
+            const int m = lane & 31;
+            return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1);
+        }
+        const int m = lane & 15;
+        return 8 * (m >> 2) + (m & 3) + 4 * blk;
+    }
+    // Reference: byte offset of the 8 values (16 bytes bf16 / 8 bytes fp8).
+    static MLA_HD int reference(int lane, int s, int blk) {
+        const int g = HW == 32 ? (lane >> 5) : (lane >> 4);
+        const int kbyte = (KV8 ? 1 : 2) * ((HW == 32 ? 16 : 32) * s + 8 * g);
+        return L::chunk_offset(token(lane, blk), kbyte >> 4) + (kbyte & 15);
+    }
+    // Base index and immediate of step s of block blk.
+    static MLA_HD constexpr int base_index(int s, int blk) {
+        return HW == 32 ? (s % 4) : (2 * blk + (s % 2));
+    }
+    static MLA_HD constexpr int delta(int s) {
+        return HW == 32 ? (s / 4) * (KV8 ? 2048 : 4096) : (s / 2) * (KV8 ? 2048 : 4096);
+    }
+    static MLA_HD int base(int lane, int bi) {
+        return HW == 32 ? reference(lane, bi, 0) : reference(lane, bi % 2, bi / 2);
+    }
+};
+
+// ---- P . latent operand (A of O^T = C^T . P^T): transposed LDS reads ----
+//
+// bf16, ds_read_b64_tr_b16: a 16-lane group reads a 4-token x 16-column block;
+// lane q supplies the address of token q / 4, columns 4 (q % 4) .. +3 and
+// receives column q over the 4 tokens. Two reads (hi = 0, 1) cover 8 tokens.
+// fp8, ds_read_b64_tr_b8: a 16-lane group reads an 8-token x 16-byte block;
+// lane q supplies token q / 2, bytes 8 (q % 2) .. +7 and receives byte column q
+// over the 8 tokens.
+// HW=32: output block md covers latent columns 32 md .. +31, token half kk.
+// HW=16: output block md covers latent columns 16 md .. +15.
+template <int HW, bool KV8>
+struct PvAddr {
+    using L = TileLayout<KV8>;
+    static constexpr int kDBlocks = 512 / HW;
+    static constexpr int kHalves = KV8 ? 1 : 2;
+    static constexpr int kBases = KV8 ? (HW == 32 ? 2 : 4) : (HW == 32 ? 1 : 2);
+
+    static MLA_HD int reference(int lane, int md, int kk, int hi) {
+        const int grp = lane >> 4, q = lane & 15;
+        int t, cbyte;
+        if (HW == 32) {
+            const int rowb = 16 * kk + 8 * (grp >> 1);
+            const int colb = 32 * md + 16 * (grp & 1);  // element column
+            if (KV8) {
+                t = rowb + (q >> 1);
+                cbyte = colb + 8 * (q & 1);
+            } else {
+                t = rowb + (q >> 2) + 4 * hi;
+                cbyte = 2 * (colb + 4 * (q & 3));
+            }
+        } else {
+            const int rowb = 8 * grp;
+            const int colb = 16 * md;
+            if (KV8) {
+                t = rowb + (q >> 1);
+                cbyte = colb + 8 * (q & 1);
+            } else {
+                t = rowb + (q >> 2) + 4 * hi;
+                cbyte = 2 * (colb + 4 * (q & 3));
+            }
+        }
+        return L::chunk_offset(t, cbyte >> 4) + (cbyte & 15);
+    }
+    static MLA_HD constexpr int base_index(int md) {
+        return KV8 ? (HW == 32 ? (md & 1) : (md & 3)) : (HW == 32 ? 0 : (md & 1));
+    }
+    static MLA_HD constexpr int delta(int md, int kk, int hi) {
+        if (KV8) return HW == 32 ? ((md >> 1) * 2 + kk) * 1024 : (md >> 2) * 2048;
+        if (HW == 32)
+            return ((md >> 1) * 4 + 2 * kk) * 1024 + hi * 512 + 64 * ((md & 1) ^ hi);
+        return (md >> 2) * 4096 + hi * 512 + 64 * (((md >> 1) & 1) ^ hi);
+    }
+    static MLA_HD int base(int lane, int bi) {
+        // The instance with delta 0 for this base.
+        return reference(lane, bi, 0, 0);
+    }
+};
+
+}  // namespace mla

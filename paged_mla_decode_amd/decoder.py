@@ -1,0 +1,108 @@
+"""Convenience wrapper around the C ABI: owns the pinned host plan buffer and
+the device workspace (torch allocations), and calls mla_decode_plan /
+mla_decode. Every step of the computation runs in the HIP library.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _binding as B
+
+_DTYPES = {"bf16": B.MLA_DTYPE_BF16, "fp32": B.MLA_DTYPE_FP32, "fp8_e4m3fn": B.MLA_DTYPE_FP8_E4M3FN}
+
+
+class PagedMlaDecoder:
+    """Absorbed-MLA decode over a paged latent cache for batches of up to
+    ``max_batch`` requests and ``max_rows`` query rows."""
+
+    def __init__(self, num_heads: int, page_size: int, max_batch: int, max_rows: int | None = None,
+                 kv_dtype: str = "bf16", out_dtype: str = "bf16", num_cus: int = 0,
+                 max_splits: int = 0, device="cuda"):
+        self.device = torch.device(device)
+        self.params = B.make_params(num_heads, page_size, _DTYPES[kv_dtype], _DTYPES[out_dtype],
+                                    num_cus, max_splits)
+        self.kv_dtype = kv_dtype
+        self.out_dtype = out_dtype
+        self.num_heads = num_heads
+        max_rows = max_batch if max_rows is None else max_rows
+        plan_bytes, ws_bytes = B.mla_decode_workspace_size(self.params, max_batch, max_rows)
+        self.plan_h = torch.empty(plan_bytes, dtype=torch.uint8, pin_memory=True)
+        self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
+        self._copy_done = None
+        self.variant = B.mla_decode_variant(self.params)
+
+    def plan(self, kv_indptr, kv_last_page_len=None, qo_indptr=None, stream=None):
+        """Build the plan for a batch (host arrays) and copy it to the workspace."""
+        kv_indptr = np.ascontiguousarray(kv_indptr, dtype=np.int32)
+        last = None if kv_last_page_len is None else np.ascontiguousarray(kv_last_page_len, np.int32)
+        qo = None if qo_indptr is None else np.ascontiguousarray(qo_indptr, dtype=np.int32)
+        if self._copy_done is not None:  # the previous plan copy still reads plan_h
+            self._copy_done.synchronize()
+        stream = stream or torch.cuda.current_stream(self.device)
+        st = B.mla_decode_plan(self.params, len(kv_indptr) - 1, qo, kv_indptr, last, self.plan_h,
+                               self.plan_h.numel(), self.workspace, self.workspace.numel(), stream)
+        if st != B.MLA_OK:
+            raise B.MlaError("mla_decode_plan", st)
+        self._copy_done = torch.cuda.Event()
+        self._copy_done.record(stream)
+        return self.header()
+
+    def header(self):
+        return B.read_plan(self.plan_h)[0]
+
+    def run(self, q_nope, q_rope, kv_cache, kv_indices, sm_scale, kv_scale=1.0, kv_lens=None,
+            out=None, lse=None, stream=None):
+        """out [N, H, 512] (bf16 or fp32) and lse [N, H] fp32 for the planned batch.
+
+        q_nope/q_rope: bf16 [N, H, 512] / [N, H, 64] (any strides with a unit last
+        dim). kv_cache: [pages, page_size, 576] bf16, or uint8 e4m3fn codes.
+        """
+        h = self.header()
+        N, H = h.num_rows, self.num_heads
+        if out is None:
+            dt = torch.float32 if self.out_dtype == "fp32" else torch.bfloat16
+            out = torch.empty((N, H, 512), dtype=dt, device=self.device)
+        if lse is None:
+            lse = torch.empty((N, H), dtype=torch.float32, device=self.device)
+        assert q_nope.stride(-1) == 1 and q_rope.stride(-1) == 1
+        stream = stream or torch.cuda.current_stream(self.device)
+        st = B.mla_decode(self.params, self.plan_h, self.workspace, self.workspace.numel(), q_nope,
+                          q_nope.stride(0), q_nope.stride(1), q_rope, q_rope.stride(0),
+                          q_rope.stride(1), kv_cache, kv_scale, kv_indices, kv_lens, sm_scale, out,
+                          lse, stream)
+        if st != B.MLA_OK:
+            raise B.MlaError("mla_decode", st)
+        return out, lse
+
+
+def merge_states(v_a, s_a, v_b, s_b, out=None, s_out=None, stream=None):
+    """LSE merge of two states (bf16 or fp32 v of shape [..., D], fp32 s of shape [...])."""
+    assert v_a.dtype == v_b.dtype and v_a.shape == v_b.shape
+    D = v_a.shape[-1]
+    rows = v_a.numel() // D
+    out = torch.empty_like(v_a) if out is None else out
+    s_out = torch.empty_like(s_a) if s_out is None else s_out
+    dt = B.MLA_DTYPE_FP32 if v_a.dtype == torch.float32 else B.MLA_DTYPE_BF16
+    st = B.mla_merge_states(v_a, s_a, v_b, s_b, out, s_out, rows, D, dt,
+                            stream or torch.cuda.current_stream(v_a.device))
+    if st != B.MLA_OK:
+        raise B.MlaError("mla_merge_states", st)
+    return out, s_out
+
+
+def tree_suffix_compact(tree_mask, req_to_token, prefix_lens, width, num_rows=None,
+                        num_actual_rows=None, stream=None):
+    """(page_table [rows, width] int32, cache_seqlens [rows] int32) on the device."""
+    n_actual = tree_mask.shape[0] if num_actual_rows is None else int(num_actual_rows)
+    rows = n_actual if num_rows is None else int(num_rows)
+    dev = req_to_token.device
+    table = torch.empty((rows, width), dtype=torch.int32, device=dev)
+    seqlens = torch.empty(rows, dtype=torch.int32, device=dev)
+    st = B.mla_tree_suffix_compact(tree_mask, tree_mask.stride(0), req_to_token,
+                                   req_to_token.stride(0), prefix_lens, width, rows, n_actual,
+                                   table, table.stride(0), seqlens,
+                                   stream or torch.cuda.current_stream(dev))
+    if st != B.MLA_OK:
+        raise B.MlaError("mla_tree_suffix_compact", st)
+    return table, seqlens

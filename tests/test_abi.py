@@ -1,0 +1,156 @@
+"""C-ABI library: loads, exports every declared symbol, and rejects bad
+arguments on the host with its documented status codes (no GPU work)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_mla_decode_amd as m
+from paged_mla_decode_amd import _binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "mla_decode.h")
+FAKE = 1 << 40  # a non-null, 16-byte aligned stand-in address; never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:const char\*|int32_t)\s+(mla_\w+)\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 7
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTED_SYMBOLS) == names
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(B.mla_decode_params) == 32
+    assert ctypes.sizeof(B.mla_work_item) == 32
+    assert ctypes.sizeof(B.mla_merge_item) == 16
+    assert ctypes.sizeof(B.mla_plan_header) == 48 + 8 * 7
+
+
+def test_status_strings():
+    assert m.mla_status_string(0) == "MLA_OK"
+    assert m.mla_status_string(5) == "MLA_ERR_PLAN_MISMATCH"
+    assert m.mla_status_string(99) == "MLA_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("H,variant", [(16, "hw16,hs1"), (32, "hw16,hs2"), (64, "hw16,hs4"),
+                                       (128, "hw32,hs4")])
+def test_variant_names(H, variant):
+    p = m.make_params(H, 1, num_cus=256)
+    assert variant in m.mla_decode_variant(p)
+    p8 = m.make_params(H, 64, kv_dtype=m.MLA_DTYPE_FP8_E4M3FN, out_dtype=m.MLA_DTYPE_FP32,
+                       num_cus=256)
+    assert m.mla_decode_variant(p8).endswith("kv_fp8,out_fp32>")
+
+
+@pytest.mark.parametrize("bad", [
+    dict(num_heads=48), dict(num_heads=256), dict(kv_lora_rank=256), dict(qk_rope_head_dim=128),
+    dict(page_size=0), dict(kv_dtype=1), dict(out_dtype=2)])
+def test_unsupported_params(bad):
+    kw = dict(num_heads=128, page_size=64, num_cus=256)
+    kw.update(bad)
+    p = m.make_params(**kw)
+    assert m.mla_decode_variant(p) is None
+    plan = np.zeros(1 << 16, np.uint8)
+    st = m.mla_decode_plan(p, 1, None, np.array([0, 1], np.int32), None, plan, plan.size)
+    assert st in (m.MLA_ERR_UNSUPPORTED, m.MLA_ERR_INVALID_ARG)
+
+
+def _plan(p, kv_indptr, last=None, qo=None, size=1 << 20):
+    plan = np.zeros(size, np.uint8)
+    qo = None if qo is None else np.asarray(qo, np.int32)
+    st = m.mla_decode_plan(p, len(kv_indptr) - 1, qo, np.asarray(kv_indptr, np.int32),
+                           None if last is None else np.asarray(last, np.int32), plan, size)
+    return st, plan
+
+
+def test_plan_rejects_malformed_csr():
+    p = m.make_params(16, 4, num_cus=256)
+    assert _plan(p, [0, 3, 2])[0] == m.MLA_ERR_INVALID_ARG  # decreasing indptr
+    assert _plan(p, [-1, 2])[0] == m.MLA_ERR_INVALID_ARG
+    assert _plan(p, [0, 2, 3], last=[0, 1])[0] == m.MLA_ERR_INVALID_ARG  # last_page_len < 1
+    assert _plan(p, [0, 2, 3], last=[5, 1])[0] == m.MLA_ERR_INVALID_ARG  # > page_size
+    assert _plan(p, [0, 2, 3], qo=[1, 2, 3])[0] == m.MLA_ERR_INVALID_ARG  # qo_indptr[0] != 0
+    assert _plan(p, [0, 2, 3], qo=[0, 2, 1])[0] == m.MLA_ERR_INVALID_ARG
+    assert m.mla_decode_plan(p, 1, None, None, None, np.zeros(64, np.uint8), 64) == \
+        m.MLA_ERR_INVALID_ARG
+    assert _plan(p, [0, 2, 3], last=[4, 1])[0] == m.MLA_OK
+
+
+def test_plan_buffer_too_small():
+    p = m.make_params(16, 1, num_cus=256)
+    st, _ = _plan(p, [0, 100, 200], size=64)
+    assert st == m.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_bounds_cover_actual_plans():
+    rng = np.random.default_rng(0)
+    for H in (16, 128):
+        p = m.make_params(H, 16, num_cus=256)
+        for _ in range(20):
+            B_ = int(rng.integers(1, 40))
+            npages = rng.integers(0, 400, size=B_)
+            indptr = np.concatenate([[0], np.cumsum(npages)]).astype(np.int32)
+            last = np.where(npages > 0, rng.integers(1, 17, size=B_), 1)
+            pb, wb = m.mla_decode_workspace_size(p, B_, B_)
+            st, plan = _plan(p, indptr, last, size=pb)
+            assert st == m.MLA_OK
+            h = m.read_plan(plan)[0]
+            assert h.plan_bytes <= pb and h.workspace_bytes <= wb
+
+
+def test_decode_validates_before_launch():
+    p = m.make_params(16, 1, num_cus=256)
+    st, plan = _plan(p, [0, 5])
+    h = m.read_plan(plan)[0]
+    ws = h.workspace_bytes
+
+    def call(**over):
+        args = dict(params=p, plan_h=plan, workspace_d=FAKE, workspace_bytes=ws, q_nope_d=FAKE,
+                    q_nope_stride_n=16 * 512, q_nope_stride_h=512, q_rope_d=FAKE,
+                    q_rope_stride_n=16 * 64, q_rope_stride_h=64, kv_cache_d=FAKE, kv_scale=1.0,
+                    kv_indices_d=FAKE, kv_lens_d=None, sm_scale=0.1, out_d=FAKE, lse_d=None,
+                    stream=0)
+        args.update(over)
+        return m.mla_decode(**args)
+
+    assert call(q_nope_d=None) == m.MLA_ERR_INVALID_ARG
+    assert call(kv_cache_d=None) == m.MLA_ERR_INVALID_ARG
+    assert call(out_d=FAKE + 8) == m.MLA_ERR_INVALID_ARG  # misaligned
+    assert call(q_nope_stride_h=500) == m.MLA_ERR_INVALID_ARG
+    assert call(sm_scale=float("nan")) == m.MLA_ERR_INVALID_ARG
+    assert call(kv_scale=2.0) == m.MLA_ERR_INVALID_ARG  # bf16 cache takes no scale
+    assert call(workspace_bytes=ws - 1) == m.MLA_ERR_WORKSPACE_TOO_SMALL
+    other = m.make_params(32, 1, num_cus=256)
+    assert call(params=other) == m.MLA_ERR_PLAN_MISMATCH
+    bad = plan.copy()
+    bad[:4] = 0
+    assert call(plan_h=bad) == m.MLA_ERR_INVALID_ARG
+
+
+def test_merge_and_compact_validate():
+    assert m.mla_merge_states(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 7, 0, 0) == m.MLA_ERR_INVALID_ARG
+    assert m.mla_merge_states(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 2, 0) == \
+        m.MLA_ERR_UNSUPPORTED
+    assert m.mla_merge_states(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8192, 0, 0) == \
+        m.MLA_ERR_UNSUPPORTED
+    assert m.mla_merge_states(None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 0, 0) == \
+        m.MLA_ERR_INVALID_ARG
+    assert m.mla_merge_states(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 512, 0, 0) == m.MLA_OK
+    c = m.mla_tree_suffix_compact
+    assert c(FAKE, 64, FAKE, 80, FAKE, 0, 8, 8, FAKE, 64, FAKE, 0) == m.MLA_ERR_INVALID_ARG
+    assert c(FAKE, 2048, FAKE, 2048, FAKE, 2000, 8, 8, FAKE, 2048, FAKE, 0) == m.MLA_ERR_UNSUPPORTED
+    assert c(FAKE, 64, FAKE, 80, FAKE, 64, 8, 9, FAKE, 64, FAKE, 0) == m.MLA_ERR_INVALID_ARG
+    assert c(FAKE, 64, FAKE, 80, FAKE, 64, 8, 8, FAKE, 32, FAKE, 0) == m.MLA_ERR_INVALID_ARG
+    assert c(FAKE, 32, FAKE, 80, FAKE, 64, 8, 8, FAKE, 64, FAKE, 0) == m.MLA_ERR_INVALID_ARG
+    assert c(None, 64, FAKE, 80, FAKE, 64, 8, 8, FAKE, 64, FAKE, 0) == m.MLA_ERR_INVALID_ARG
+    assert c(FAKE, 64, FAKE, 80, FAKE, 64, 0, 0, FAKE, 64, FAKE, 0) == m.MLA_OK

@@ -1,0 +1,141 @@
+"""Parity of the HIP decode path (through the C ABI) with the CPU oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import compare, require_gpu, run_decode, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp32"])
+def test_tiny(dev, out_dtype):
+    batch = workloads.tiny()
+    say(f"tiny out={out_dtype}")
+    out, lse, dec = run_decode(batch, dev, out_dtype)
+    assert dec.variant == f"mla_decode<hw16,hs1,kv_bf16,out_{out_dtype}>"
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    compare(out, lse, ref_out, ref_lse, out_dtype == "fp32", "tiny")
+
+
+LENS = [1, 31, 32, 33, 100, 257, 64, 600]
+
+
+@pytest.mark.parametrize("H", [16, 32, 64, 128])
+@pytest.mark.parametrize("ps", [1, 16, 64])
+def test_shapes(dev, H, ps):
+    batch = workloads.random_decode_batch(100 + H + ps, LENS, num_heads=H, page_size=ps)
+    say(f"shapes H={H} ps={ps}")
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    for splits in (1, 0, 4):
+        out, lse, dec = run_decode(batch, dev, "bf16", max_splits=splits, num_cus=8)
+        h = dec.header()
+        if splits == 1:
+            assert h.num_merges == 0
+        compare(out, lse, ref_out, ref_lse, False, f"H={H} ps={ps} splits={splits} merges={h.num_merges}")
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_fp32_mode_with_splits(dev, H):
+    batch = workloads.random_decode_batch(7 + H, [5, 300, 1000, 77], num_heads=H, page_size=16)
+    say(f"fp32 H={H}")
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    out, lse, dec = run_decode(batch, dev, "fp32", num_cus=4)
+    assert dec.header().num_merges > 0
+    compare(out, lse, ref_out, ref_lse, True, f"fp32 H={H}")
+
+
+@pytest.mark.parametrize("H", [16, 32, 128])
+@pytest.mark.parametrize("ps", [1, 64])
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp32"])
+def test_fp8_cache(dev, H, ps, out_dtype):
+    batch = workloads.random_decode_batch(11 + H + ps, [3, 64, 129, 500], num_heads=H, page_size=ps,
+                                          cache_dtype="fp8_e4m3fn")
+    say(f"fp8 H={H} ps={ps} out={out_dtype}")
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    out, lse, dec = run_decode(batch, dev, out_dtype, num_cus=4)
+    assert "kv_fp8" in dec.variant
+    compare(out, lse, ref_out, ref_lse, out_dtype == "fp32", f"fp8 H={H} ps={ps}")
+
+
+def test_kv_lens_clips_on_device(dev):
+    batch = workloads.random_decode_batch(21, [40, 200, 333, 64], num_heads=128, page_size=16)
+    clip = np.array([17, 200, 100, 0], np.int32)
+    say("kv_lens clip")
+    out, lse, _ = run_decode(batch, dev, "bf16", kv_lens=clip, num_cus=4)
+    # oracle over the clipped lengths: same pages, fewer tokens
+    L = clip
+    npages = (L + 15) // 16
+    kv_indptr = np.concatenate([[0], np.cumsum(npages)]).astype(np.int32)
+    kv_indices = np.concatenate([batch.kv_indices[batch.kv_indptr[b]:batch.kv_indptr[b] + npages[b]]
+                                 for b in range(batch.batch)]).astype(np.int32)
+    last = np.where(L > 0, L - 16 * (npages - 1), 1).astype(np.int32)
+    ref_out, ref_lse = oracle.mla_decode(batch.q_nope, batch.q_rope, batch.cache, kv_indptr,
+                                         kv_indices, 16, batch.sm_scale, kv_last_page_len=last)
+    compare(out, lse, ref_out, ref_lse, False, "kv_lens")
+
+
+def test_empty_requests(dev):
+    batch = workloads.random_decode_batch(22, [0, 45, 0, 1], num_heads=16, page_size=8)
+    say("empty requests")
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    for splits in (1, 0):
+        out, lse, _ = run_decode(batch, dev, "bf16", max_splits=splits, num_cus=2)
+        compare(out, lse, ref_out, ref_lse, False, f"empty splits={splits}")
+        assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_extreme_score_spread_takes_the_exact_rerun(dev, H):
+    """A token far past the first tile with a score ~150 (log2) above the rest:
+    the fixed softmax reference would overflow, so the kernel recomputes."""
+    batch = workloads.random_decode_batch(23, [300, 90], num_heads=H, page_size=1)
+    rows = workloads.token_rows(batch.kv_indptr, batch.kv_indices, batch.seq_lens, 1)
+    hot = workloads.bf16_bits_to_f32(batch.cache.reshape(-1, 576)[rows[200]])
+    qn = workloads.bf16_bits_to_f32(batch.q_nope).copy()
+    qn[0, :, :] = hot[:512] * 10.0
+    batch.q_nope = workloads.f32_to_bf16_bits(qn)
+    say(f"extreme spread H={H}")
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    assert ref_lse[0].min() - math.log(2) * 64 > 0  # the spread is really that large
+    out, lse, _ = run_decode(batch, dev, "fp32", max_splits=1)
+    compare(out, lse, ref_out, ref_lse, True, "extreme fp32")
+    out, lse, _ = run_decode(batch, dev, "bf16", max_splits=0, num_cus=2)
+    compare(out, lse, ref_out, ref_lse, False, "extreme bf16 split")
+
+
+def test_concatenated_query_through_strides(dev):
+    batch = workloads.random_decode_batch(24, [70, 5, 130], num_heads=64, page_size=4)
+    say("strided q")
+    from gpu_util import bf16_to_device
+    q_cat = np.concatenate([batch.q_nope, batch.q_rope], axis=-1)  # [N, H, 576]
+    qd = bf16_to_device(q_cat, dev)
+    out, lse, _ = run_decode(batch, dev, "bf16", q_pair=(qd[..., :512], qd[..., 512:]))
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    compare(out, lse, ref_out, ref_lse, False, "strided q")
+
+
+def test_multiple_query_rows_per_request(dev):
+    batch = workloads.random_decode_batch(25, [50, 300, 17], num_heads=128, page_size=1,
+                                          rows_per_request=4)
+    say("qo rows")
+    out, lse, _ = run_decode(batch, dev, "bf16", num_cus=4)
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    compare(out, lse, ref_out, ref_lse, False, "qo rows")
+
+
+def test_deterministic(dev):
+    batch = workloads.random_decode_batch(26, [700, 1500, 90], num_heads=128, page_size=64)
+    say("determinism")
+    a, la, _ = run_decode(batch, dev, "bf16", num_cus=8)
+    b, lb, _ = run_decode(batch, dev, "bf16", num_cus=8)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)

@@ -1,0 +1,102 @@
+"""Host planner invariants (no GPU): every (query row, token) is covered by
+exactly one work item, chunks stay inside their request and start on a tile
+boundary, split rows map to consistent partial slots and merges, and the
+items are ordered longest first. Several plans are correct; the kernel's
+result does not depend on which one is chosen, so the plan is pinned by these
+properties rather than by equality."""
+import numpy as np
+import pytest
+
+import paged_mla_decode_amd as m
+import workloads
+
+TILE = 32
+
+
+def build(p, batch):
+    pb, _ = m.mla_decode_workspace_size(p, batch.batch, batch.num_rows)
+    plan = np.zeros(pb, np.uint8)
+    qo = None if np.array_equal(batch.qo_indptr, np.arange(batch.batch + 1)) else batch.qo_indptr
+    st = m.mla_decode_plan(p, batch.batch, qo, batch.kv_indptr, batch.kv_last_page_len, plan, pb)
+    assert st == m.MLA_OK, m.mla_status_string(st)
+    return m.read_plan(plan)
+
+
+def check_invariants(p, batch, h, items, merges):
+    assert h.magic == m._binding.MLA_PLAN_MAGIC and h.num_items == len(items)
+    assert h.num_rows == batch.num_rows and h.batch == batch.batch
+    assert h.num_page_entries == batch.kv_indptr[-1]
+    lens = batch.row_seq_lens
+    row_req = np.repeat(np.arange(batch.batch), np.diff(batch.qo_indptr))
+    covered = {}
+    partial_of = {}
+    for it in items:
+        assert 0 <= it.row < batch.num_rows
+        assert it.request == row_req[it.row]
+        assert it.page_base == batch.kv_indptr[it.request]
+        assert 0 <= it.kv_begin <= it.kv_end <= lens[it.row]
+        assert it.kv_begin % TILE == 0
+        assert it.head_begin == 0 and it.num_heads == p.num_heads
+        covered.setdefault(it.row, []).append((it.kv_begin, it.kv_end))
+        if it.partial >= 0:
+            assert it.partial not in partial_of
+            partial_of[it.partial] = it
+    # exact cover of every row's tokens
+    for r in range(batch.num_rows):
+        segs = sorted(covered[r])
+        assert segs[0][0] == 0 and segs[-1][1] == lens[r]
+        for (a0, a1), (b0, b1) in zip(segs, segs[1:]):
+            assert a1 == b0
+    # split rows <=> merge items over consecutive partial slots
+    assert len(partial_of) == h.num_partials
+    merged_rows = set()
+    for mi in merges:
+        merged_rows.add(mi.row)
+        assert mi.num_partials >= 2
+        chunks = [partial_of[mi.partial_begin + k] for k in range(mi.num_partials)]
+        assert all(c.row == mi.row for c in chunks)
+        assert sorted((c.kv_begin, c.kv_end) for c in chunks) == sorted(covered[mi.row])
+    for r, segs in covered.items():
+        assert (len(segs) > 1) == (r in merged_rows)
+    # longest first
+    sizes = [it.kv_end - it.kv_begin for it in items]
+    assert sizes == sorted(sizes, reverse=True)
+    assert h.num_merges == len(merges)
+
+
+@pytest.mark.parametrize("make,H,ps", [
+    (lambda: workloads.v3(), 128, 64),
+    (lambda: workloads.v2_lite(), 16, 1),
+    (lambda: workloads.random_decode_batch(1, [0, 1, 31, 32, 33, 5000, 0, 70000], 128, 16), 128, 16),
+    (lambda: workloads.random_decode_batch(2, [7, 33], 16, 1, rows_per_request=3), 16, 1),
+])
+def test_plan_invariants(make, H, ps):
+    batch = make()
+    for cus, splits in ((256, 0), (256, 1), (80, 3), (1, 0)):
+        p = m.make_params(H, ps, num_cus=cus, max_splits=splits)
+        h, items, merges = build(p, batch)
+        check_invariants(p, batch, h, items, merges)
+        if splits == 1:
+            assert h.num_merges == 0 and h.num_partials == 0
+
+
+def test_skewed_batch_splits_the_long_request_across_the_chip():
+    batch = workloads.skewed_fp8()
+    p = m.make_params(128, 64, kv_dtype=m.MLA_DTYPE_FP8_E4M3FN, num_cus=256)
+    h, items, merges = build(p, batch)
+    check_invariants(p, batch, h, items, merges)
+    long_row = int(np.argmax(batch.seq_lens))
+    long_chunks = [it for it in items if it.row == long_row]
+    assert len(long_chunks) >= 128
+    # no chunk is much longer than the balanced share of the whole batch
+    total = int(batch.seq_lens.sum())
+    assert max(it.kv_end - it.kv_begin for it in items) <= max(512, -(-total // 256)) + TILE
+
+
+def test_empty_requests_get_an_empty_item():
+    batch = workloads.random_decode_batch(3, [0, 5, 0], 16, 4)
+    p = m.make_params(16, 4, num_cus=256)
+    h, items, merges = build(p, batch)
+    check_invariants(p, batch, h, items, merges)
+    empty = [it for it in items if it.kv_begin == it.kv_end]
+    assert sorted(it.row for it in empty) == [0, 2]
