@@ -1,0 +1,205 @@
+"""Benchmark: absorbed-MLA paged decode on the DeepSeek-V3-shaped workload.
+
+Workload: B=128 requests, H=128 heads, latent 512 + rope 64 in bf16, page size
+64 with kv_last_page_len, lengths lognormal (median 2048, sigma 0.8, clipped
+to [16, 16384]), pages scattered over the pool (seeded, workloads.v3).
+
+One step = one attention-layer call of the hot path: mla_decode (the decode
+kernel plus the merge of split-KV partials). The host plan is built once per
+batch and reused by every layer, so it is built before the timed region and
+reported separately (plan_us). Two identical copies of the inputs (different
+device addresses, about 1.2 GB together) alternate between steps so that the
+256 MB Infinity Cache cannot serve one step's latent reads from the previous
+step.
+
+value = latent-cache GB/s = (sum of KV tokens x 1152 bytes) / step time;
+also reported: decode tokens/s (query rows / step time) and the fraction of
+MI355X's 8 TB/s HBM peak. The CPU oracle is timed on the host's cores on a
+bounded prefix of the same batch (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(batch, target_s=12.0):
+    """Oracle GB/s on a prefix of the batch sized to about target_s seconds."""
+    import oracle
+
+    cal = batch.subset(range(2))
+    t0 = time.perf_counter()
+    oracle.decode_batch(cal)
+    dt = time.perf_counter() - t0
+    rate = float(cal.seq_lens.sum()) / max(dt, 1e-9)  # tokens/s
+    want = rate * target_s
+    cum = np.cumsum(batch.seq_lens.astype(np.int64))
+    n = int(min(batch.batch, max(1, np.searchsorted(cum, want) + 1)))
+    sub = batch.subset(range(n))
+    t0 = time.perf_counter()
+    oracle.decode_batch(sub)
+    dt = time.perf_counter() - t0
+    toks = int(sub.seq_lens.sum())
+    return {
+        "value": toks * batch.cache_bytes_per_token / dt / 1e9,
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"first {n} of {batch.batch} requests ({toks} KV tokens, all {batch.num_heads} heads), "
+                  f"fp64 C oracle, {dt:.1f} s",
+        "tokens_per_s": sub.num_rows / dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="v3", choices=["v3", "v2_lite", "skewed_fp8"])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share: --gpus {args.gpus} is not supported "
+              "(this build runs on a single MI355X; sharding is described, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    from paged_mla_decode_amd.decoder import PagedMlaDecoder
+
+    dev = torch.device("cuda:0")
+    make = {"v3": workloads.v3, "v2_lite": workloads.v2_lite, "skewed_fp8": workloads.skewed_fp8}
+    t0 = time.perf_counter()
+    batch = make[args.workload]()
+    log(f"workload {batch.name}: B={batch.batch} H={batch.num_heads} ps={batch.page_size} "
+        f"tokens={int(batch.seq_lens.sum())} gen {time.perf_counter() - t0:.1f}s")
+
+    def to_dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    qn = to_dev_bf16(batch.q_nope)
+    qr = to_dev_bf16(batch.q_rope)
+    if batch.cache_dtype == "bf16":
+        cache = to_dev_bf16(batch.cache)
+    else:
+        cache = torch.from_numpy(np.ascontiguousarray(batch.cache)).to(dev)
+    idx = torch.from_numpy(batch.kv_indices).to(dev)
+    sets = [(qn, qr, cache, idx), (qn.clone(), qr.clone(), cache.clone(), idx.clone())]
+
+    dec = PagedMlaDecoder(batch.num_heads, batch.page_size, max_batch=batch.batch,
+                          max_rows=batch.num_rows, kv_dtype=batch.cache_dtype, out_dtype="bf16",
+                          device=dev)
+    t0 = time.perf_counter()
+    h = dec.plan(batch.kv_indptr, batch.kv_last_page_len)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    torch.cuda.synchronize()
+    outs = [torch.empty((batch.num_rows, batch.num_heads, 512), dtype=torch.bfloat16, device=dev)
+            for _ in sets]
+    lses = [torch.empty((batch.num_rows, batch.num_heads), dtype=torch.float32, device=dev)
+            for _ in sets]
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        s = sets[i % 2]
+        if ev is not None:
+            ev[0].record(stream)
+        dec.run(s[0], s[1], s[2], s[3], batch.sm_scale, batch.kv_scale, out=outs[i % 2],
+                lse=lses[i % 2], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(b) for a, b in events])
+
+    tokens = int(batch.seq_lens.sum())
+    latent_bytes = tokens * batch.cache_bytes_per_token
+    flops = 2.0 * batch.num_heads * (576 + 512) * tokens
+    ms_per_step = elapsed * 1e3 / args.steps
+    gbs = latent_bytes / (ms_per_step * 1e-3) / 1e9
+    launch_avg_ms = float(launch_ms.mean())
+    achieved = latent_bytes / (launch_avg_ms * 1e-3) / 1e9
+    log(f"plan: items={h.num_items} merges={h.num_merges} partials={h.num_partials} "
+        f"chunk={h.chunk_tokens} plan_us={plan_us:.0f}")
+    log(f"step {ms_per_step * 1e3:.1f} us, launch avg {launch_avg_ms * 1e3:.1f} us "
+        f"(p10 {np.percentile(launch_ms, 10) * 1e3:.1f}, p90 {np.percentile(launch_ms, 90) * 1e3:.1f}), "
+        f"{gbs:.0f} GB/s, {achieved / HBM_PEAK_GBS * 100:.1f}% HBM, "
+        f"{flops / (launch_avg_ms * 1e-3) / 1e12:.0f} TFLOP/s")
+
+    res = {
+        "metric": "MLA decode latent-cache GB/s (% of HBM peak) and tokens/s, DeepSeek-V3 shapes",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if batch.cache_dtype == "bf16" else "fp8_e4m3fn cache, bf16 mfma",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{batch.name}: B={batch.batch} H={batch.num_heads} latent 512+64 "
+                        f"page_size={batch.page_size} seed={batch.seed}",
+            "batch": batch.batch, "num_heads": batch.num_heads, "kv_lora_rank": 512,
+            "qk_rope_head_dim": 64, "page_size": batch.page_size, "kv_tokens": tokens,
+            "query_rows": batch.num_rows, "parallelism": "single GPU",
+        },
+        "tokens_per_s": round(batch.num_rows / (ms_per_step * 1e-3), 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "plan_us": round(plan_us, 1),
+        "plan": {"items": h.num_items, "merges": h.num_merges, "partials": h.num_partials,
+                 "chunk_tokens": h.chunk_tokens},
+        "roofline": {
+            "kernel": "mla_decode launch (decode kernel + split-KV merge kernel)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": latent_bytes,
+            "launch_avg_us": round(launch_avg_ms * 1e3, 2),
+            "mfma_tflops": round(flops / (launch_avg_ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (launch_avg_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline(batch)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

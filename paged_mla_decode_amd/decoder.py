@@ -30,6 +30,7 @@ class PagedMlaDecoder:
         self.plan_h = torch.empty(plan_bytes, dtype=torch.uint8, pin_memory=True)
         self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
         self._copy_done = None
+        self._header = None
         self.variant = B.mla_decode_variant(self.params)
 
     def plan(self, kv_indptr, kv_last_page_len=None, qo_indptr=None, stream=None):
@@ -46,10 +47,11 @@ class PagedMlaDecoder:
             raise B.MlaError("mla_decode_plan", st)
         self._copy_done = torch.cuda.Event()
         self._copy_done.record(stream)
-        return self.header()
+        self._header = B.read_plan(self.plan_h)[0]
+        return self._header
 
     def header(self):
-        return B.read_plan(self.plan_h)[0]
+        return self._header
 
     def run(self, q_nope, q_rope, kv_cache, kv_indices, sm_scale, kv_scale=1.0, kv_lens=None,
             out=None, lse=None, stream=None):
