@@ -75,6 +75,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="v3", choices=["v3", "v2_lite", "skewed_fp8"])
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (a known-size "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share: --gpus {args.gpus} is not supported "
@@ -129,6 +132,12 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
+    if args.copy_mb:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

@@ -1,0 +1,174 @@
+// Device-side helpers shared by the decode kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace mla {
+namespace dev {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kOverflowSlack = 64.0f;  // log2 units: probabilities stay below 2^64
+
+// ---------------------------------------------------------------------------
+// Small device helpers
+// ---------------------------------------------------------------------------
+
+// Barriers written as inline assembly with a memory clobber, so that the
+// compiler neither moves memory operations across them nor adds waits of its
+// own. Direct-to-LDS loads complete in issue order with the other vector
+// memory loads, so "vmcnt <= N" means everything but the N most recent loads
+// has landed in LDS.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// Wait until at most `pending` tiles of loads (kLoads instructions each) are
+// outstanding, then a workgroup barrier. pending is wave-uniform, in [0, kMax].
+template <int kMax, int kLoads>
+__device__ __forceinline__ void wait_tiles_barrier(int pending) {
+    if constexpr (kMax >= 1) {
+        if (pending >= kMax) {
+            wait_vmcnt_barrier<kMax * kLoads>();
+            return;
+        }
+        wait_tiles_barrier<kMax - 1, kLoads>(pending);
+    } else {
+        wait_vmcnt_barrier<0>();
+    }
+}
+
+// All of this wave's LDS accesses are complete, then a workgroup barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-byte direct global->LDS load: lane l's 16 bytes land at lds + 16 l.
+// Issued as inline assembly so that the compiler's wait-count model never sees
+// these LDS writes (it would otherwise drain every load before each LDS read);
+// wait_vmcnt_barrier() orders them instead. M0 holds the wave-uniform LDS
+// address; one wait state separates its write from the load.
+__device__ __forceinline__ void dma16(const void* src, LDS_AS void* dst) {
+    const uint32_t lds = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(src)
+                 : "memory", "m0");
+}
+
+// Value held by lane ^ 32 / lane ^ 16, combined with the own value.
+__device__ __forceinline__ float max_xor32(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Eight e4m3fn codes (two dwords) -> eight bf16 values, exact.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned lo, unsigned hi) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return r;
+}
+
+typedef int i32x4s __attribute__((ext_vector_type(4)));
+typedef int i32x8s __attribute__((ext_vector_type(8)));
+typedef int i32x16s __attribute__((ext_vector_type(16)));
+// Scalar buffer loads (SMEM, tracked by lgkmcnt, range-checked by the buffer
+// descriptor: dwords past num_records read as 0).
+__device__ i32x8s sbuffer_load_x8(i32x4s rsrc, int byte_off, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v8i32");
+__device__ i32x16s sbuffer_load_x16(i32x4s rsrc, int byte_off, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v16i32");
+
+// Raw buffer descriptor for a dword array of n entries (gfx9 family dword 3).
+__device__ __forceinline__ i32x4s make_rsrc(const void* base, int64_t n_dwords) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t bytes = (uint64_t)n_dwords * 4u;
+    i32x4s r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)(uint32_t)((a >> 32) & 0xFFFFu);  // stride 0
+    r[2] = (int)(uint32_t)(bytes > 0xFFFFFFFFull ? 0xFFFFFFFFull : bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// v[off] for a per-lane off in [0, N), from a wave-uniform (SGPR) vector.
+template <int N, class V>
+__device__ __forceinline__ int select_lane(const V& v, int off) {
+    int x = v[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) x = off == j ? v[j] : x;
+    return x;
+}
+
+// Software pipeline over N unrolled steps: the LDS operand of step i + D is
+// requested right after step i's MFMA is issued, so D reads are in flight
+// while the matrix core works. With one wave per SIMD there is no other wave
+// to hide LDS latency behind, so this is what keeps the MFMA pipe busy.
+template <int N, int D, int kReads, int kMfmas, class Load, class Use>
+__device__ __forceinline__ void pipelined(Load load, Use use) {
+    using Op = decltype(load(0));
+    Op buf[D];
+#pragma unroll
+    for (int i = 0; i < D && i < N; ++i) buf[i] = load(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const Op cur = buf[i % D];
+        use(i, cur);
+        if (i + D < N) buf[i % D] = load(i + D);
+    }
+    // Pin the interleave: the prologue reads, then per step its MFMAs followed
+    // by the reads D steps ahead (the scheduler would otherwise sink every read
+    // next to its MFMA under register pressure).
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads * (D < N ? D : N), 0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas, 0);
+        if (i + D < N) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+    }
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace dev
+}  // namespace mla

@@ -30,128 +30,13 @@
 
 #include <type_traits>
 
+#include "mla_device.h"
 #include "mla_internal.h"
 #include "mla_tile_layout.h"
 
 namespace mla {
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
-typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kOverflowSlack = 64.0f;  // log2 units: probabilities stay below 2^64
-
-// ---------------------------------------------------------------------------
-// Small device helpers
-// ---------------------------------------------------------------------------
-
-// Barriers written as inline assembly with a memory clobber, so that the
-// compiler neither moves memory operations across them nor adds waits of its
-// own. Direct-to-LDS loads complete in issue order with the other vector
-// memory loads, so "vmcnt <= N" means everything but the N most recent loads
-// has landed in LDS.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_barrier() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-// All of this wave's LDS accesses are complete, then a workgroup barrier.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// 16-byte direct global->LDS load: lane l's 16 bytes land at lds + 16 l.
-// Issued as inline assembly so that the compiler's wait-count model never sees
-// these LDS writes (it would otherwise drain every load before each LDS read);
-// wait_vmcnt_barrier() orders them instead. M0 holds the wave-uniform LDS
-// address; one wait state separates its write from the load.
-__device__ __forceinline__ void dma16(const void* src, LDS_AS void* dst) {
-    const uint32_t lds = (uint32_t)(uintptr_t)dst;
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(lds), "v"(src)
-                 : "memory", "m0");
-}
-
-// Value held by lane ^ 32 / lane ^ 16, combined with the own value.
-__device__ __forceinline__ float max_xor32(float v) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor16(float v) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor32(float v) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_xor16(float v) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
-    return *reinterpret_cast<const bf16x8*>(p);
-}
-
-// Eight e4m3fn codes (two dwords) -> eight bf16 values, exact.
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned lo, unsigned hi) {
-    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-    bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-    bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-    bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-    return r;
-}
-
-typedef int i32x4s __attribute__((ext_vector_type(4)));
-typedef int i32x8s __attribute__((ext_vector_type(8)));
-typedef int i32x16s __attribute__((ext_vector_type(16)));
-// Scalar buffer loads (SMEM, tracked by lgkmcnt, range-checked by the buffer
-// descriptor: dwords past num_records read as 0).
-__device__ i32x8s sbuffer_load_x8(i32x4s rsrc, int byte_off, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v8i32");
-__device__ i32x16s sbuffer_load_x16(i32x4s rsrc, int byte_off, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v16i32");
-
-// Raw buffer descriptor for a dword array of n entries (gfx9 family dword 3).
-__device__ __forceinline__ i32x4s make_rsrc(const void* base, int64_t n_dwords) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    const uint64_t bytes = (uint64_t)n_dwords * 4u;
-    i32x4s r;
-    r[0] = (int)(uint32_t)a;
-    r[1] = (int)(uint32_t)((a >> 32) & 0xFFFFu);  // stride 0
-    r[2] = (int)(uint32_t)(bytes > 0xFFFFFFFFull ? 0xFFFFFFFFull : bytes);
-    r[3] = 0x00020000;
-    return r;
-}
-
-// v[off] for a per-lane off in [0, N), from a wave-uniform (SGPR) vector.
-template <int N, class V>
-__device__ __forceinline__ int select_lane(const V& v, int off) {
-    int x = v[0];
-#pragma unroll
-    for (int j = 1; j < N; ++j) x = off == j ? v[j] : x;
-    return x;
-}
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
+using namespace dev;
 
 // ---------------------------------------------------------------------------
 // The decode kernel
@@ -168,10 +53,13 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
     constexpr int kSteps = SA::kSteps;
     constexpr int kDBlocks = PA::kDBlocks;
     static_assert(kLoadsMax + kNTok < 64, "vmcnt budget");
-    // The scheduler may not hoist LDS reads more than this many MFMA steps
-    // ahead: unbounded hoisting costs four VGPRs per operand in flight.
-    constexpr int kSchedStep = 2;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * L::kTileBytes];
+    // LDS operand reads kept in flight ahead of the MFMAs.
+    constexpr int kPipe = HW == 32 ? ((KV8 && OUT32) ? 2 : 4) : 3;
+    // Ring of kStages tile buffers: tiles i+1 .. i+kStages-1 are in flight
+    // while tile i is computed. Bounded by LDS and by the 6-bit vmcnt.
+    constexpr int kStages = Stages<HW, HS, KV8, OUT32>::value;
+    static_assert((kStages - 1) * kLoadsMax < 64, "vmcnt budget");
+    __shared__ __attribute__((aligned(1024))) char smem[kStages * L::kTileBytes];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -286,18 +174,16 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
         fetch_idx(0);
         auto tile_step = [&](const LDS_AS char* __restrict__ T, LDS_AS char* __restrict__ N, int i) {
             const int tstart = kv_begin + i * kTile;
-            if (i + 1 < ntiles) {
+            const int ahead = i + kStages - 1;  // the tile whose loads this step issues
+            if (ahead < ntiles) {
                 const uint8_t* rowp[kNTok];
-                resolve_rows(i + 1, rowp);
-                if (i + 2 < ntiles) fetch_idx(i + 2);
+                resolve_rows(ahead, rowp);
+                if (ahead + 1 < ntiles) fetch_idx(ahead + 1);
                 issue_tile(N, rowp);
             }
-            if (i < 0) return;
-            // Outstanding after tile i's loads: those of tile i+1, if any.
-            if (i + 1 < ntiles)
-                wait_vmcnt_barrier<kLoadsMin>();
-            else
-                wait_vmcnt_barrier<0>();
+            if (i < 0) return;  // pipeline fill
+            // Tiles issued after tile i and still outstanding: min(kStages-1, ntiles-1-i).
+            wait_tiles_barrier<kStages - 1, kLoadsMin>(min(kStages - 1, ntiles - 1 - i));
 
             const int nvalid = min(kTile, kv_end - tstart);
 
@@ -305,41 +191,37 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
             float sv[NV];
             if constexpr (HW == 32) {
                 f32x16 S = {};
-#pragma unroll
-                for (int s = 0; s < kSteps; ++s) {
+                auto load = [&](int s) -> bf16x8 {
                     const int off = sbase[SA::base_index(s, 0)] + SA::delta(s);
-                    bf16x8 A;
                     if constexpr (KV8) {
                         const i32x2 raw = *(const LDS_AS i32x2*)(T + off);
-                        A = fp8x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]);
+                        return fp8x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]);
                     } else {
-                        A = *(const LDS_AS bf16x8*)(T + off);
+                        return *(const LDS_AS bf16x8*)(T + off);
                     }
-                    S = mfma32(A, q[s], S);
-                    if ((s + 1) % kSchedStep == 0) __builtin_amdgcn_sched_barrier(0);
-                }
+                };
+                pipelined<kSteps, kPipe, 1, 1>(load, [&](int s, bf16x8 A) { S = mfma32(A, q[s], S); });
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sv[r] = S[r];
             } else {
                 f32x4 S0 = {}, S1 = {};
-#pragma unroll
-                for (int s = 0; s < kSteps; ++s) {
+                struct Pair { bf16x8 a0, a1; };
+                auto load = [&](int s) -> Pair {
                     const int off0 = sbase[SA::base_index(s, 0)] + SA::delta(s);
                     const int off1 = sbase[SA::base_index(s, 1)] + SA::delta(s);
-                    bf16x8 A0, A1;
                     if constexpr (KV8) {
                         const i32x2 r0 = *(const LDS_AS i32x2*)(T + off0);
                         const i32x2 r1 = *(const LDS_AS i32x2*)(T + off1);
-                        A0 = fp8x8_to_bf16((unsigned)r0[0], (unsigned)r0[1]);
-                        A1 = fp8x8_to_bf16((unsigned)r1[0], (unsigned)r1[1]);
+                        return {fp8x8_to_bf16((unsigned)r0[0], (unsigned)r0[1]),
+                                fp8x8_to_bf16((unsigned)r1[0], (unsigned)r1[1])};
                     } else {
-                        A0 = *(const LDS_AS bf16x8*)(T + off0);
-                        A1 = *(const LDS_AS bf16x8*)(T + off1);
+                        return {*(const LDS_AS bf16x8*)(T + off0), *(const LDS_AS bf16x8*)(T + off1)};
                     }
-                    S0 = mfma16(A0, q[s], S0);
-                    S1 = mfma16(A1, q[s], S1);
-                    if ((s + 1) % kSchedStep == 0) __builtin_amdgcn_sched_barrier(0);
-                }
+                };
+                pipelined<kSteps, kPipe, 2, 2>(load, [&](int s, Pair A) {
+                    S0 = mfma16(A.a0, q[s], S0);
+                    S1 = mfma16(A.a1, q[s], S1);
+                });
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     sv[r] = S0[r];
@@ -373,44 +255,51 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
 
             // ---- O^T += C^T . P^T ----
             constexpr int kKK = HW == 32 ? 2 : 1;
+            bf16x8 P[kKK], Plo[kKK];
 #pragma unroll
-            for (int kk = 0; kk < kKK; ++kk) {
-                bf16x8 P, Plo;
+            for (int kk = 0; kk < kKK; ++kk)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    P[e] = (__bf16)p[8 * kk + e];
-                    if (OUT32) Plo[e] = (__bf16)(p[8 * kk + e] - (float)P[e]);
+                    P[kk][e] = (__bf16)p[8 * kk + e];
+                    if (OUT32) Plo[kk][e] = (__bf16)(p[8 * kk + e] - (float)P[kk][e]);
                 }
-#pragma unroll
-                for (int md = 0; md < kDBlocks; ++md) {
-                    const int pb = pbase[PA::base_index(md)];
-                    bf16x8 A;
-                    if constexpr (KV8) {
-                        const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                            (LDS_AS i32x2*)(T + pb + PA::delta(md, kk, 0)));
-                        A = fp8x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]);
-                    } else {
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (LDS_AS i16x4*)(T + pb + PA::delta(md, kk, 0)));
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (LDS_AS i16x4*)(T + pb + PA::delta(md, kk, 1)));
-                        A = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    }
-                    if constexpr (HW == 32) {
-                        O32[md] = mfma32(A, P, O32[md]);
-                        if (OUT32) O32[md] = mfma32(A, Plo, O32[md]);
-                    } else {
-                        O16[md] = mfma16(A, P, O16[md]);
-                        if (OUT32) O16[md] = mfma16(A, Plo, O16[md]);
-                    }
-                    if ((md + 1) % kSchedStep == 0) __builtin_amdgcn_sched_barrier(0);
+            // Step j covers output block md = j % kDBlocks of token half kk = j / kDBlocks.
+            auto load_pv = [&](int j) -> bf16x8 {
+                const int md = j % kDBlocks, kk = j / kDBlocks;
+                const int pb = pbase[PA::base_index(md)];
+                if constexpr (KV8) {
+                    const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (LDS_AS i32x2*)(T + pb + PA::delta(md, kk, 0)));
+                    return fp8x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]);
+                } else {
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (LDS_AS i16x4*)(T + pb + PA::delta(md, kk, 0)));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (LDS_AS i16x4*)(T + pb + PA::delta(md, kk, 1)));
+                    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
-            }
+            };
+            pipelined<kKK * kDBlocks, kPipe, KV8 ? 1 : 2, OUT32 ? 2 : 1>(load_pv, [&](int j, bf16x8 A) {
+                const int md = j % kDBlocks, kk = j / kDBlocks;
+                if constexpr (HW == 32) {
+                    O32[md] = mfma32(A, P[kk], O32[md]);
+                    if (OUT32) O32[md] = mfma32(A, Plo[kk], O32[md]);
+                } else {
+                    O16[md] = mfma16(A, P[kk], O16[md]);
+                    if (OUT32) O16[md] = mfma16(A, Plo[kk], O16[md]);
+                }
+            });
             lds_barrier();  // everyone is done with this buffer before it is refilled
         };
-        for (int i = -1; i < ntiles; ++i) {
-            const int cur = (i & 1) * L::kTileBytes;  // i = -1 computes nothing and fills buffer 0
-            tile_step((const LDS_AS char*)smem + cur, (LDS_AS char*)smem + (L::kTileBytes - cur), i);
+        // Tile t lives in buffer t % kStages. Step i computes tile i and fills
+        // the buffer of tile i-1 (freed by the previous step) with tile
+        // i + kStages - 1; steps i < 0 only fill the pipeline.
+        int cur = 1 % kStages;  // buffer of tile -(kStages-1)
+        for (int i = -(kStages - 1); i < ntiles; ++i) {
+            const int nxt = cur == 0 ? kStages - 1 : cur - 1;  // buffer of tile i-1 = tile i+kStages-1
+            tile_step((const LDS_AS char*)smem + cur * L::kTileBytes,
+                      (LDS_AS char*)smem + nxt * L::kTileBytes, i);
+            cur = cur + 1 == kStages ? 0 : cur + 1;
         }
     }
     // Did any head of the workgroup outgrow its reference? All waves must agree,

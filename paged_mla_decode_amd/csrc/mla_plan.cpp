@@ -42,8 +42,8 @@ bool select_variant(const mla_decode_params* p, Variant* v) {
     if (p->out_dtype != MLA_DTYPE_BF16 && p->out_dtype != MLA_DTYPE_FP32) return false;
     switch (p->num_heads) {
         case 128: *v = Variant{32, 4, 1, 512}; return true;
-        case 64: *v = Variant{16, 4, 2, 256}; return true;
-        case 32: *v = Variant{16, 2, 2, 128}; return true;
+        case 64: *v = Variant{16, 4, 1, 256}; return true;
+        case 32: *v = Variant{16, 2, 1, 128}; return true;
         case 16: *v = Variant{16, 1, 2, 128}; return true;
         default: return false;
     }

@@ -148,4 +148,46 @@ struct PvAddr {
     }
 };
 
+// ---- P . latent with the latent columns split across the 4 waves (H=128) ----
+// Wave w computes output blocks 4w .. 4w+3 (latent columns 128w .. 128w+127)
+// for all heads; its transposed reads are those of PvAddr<32> for block
+// 4w + md, i.e. the same per-lane bases plus a wave-uniform offset.
+template <bool KV8>
+struct PvSplitAddr {
+    using P = PvAddr<32, KV8>;
+    static constexpr int kBlocksPerWave = 4;
+    static constexpr int kWaveStride = KV8 ? 4096 : 8192;
+    static MLA_HD int reference(int lane, int w, int md, int kk, int hi) {
+        return P::reference(lane, kBlocksPerWave * w + md, kk, hi);
+    }
+    static MLA_HD int decomposed(int lane, int w, int md, int kk, int hi) {
+        return P::base(lane, P::base_index(md)) + w * kWaveStride + P::delta(md, kk, hi);
+    }
+};
+
+// Probabilities shared between the waves of the H=128 kernel: bf16
+// [128 heads][32 tokens], rows padded to 80 bytes so that the 16-byte accesses
+// of 16 consecutive heads fall on distinct LDS banks.
+struct PBuf {
+    static constexpr int kRow = 80;
+    static constexpr int kBytes = 128 * kRow;
+    // 8 consecutive tokens (16 bytes) starting at token 16 kk + 8 g of head h.
+    static MLA_HD int offset(int h, int kk, int g) { return h * kRow + (16 * kk + 8 * g) * 2; }
+};
+
+// Pipeline depth (tile buffers in LDS) of a decode kernel instantiation.
+// Bounded by 160 KiB of LDS per CU and by vmcnt (6 bits): the loads of
+// stages-1 tiles must be countable.
+template <int HW, int HS, bool KV8, bool OUT32>
+struct Stages {
+    static constexpr int kLoads = (TileLayout<KV8>::kNB + HS - 1) / HS;
+    static constexpr int kByLds = (144 * 1024) / TileLayout<KV8>::kTileBytes;
+    static constexpr int kByCnt = 1 + 63 / kLoads;
+    // Four or more stages of the 32-heads-per-wave variant push its register
+    // allocation (query + accumulators fill the file) into spilling.
+    static constexpr int kCap = HW == 32 ? ((KV8 || OUT32) ? 2 : 3) : 6;
+    static constexpr int value = kByLds < kByCnt ? (kByLds < kCap ? kByLds : kCap)
+                                                 : (kByCnt < kCap ? kByCnt : kCap);
+};
+
 }  // namespace mla

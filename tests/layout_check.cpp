@@ -68,6 +68,35 @@ void check_pv() {
                 }
 }
 
+template <bool KV8>
+void check_pv_split() {
+    using S = PvSplitAddr<KV8>;
+    for (int lane = 0; lane < 64; ++lane)
+        for (int w = 0; w < 4; ++w)
+            for (int md = 0; md < S::kBlocksPerWave; ++md)
+                for (int kk = 0; kk < 2; ++kk)
+                    for (int hi = 0; hi < (KV8 ? 1 : 2); ++hi) {
+                        const int ref = S::reference(lane, w, md, kk, hi);
+                        const int dec = S::decomposed(lane, w, md, kk, hi);
+                        CHECK(ref == dec, "pv split kv8=%d lane=%d w=%d md=%d kk=%d hi=%d", KV8, lane, w, md, kk, hi);
+                    }
+}
+
+void check_pbuf() {
+    std::set<int> offs;
+    for (int h = 0; h < 128; ++h)
+        for (int kk = 0; kk < 2; ++kk)
+            for (int g = 0; g < 2; ++g) {
+                const int o = PBuf::offset(h, kk, g);
+                CHECK(o % 16 == 0 && o + 16 <= PBuf::kBytes, "pbuf offset");
+                CHECK(offs.insert(o).second, "pbuf overlap");
+            }
+    // 16 consecutive heads at the same token chunk start on 16 distinct 4-bank groups.
+    std::set<int> banks;
+    for (int h = 0; h < 16; ++h) banks.insert((PBuf::offset(h, 0, 0) / 4) % 64 / 4);
+    CHECK(banks.size() == 16, "pbuf bank spread %zu", banks.size());
+}
+
 int main() {
     check_dma<false>();
     check_dma<true>();
@@ -79,6 +108,9 @@ int main() {
     check_pv<32, true>();
     check_pv<16, false>();
     check_pv<16, true>();
+    check_pv_split<false>();
+    check_pv_split<true>();
+    check_pbuf();
     if (failures) {
         std::printf("FAILED: %d\n", failures);
         return 1;
