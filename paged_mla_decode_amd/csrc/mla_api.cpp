@@ -136,6 +136,9 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
     a.part_lse = reinterpret_cast<float*>(const_cast<char*>(ws) + h->partial_lse_offset);
     a.num_heads = params->num_heads;
     a.page_size = params->page_size;
+    a.page_shift = -1;
+    for (int b = 0; b < 31; ++b)
+        if (params->page_size == (1 << b)) a.page_shift = b;
     a.scale_log2 = (float)((double)sm_scale * (double)kv_scale * 1.4426950408889634);
     a.out_scale = kv_scale;
     int err = launch_decode(v, params->kv_dtype, params->out_dtype, a, h->num_items, stream);

@@ -73,6 +73,16 @@ __device__ __forceinline__ void dma16(const void* src, LDS_AS void* dst) {
                  : "memory", "m0");
 }
 
+// 4-byte direct global->LDS load: lane l's dword lands at lds + 4 l. Same
+// ordering rules as dma16.
+__device__ __forceinline__ void dma4(const void* src, LDS_AS void* dst) {
+    const uint32_t lds = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(lds), "v"(src)
+                 : "memory", "m0");
+}
+
 // Value held by lane ^ 32 / lane ^ 16, combined with the own value.
 __device__ __forceinline__ float max_xor32(float v) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -51,7 +51,8 @@ struct DecodeArgs {
     float* part_lse;
     int32_t num_heads;
     int32_t page_size;
-    float scale_log2;  // sm_scale * kv_scale * log2(e)
+    int32_t page_shift;  // log2(page_size) when it is a power of two, else -1
+    float scale_log2;    // sm_scale * kv_scale * log2(e)
     float out_scale;   // kv_scale (fp8 cache) or 1
 };
 
@@ -67,6 +68,9 @@ struct MergePartialsArgs {
 // Kernel launchers (device code lives in mla_kernels.hip). Return hipError_t as int.
 int launch_decode(const Variant& v, int kv_dtype, int out_dtype, const DecodeArgs& a,
                   int num_items, void* stream);
+// The 128-head kernel (latent columns split across the waves), mla_decode_h128.hip.
+int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num_items,
+                       void* stream);
 int launch_merge_partials(int out_dtype, const MergePartialsArgs& a, int num_merges,
                           void* stream);
 int launch_merge_states(const void* v_a, const float* s_a, const void* v_b, const float* s_b,

@@ -532,7 +532,7 @@ int launch_decode(const Variant& v, int kv_dtype, int out_dtype, const DecodeArg
                   void* stream) {
     hipStream_t s = (hipStream_t)stream;
     if (num_items <= 0) return 0;
-    if (v.hw == 32 && v.hs == 4) return launch_decode_hs<32, 4>(kv_dtype, out_dtype, a, num_items, s);
+    if (v.hw == 32 && v.hs == 4) return launch_decode_h128(kv_dtype, out_dtype, a, num_items, stream);
     if (v.hw == 16 && v.hs == 1) return launch_decode_hs<16, 1>(kv_dtype, out_dtype, a, num_items, s);
     if (v.hw == 16 && v.hs == 2) return launch_decode_hs<16, 2>(kv_dtype, out_dtype, a, num_items, s);
     if (v.hw == 16 && v.hs == 4) return launch_decode_hs<16, 4>(kv_dtype, out_dtype, a, num_items, s);

@@ -148,21 +148,84 @@ struct PvAddr {
     }
 };
 
-// ---- P . latent with the latent columns split across the 4 waves (H=128) ----
-// Wave w computes output blocks 4w .. 4w+3 (latent columns 128w .. 128w+127)
-// for all heads; its transposed reads are those of PvAddr<32> for block
-// 4w + md, i.e. the same per-lane bases plus a wave-uniform offset.
+// ---- Layout of the 128-head kernel ----
+// The tile geometry of TileLayout, with a swizzle chosen for that kernel's
+// reads: slot = chunk ^ ((t / kTPL) % kCG), where kTPL tokens share one
+// 256-byte LDS line (64 banks of 4 bytes). The sixteen lanes one pass of a
+// 16-byte read serves hold sixteen consecutive tokens at one chunk; this
+// swizzle puts them on the 16 distinct 16-byte bank groups of a line.
+//
+// Score operand: 16-byte reads. Lane l holds token perm(l % 32) (bits 2 and 3
+// swapped, so that the accumulator rows a lane owns are eight consecutive
+// tokens) and 16-byte granule 2 s + l / 32 of the row. bf16: one read is one
+// MFMA k-slice (36 reads per tile). fp8: one read holds the k-slices of two
+// MFMAs (18 reads per tile); the query is loaded in the matching feature order.
+//
+// P . latent operand: transposed reads (ds_read_b64_tr_b16 / _b8) of output
+// block 4 md + w for wave w (latent columns 128 md + 32 w .. +31), token half
+// kk: a per-lane, per-wave base (one per 4-token half of a bf16 read) plus an
+// immediate in (md, kk). In output round md the four waves together own 128
+// consecutive columns.
 template <bool KV8>
-struct PvSplitAddr {
-    using P = PvAddr<32, KV8>;
-    static constexpr int kBlocksPerWave = 4;
-    static constexpr int kWaveStride = KV8 ? 4096 : 8192;
-    static MLA_HD int reference(int lane, int w, int md, int kk, int hi) {
-        return P::reference(lane, kBlocksPerWave * w + md, kk, hi);
+struct H128Layout {
+    using G = TileLayout<KV8>;
+    static constexpr int kTile = G::kTile, kRowBytes = G::kRowBytes, kCPT = G::kCPT;
+    static constexpr int kCG = G::kCG, kTPB = G::kTPB, kNTB = G::kNTB, kNB = G::kNB;
+    static constexpr int kTileBytes = G::kTileBytes;
+    static constexpr int kTPL = 256 / (kCG * 16);  // tokens per 256-byte line: 2 | 4
+
+    static MLA_HD constexpr int swz(int t) { return (t / kTPL) % kCG; }
+    static MLA_HD constexpr int chunk_offset(int t, int j) {
+        return ((j / kCG) * kNTB + t / kTPB) * 1024 + ((t % kTPB) * kCG + ((j % kCG) ^ swz(t))) * 16;
     }
-    static MLA_HD int decomposed(int lane, int w, int md, int kk, int hi) {
-        return P::base(lane, P::base_index(md)) + w * kWaveStride + P::delta(md, kk, hi);
+    // Direct load of block (chunk group cg, token block tb): lane -> (token, chunk).
+    static MLA_HD constexpr int block_token(int tb, int lane) { return tb * kTPB + lane / kCG; }
+    static MLA_HD constexpr int block_chunk(int cg, int tb, int lane) {
+        return cg * kCG + ((lane % kCG) ^ swz(block_token(tb, lane)));
     }
+
+    static constexpr int kScoreReads = KV8 ? 18 : 36;
+    static constexpr int kScoreBases = kCG / 2;
+    static MLA_HD constexpr int score_token(int lane) {
+        const int m = lane & 31;
+        return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1);
+    }
+    static MLA_HD constexpr int score_ref(int lane, int s) {
+        return chunk_offset(score_token(lane), 2 * s + (lane >> 5));
+    }
+    static MLA_HD constexpr int score_base_index(int s) { return s % kScoreBases; }
+    static MLA_HD constexpr int score_delta(int s) { return score_ref(0, s) - score_ref(0, score_base_index(s)); }
+    // First of the 8 features lane group g supplies to MFMA k-slice u (u < 36).
+    static MLA_HD constexpr int q_feature(int u, int g) {
+        return KV8 ? 32 * (u / 2) + 16 * g + 8 * (u % 2) : 16 * u + 8 * g;
+    }
+
+    static constexpr int kPvBases = KV8 ? 1 : 2;
+    // Byte offset lane `lane` reads for output block blk (32 latent columns),
+    // token half kk, 4-token half hi (bf16 only).
+    static MLA_HD constexpr int pv_ref(int lane, int blk, int kk, int hi) {
+        const int grp = lane >> 4, q = lane & 15;
+        const int rowb = 16 * kk + 8 * (grp >> 1);
+        const int colb = 32 * blk + 16 * (grp & 1);
+        const int t = KV8 ? rowb + (q >> 1) : rowb + (q >> 2) + 4 * hi;
+        const int cbyte = KV8 ? colb + 8 * (q & 1) : 2 * (colb + 4 * (q & 3));
+        return chunk_offset(t, cbyte >> 4) + (cbyte & 15);
+    }
+    static MLA_HD constexpr int pv_base(int lane, int w, int hi) { return pv_ref(lane, w, 0, hi); }
+    static MLA_HD constexpr int pv_delta(int md, int kk) { return pv_ref(0, 4 * md, kk, 0) - pv_ref(0, 0, 0, 0); }
+    // Latent column of accumulator value r of output block 4 md + w, lane group g.
+    static MLA_HD constexpr int column(int w, int md, int g, int r) {
+        return 128 * md + 32 * w + 8 * (r / 4) + 4 * g + r % 4;
+    }
+};
+
+// Output staging of the H=128 kernel: one round of [128 heads][128 columns]
+// fp32, rows padded to 528 bytes so that 16 consecutive heads at the same
+// column land on 16 distinct 4-bank groups.
+struct OutStage {
+    static constexpr int kRow = 528;
+    static constexpr int kBytes = 128 * kRow;
+    static MLA_HD int offset(int h, int col) { return h * kRow + 4 * col; }
 };
 
 // Probabilities shared between the waves of the H=128 kernel: bf16

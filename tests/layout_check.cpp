@@ -69,17 +69,90 @@ void check_pv() {
 }
 
 template <bool KV8>
-void check_pv_split() {
-    using S = PvSplitAddr<KV8>;
+void check_h128() {
+    using L = H128Layout<KV8>;
+    // direct loads cover every (token, chunk) of a tile once, in lane order within a block
+    std::set<std::pair<int, int>> seen;
+    for (int b = 0; b < L::kNB; ++b) {
+        const int tb = b % L::kNTB, cg = b / L::kNTB;
+        for (int lane = 0; lane < 64; ++lane) {
+            const int t = L::block_token(tb, lane), j = L::block_chunk(cg, tb, lane);
+            CHECK(t >= 0 && t < L::kTile && j >= 0 && j < L::kCPT, "h128 dma out of tile kv8=%d", KV8);
+            CHECK(L::chunk_offset(t, j) == b * 1024 + lane * 16, "h128 dma slot kv8=%d b=%d lane=%d", KV8, b, lane);
+            CHECK(L::block_chunk(cg, tb, lane) == L::block_chunk(0, tb, lane) + cg * L::kCG, "h128 dma chunk group");
+            CHECK(seen.insert({t, j}).second, "h128 dma duplicate kv8=%d", KV8);
+        }
+    }
+    CHECK((int)seen.size() == L::kTile * L::kCPT, "h128 dma coverage kv8=%d", KV8);
+    // score reads: decomposition, coverage, and one 16-byte bank group per lane of each 16-lane pass
+    std::set<int> all;
+    for (int s = 0; s < L::kScoreReads; ++s) {
+        for (int lane = 0; lane < 64; ++lane) {
+            const int ref = L::score_ref(lane, s);
+            CHECK(ref == L::score_ref(lane, L::score_base_index(s)) + L::score_delta(s),
+                  "h128 score kv8=%d lane=%d s=%d", KV8, lane, s);
+            CHECK(ref % 16 == 0 && ref >= 0 && ref + 16 <= L::kTileBytes, "h128 score range");
+            CHECK(all.insert(ref).second, "h128 score overlap");
+        }
+        for (int p = 0; p < 4; ++p) {
+            std::set<int> banks;
+            for (int lane = 16 * p; lane < 16 * p + 16; ++lane) banks.insert((L::score_ref(lane, s) / 16) % 16);
+            CHECK(banks.size() == 16, "h128 score bank conflict kv8=%d s=%d pass=%d (%zu groups)", KV8, s, p, banks.size());
+        }
+    }
+    CHECK((int)all.size() == L::kTileBytes / 16, "h128 score coverage");
+    // query feature order: every feature once per lane group pair
+    std::set<int> feats;
+    for (int u = 0; u < 36; ++u)
+        for (int g = 0; g < 2; ++g) {
+            const int f = L::q_feature(u, g);
+            CHECK(f % 8 == 0 && f < 576 && (f < 512) == (u < 32), "h128 q feature");
+            CHECK(feats.insert(f).second, "h128 q feature duplicate");
+            // the features lane group g of k-slice u multiplies are the ones it reads
+            const int gran = KV8 ? 2 * (u / 2) + g : 2 * u + g;
+            const int byte0 = KV8 ? 8 * (u % 2) : 0;
+            CHECK(f == (KV8 ? 16 * gran + byte0 : 8 * gran), "h128 q feature vs granule");
+        }
+    // P . latent reads: decomposition and the general kernel's addressing of the same block
+    using P = PvAddr<32, KV8>;
+    std::set<int> cols;
     for (int lane = 0; lane < 64; ++lane)
         for (int w = 0; w < 4; ++w)
-            for (int md = 0; md < S::kBlocksPerWave; ++md)
+            for (int md = 0; md < 4; ++md) {
                 for (int kk = 0; kk < 2; ++kk)
-                    for (int hi = 0; hi < (KV8 ? 1 : 2); ++hi) {
-                        const int ref = S::reference(lane, w, md, kk, hi);
-                        const int dec = S::decomposed(lane, w, md, kk, hi);
-                        CHECK(ref == dec, "pv split kv8=%d lane=%d w=%d md=%d kk=%d hi=%d", KV8, lane, w, md, kk, hi);
+                    for (int hi = 0; hi < L::kPvBases; ++hi) {
+                        const int ref = L::pv_ref(lane, 4 * md + w, kk, hi);
+                        CHECK(ref == L::pv_base(lane, w, hi) + L::pv_delta(md, kk),
+                              "h128 pv kv8=%d lane=%d w=%d md=%d kk=%d hi=%d", KV8, lane, w, md, kk, hi);
+                        CHECK(ref >= 0 && ref + 8 <= L::kTileBytes && ref % 8 == 0, "h128 pv range");
+                        // same (token, column) as the general layout's read of this block
+                        const int gref = P::reference(lane, 4 * md + w, kk, hi);
+                        const int gt = (gref / 1024) % L::kNTB * L::kTPB + (gref % 1024) / (16 * L::kCG);
+                        const int lt = (ref / 1024) % L::kNTB * L::kTPB + (ref % 1024) / (16 * L::kCG);
+                        CHECK(gt == lt && gref / 1024 == ref / 1024 && gref % 16 == ref % 16, "h128 pv element");
                     }
+                for (int r = 0; r < 16; ++r) {
+                    const int c = L::column(w, md, lane / 32, r);
+                    CHECK(c == 32 * (4 * md + w) + 8 * (r / 4) + 4 * (lane / 32) + r % 4, "h128 column");
+                    cols.insert(c);
+                }
+            }
+    CHECK(cols.size() == 512, "h128 columns cover the latent: %zu", cols.size());
+}
+
+void check_out_stage() {
+    // Round md: wave w, lane group g, value group r4 writes 16 bytes at
+    // (head, 32 w + 8 r4 + 4 g); the store pass reads 16-byte units row-major.
+    std::set<int> offs;
+    for (int h = 0; h < 128; ++h)
+        for (int c = 0; c < 128; c += 4) {
+            const int o = OutStage::offset(h, c);
+            CHECK(o % 16 == 0 && o + 16 <= OutStage::kBytes, "out stage offset");
+            CHECK(offs.insert(o).second, "out stage overlap");
+        }
+    std::set<int> banks;
+    for (int h = 0; h < 16; ++h) banks.insert((OutStage::offset(h, 36) / 16) % 16);
+    CHECK(banks.size() == 16, "out stage bank spread %zu", banks.size());
 }
 
 void check_pbuf() {
@@ -108,9 +181,10 @@ int main() {
     check_pv<32, true>();
     check_pv<16, false>();
     check_pv<16, true>();
-    check_pv_split<false>();
-    check_pv_split<true>();
+    check_h128<false>();
+    check_h128<true>();
     check_pbuf();
+    check_out_stage();
     if (failures) {
         std::printf("FAILED: %d\n", failures);
         return 1;
