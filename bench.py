@@ -71,8 +71,8 @@ def cpu_baseline(batch, target_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="v3", choices=["v3", "v2_lite", "skewed_fp8"])
     ap.add_argument("--copy-mb", type=int, default=0,
