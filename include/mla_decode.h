@@ -89,7 +89,8 @@ typedef struct {
     int64_t items_offset;   /* byte offset of mla_work_item[num_items] */
     int64_t merges_offset;  /* byte offset of mla_merge_item[num_merges] */
     int64_t plan_bytes;     /* bytes of the plan itself (header + items + merges) */
-    int64_t partial_out_offset; /* workspace offset of float[num_partials][H][512] */
+    int64_t partial_out_offset; /* workspace offset of [num_partials][H][512] partial outputs,
+                                   bf16 (fp32 when out_dtype is MLA_DTYPE_FP32) */
     int64_t partial_lse_offset; /* workspace offset of float[num_partials][H] */
     int64_t workspace_bytes;    /* workspace bytes this plan needs */
 } mla_plan_header;

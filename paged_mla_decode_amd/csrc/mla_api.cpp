@@ -132,7 +132,7 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
     a.kv_lens = kv_lens_d;
     a.out = out_d;
     a.lse = lse_d;
-    a.part_out = reinterpret_cast<float*>(const_cast<char*>(ws) + h->partial_out_offset);
+    a.part_out = const_cast<char*>(ws) + h->partial_out_offset;
     a.part_lse = reinterpret_cast<float*>(const_cast<char*>(ws) + h->partial_lse_offset);
     a.num_heads = params->num_heads;
     a.page_size = params->page_size;

@@ -377,13 +377,13 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
             const int h = u >> 5, c4 = u & 31;
             const f32x4 v = *(const LDS_AS f32x4*)(stage + OutStage::offset(h, 4 * c4));
             const int64_t o = (row0 + h) * kLatent + 128 * md + 4 * c4;
-            if (it.partial >= 0) {
-                *reinterpret_cast<f32x4*>(a.part_out + o) = v;
-            } else if constexpr (OUT32) {
-                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = v;
+            // Partials are stored in the output's precision.
+            void* base = it.partial >= 0 ? a.part_out : a.out;
+            if constexpr (OUT32) {
+                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + o) = v;
             } else {
                 const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-                *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.out) + o) = b;
+                *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(base) + o) = b;
             }
         }
         lds_barrier();

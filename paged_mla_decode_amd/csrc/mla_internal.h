@@ -47,7 +47,7 @@ struct DecodeArgs {
     const int32_t* kv_lens;  // may be null
     void* out;
     float* lse;  // may be null
-    float* part_out;
+    void* part_out;  // [partials][H][512]: bf16, or fp32 in the fp32-output mode
     float* part_lse;
     int32_t num_heads;
     int32_t page_size;
@@ -58,7 +58,7 @@ struct DecodeArgs {
 
 struct MergePartialsArgs {
     const mla_merge_item* merges;
-    const float* part_out;
+    const void* part_out;  // as DecodeArgs::part_out
     const float* part_lse;
     void* out;
     float* lse;  // may be null

@@ -325,8 +325,8 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
     const float lse = empty ? -INFINITY : (m_run + __log2f(l)) * kLn2;
     const int nh = a.num_heads;
 
-    if (it.partial >= 0) {
-        float* po = a.part_out + ((int64_t)it.partial * nh + head) * kLatent;
+    if (it.partial >= 0 && OUT32) {
+        float* po = reinterpret_cast<float*>(a.part_out) + ((int64_t)it.partial * nh + head) * kLatent;
         if constexpr (HW == 32) {
 #pragma unroll
             for (int md = 0; md < kDBlocks; ++md)
@@ -346,8 +346,11 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
         }
         if (gq == 0) a.part_lse[(int64_t)it.partial * nh + head] = lse;
     } else {
+        // bf16 partials (bf16 output) take the same path as the output itself.
+        const int64_t orow = it.partial >= 0 ? (int64_t)it.partial * nh + head : (int64_t)it.row * nh + head;
+        void* obase = it.partial >= 0 ? a.part_out : a.out;
         if constexpr (OUT32) {
-            float* o = reinterpret_cast<float*>(a.out) + ((int64_t)it.row * nh + head) * kLatent;
+            float* o = reinterpret_cast<float*>(obase) + orow * kLatent;
             if constexpr (HW == 32) {
 #pragma unroll
                 for (int md = 0; md < kDBlocks; ++md)
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
                     *reinterpret_cast<f32x4*>(o + 16 * md + 4 * gq) = O16[md] * inv;
             }
         } else {
-            __bf16* o = reinterpret_cast<__bf16*>(a.out) + ((int64_t)it.row * nh + head) * kLatent;
+            __bf16* o = reinterpret_cast<__bf16*>(obase) + orow * kLatent;
             if constexpr (HW == 32) {
 #pragma unroll
                 for (int md = 0; md < kDBlocks; ++md)
@@ -384,7 +387,12 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
                 }
             }
         }
-        if (a.lse && gq == 0) a.lse[(int64_t)it.row * nh + head] = lse;
+        if (gq == 0) {
+            if (it.partial >= 0)
+                a.part_lse[orow] = lse;
+            else if (a.lse)
+                a.lse[orow] = lse;
+        }
     }
 }
 
@@ -407,7 +415,14 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(const MergePartials
                 const int64_t slot = (int64_t)(mi.partial_begin + p) * nh + h;
                 const float wp = fast_exp2((a.part_lse[slot] - m) * kLog2e);
                 wsum += wp;
-                const f32x8 v = *reinterpret_cast<const f32x8*>(a.part_out + slot * kLatent + 8 * lane);
+                f32x8 v;
+                if constexpr (OUT32) {
+                    v = *reinterpret_cast<const f32x8*>(reinterpret_cast<const float*>(a.part_out) + slot * kLatent + 8 * lane);
+                } else {
+                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.part_out) + slot * kLatent + 8 * lane);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = (float)b[e];
+                }
                 acc += wp * v;
             }
         }

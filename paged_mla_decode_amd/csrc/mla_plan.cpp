@@ -11,7 +11,7 @@
 //   * Total work T = sum over query rows of their token counts. With G
 //     workgroups resident at once (compute units x workgroups per CU), the
 //     target chunk is ceil(T / G) tokens, never below the variant's min_chunk
-//     (a partial costs H*512*4 bytes written and read back, plus a second load
+//     (a partial costs H*512 values, bf16 or fp32, written and read back, plus a second load
 //     of the query), rounded up to the 32-token tile.
 //   * A row longer than the target is cut into equal tile-aligned chunks
 //     (at most max_splits). Short rows stay whole and write their output
@@ -69,14 +69,17 @@ const char* variant_name(const mla_decode_params* p) {
     return names[v.hw == 32 ? 1 : 0][hsi][kv8][o32];
 }
 
+// Partials are stored in the output's precision: bf16, or fp32 in the fp32 mode.
+static int64_t partial_elem_bytes(const mla_decode_params* p) { return p->out_dtype == MLA_DTYPE_FP32 ? 4 : 2; }
+
 static void layout(int32_t num_items, int32_t num_merges, int32_t num_partials, int32_t num_heads,
-                   mla_plan_header* h) {
+                   int64_t elem_bytes, mla_plan_header* h) {
     h->items_offset = align_up(sizeof(mla_plan_header), 64);
     h->merges_offset = align_up(h->items_offset + (int64_t)num_items * sizeof(mla_work_item), 64);
     h->plan_bytes = align_up(h->merges_offset + (int64_t)num_merges * sizeof(mla_merge_item), 256);
     h->partial_out_offset = h->plan_bytes;
     h->partial_lse_offset =
-        align_up(h->partial_out_offset + (int64_t)num_partials * num_heads * kLatent * 4, 256);
+        align_up(h->partial_out_offset + (int64_t)num_partials * num_heads * kLatent * elem_bytes, 256);
     h->workspace_bytes = align_up(h->partial_lse_offset + (int64_t)num_partials * num_heads * 4, 256);
 }
 
@@ -91,7 +94,7 @@ int32_t plan_bounds(const mla_decode_params* p, int32_t num_cus, int32_t batch, 
     const int64_t items = (int64_t)num_rows + G + 1;
     const int64_t partials = std::min<int64_t>(items, 2 * G + 2);
     mla_plan_header h{};
-    layout((int32_t)items, num_rows, (int32_t)partials, p->num_heads, &h);
+    layout((int32_t)items, num_rows, (int32_t)partials, p->num_heads, partial_elem_bytes(p), &h);
     if (plan_bytes) *plan_bytes = (size_t)h.plan_bytes;
     if (workspace_bytes) *workspace_bytes = (size_t)h.workspace_bytes;
     return MLA_OK;
@@ -180,7 +183,7 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
     h.num_partials = num_partials;
     h.chunk_tokens = (int32_t)chunk;
     h.num_page_entries = kv_indptr[batch];
-    layout(h.num_items, h.num_merges, num_partials, p->num_heads, &h);
+    layout(h.num_items, h.num_merges, num_partials, p->num_heads, partial_elem_bytes(p), &h);
     if ((size_t)h.plan_bytes > plan_h_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
     char* dst = static_cast<char*>(plan_h);

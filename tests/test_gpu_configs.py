@@ -1,0 +1,128 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times (default plan over all of the device's compute units): the whole batch
+runs on the GPU and sampled requests are checked against the oracle, which
+computes only those requests. The tree-verify cascade runs end to end:
+compaction, prefix decode, suffix decode with device-side lengths, LSE merge,
+against the oracle's attention over the prefix plus the visible drafts."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import batch_to_device, compare, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def sampled_requests(batch, k, seed):
+    """The longest and the shortest request plus k-2 others, seeded."""
+    lens = batch.seq_lens
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
+    others = rng.permutation(batch.batch)
+    for b in others:
+        if len(pick) >= k:
+            break
+        pick.add(int(b))
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def run_full(batch, dev, out_dtype):
+    from paged_mla_decode_amd.decoder import PagedMlaDecoder
+    qn, qr, cache, idx = batch_to_device(batch, dev)
+    dec = PagedMlaDecoder(batch.num_heads, batch.page_size, max_batch=batch.batch,
+                          max_rows=batch.num_rows, kv_dtype=batch.cache_dtype, out_dtype=out_dtype,
+                          device=dev)
+    h = dec.plan(batch.kv_indptr, batch.kv_last_page_len)
+    out, lse = dec.run(qn, qr, cache, idx, batch.sm_scale, batch.kv_scale)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), h
+
+
+@pytest.mark.parametrize("name,out_dtype,k", [
+    ("v2_lite", "bf16", 8),
+    ("v3", "bf16", 8),
+    ("v3", "fp32", 4),
+    ("skewed_fp8", "bf16", 4),
+])
+def test_config_sampled_rows(dev, name, out_dtype, k):
+    batch = getattr(workloads, name)()
+    say(f"config {name} out={out_dtype}: B={batch.batch} H={batch.num_heads} ps={batch.page_size} "
+        f"tokens={int(batch.seq_lens.sum())}")
+    out, lse, h = run_full(batch, dev, out_dtype)
+    say(f"  plan: items={h.num_items} merges={h.num_merges} chunk={h.chunk_tokens}")
+    reqs = sampled_requests(batch, k, seed=11)
+    sub = batch.subset(reqs)
+    ref_out, ref_lse = oracle.decode_batch(sub)
+    rows = np.concatenate([np.arange(batch.qo_indptr[b], batch.qo_indptr[b + 1]) for b in reqs])
+    split_rows = int(np.sum(batch.seq_lens[reqs] > h.chunk_tokens))
+    say(f"  sampled requests {reqs.tolist()} (lengths {batch.seq_lens[reqs].tolist()}, "
+        f"{split_rows} split)")
+    compare(out[rows], lse[rows], ref_out, ref_lse, out_dtype == "fp32", f"{name} sampled")
+    if name in ("v3", "skewed_fp8"):
+        assert split_rows > 0, "the sample must include a split-KV row"
+
+
+def test_tree_verify_cascade(dev):
+    from paged_mla_decode_amd.decoder import PagedMlaDecoder, merge_states, tree_suffix_compact
+    tv = workloads.tree_verify()
+    pre = tv.prefix
+    W, D = tv.width, tv.max_tree_depth
+    B = pre.batch
+    N = pre.num_rows
+    say(f"tree cascade: B={B} W={W} rows={N} prefix={int(pre.seq_lens[0])} depth<={D}")
+    qn, qr, cache, idx = batch_to_device(pre, dev)
+
+    # 1. stable compaction of the suffix tables (one launch)
+    mask_d = torch.from_numpy(tv.tree_mask).to(dev)
+    r2t_d = torch.from_numpy(tv.req_to_token).to(dev)
+    pl_d = torch.from_numpy(tv.prefix_lens).to(dev)
+    table, seqlens = tree_suffix_compact(mask_d, r2t_d, pl_d, W)
+    seq_h = seqlens.cpu().numpy()
+    assert np.array_equal(seq_h, tv.tree_mask.sum(axis=1)), "seqlens = visible drafts per row"
+    assert seq_h.max() <= D, "depth bound: truncation to max_tree_depth drops nothing"
+
+    # 2. prefix: every draft row attends to its request's prefix
+    dp = PagedMlaDecoder(pre.num_heads, 1, max_batch=B, max_rows=N, device=dev)
+    dp.plan(pre.kv_indptr, pre.kv_last_page_len, pre.qo_indptr)
+    out_p, lse_p = dp.run(qn, qr, cache, idx, pre.sm_scale)
+
+    # 3. suffix: row r attends to the first D entries of its compacted table,
+    #    clipped on the device to its visible count
+    ds = PagedMlaDecoder(pre.num_heads, 1, max_batch=N, max_rows=N, device=dev)
+    ds.plan(np.arange(N + 1, dtype=np.int32) * D, np.ones(N, dtype=np.int32))
+    suffix_idx = table[:, :D].contiguous().view(-1)
+    out_s, lse_s = ds.run(qn, qr, cache, suffix_idx, pre.sm_scale, kv_lens=seqlens)
+
+    # 4. LSE merge of the two states
+    out, lse = merge_states(out_p, lse_p, out_s, lse_s)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+
+    # Oracle: attention of each sampled row over prefix + its visible drafts.
+    rng = np.random.Generator(np.random.PCG64(12))
+    rows = np.unique(np.concatenate([
+        np.arange(0, N, W),                                     # every root row
+        np.argsort(-tv.tree_mask.sum(axis=1), kind="stable")[:6],  # deepest rows
+        rng.choice(N, size=10, replace=False)]))
+    kv_indptr = [0]
+    kv_indices = []
+    for r in rows:
+        req, plen = int(r) // W, int(tv.prefix_lens[int(r) // W])
+        vis = np.nonzero(tv.tree_mask[r])[0]
+        slots = np.concatenate([tv.req_to_token[req, :plen], tv.req_to_token[req, plen + vis]])
+        kv_indices.append(slots)
+        kv_indptr.append(kv_indptr[-1] + len(slots))
+    ref_out, ref_lse = oracle.mla_decode(
+        pre.q_nope[rows], pre.q_rope[rows], pre.cache, np.asarray(kv_indptr, np.int32),
+        np.concatenate(kv_indices).astype(np.int32), 1, pre.sm_scale,
+        kv_last_page_len=np.ones(len(rows), np.int32))
+    say(f"  checking {len(rows)} rows")
+    compare(out[rows], lse[rows], ref_out, ref_lse, False, "tree cascade")
