@@ -40,6 +40,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_sha256():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "paged_mla_decode_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none for this workload or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"mla_decode_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+                k, v = line.split(":", 1)
+                fields[k] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    return int(fields["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in fields else None
+
+
 def cpu_baseline(batch, target_s=12.0):
     """Oracle GB/s on a prefix of the batch sized to about target_s seconds."""
     import oracle
@@ -197,7 +225,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
             "algorithmic_bytes_per_launch": latent_bytes,
             "launch_avg_us": round(launch_avg_ms * 1e3, 2),
             "mfma_tflops": round(flops / (launch_avg_ms * 1e-3) / 1e12, 1),
