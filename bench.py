@@ -186,8 +186,8 @@ def main():
     gbs = latent_bytes / (ms_per_step * 1e-3) / 1e9
     launch_avg_ms = float(launch_ms.mean())
     achieved = latent_bytes / (launch_avg_ms * 1e-3) / 1e9
-    log(f"plan: items={h.num_items} merges={h.num_merges} partials={h.num_partials} "
-        f"chunk={h.chunk_tokens} plan_us={plan_us:.0f}")
+    log(f"plan: workers={h.num_workers} items={h.num_items} merges={h.num_merges} "
+        f"partials={h.num_partials} capacity={h.chunk_tokens} plan_us={plan_us:.0f}")
     log(f"step {ms_per_step * 1e3:.1f} us, launch avg {launch_avg_ms * 1e3:.1f} us "
         f"(p10 {np.percentile(launch_ms, 10) * 1e3:.1f}, p90 {np.percentile(launch_ms, 90) * 1e3:.1f}), "
         f"{gbs:.0f} GB/s, {achieved / HBM_PEAK_GBS * 100:.1f}% HBM, "
@@ -216,8 +216,8 @@ def main():
         "tokens_per_s": round(batch.num_rows / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "plan_us": round(plan_us, 1),
-        "plan": {"items": h.num_items, "merges": h.num_merges, "partials": h.num_partials,
-                 "chunk_tokens": h.chunk_tokens},
+        "plan": {"workers": h.num_workers, "items": h.num_items, "merges": h.num_merges,
+                 "partials": h.num_partials, "capacity_tokens": h.chunk_tokens},
         "roofline": {
             "kernel": "mla_decode launch (decode kernel + split-KV merge kernel)",
             "bound": "hbm",

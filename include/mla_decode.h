@@ -73,7 +73,7 @@ const char* mla_status_string(int32_t status);
  * of the device workspace. It is plain data: tests may read it.
  */
 #define MLA_PLAN_MAGIC 0x504C4D41u /* "AMLP" */
-#define MLA_PLAN_VERSION 1
+#define MLA_PLAN_VERSION 2
 
 typedef struct {
     uint32_t magic;
@@ -81,14 +81,19 @@ typedef struct {
     int32_t num_heads, page_size, kv_dtype, out_dtype;
     int32_t batch;          /* requests */
     int32_t num_rows;       /* query rows (qo_indptr[batch]) */
-    int32_t num_items;      /* decode work items = workgroups of the decode launch */
+    int32_t num_items;      /* decode work items (a query row and a token range each) */
     int32_t num_merges;     /* query rows whose KV was split into several chunks */
     int32_t num_partials;   /* partial (out, lse) slots written by split chunks */
-    int32_t chunk_tokens;   /* target chunk length the plan used */
+    int32_t chunk_tokens;   /* per-worker capacity the plan used, in tokens (including
+                               a fixed per-item cost counted as tokens) */
+    int32_t num_workers;    /* workgroups of the decode launch; worker w processes
+                               items [workers[w], workers[w+1]) in order */
+    int32_t reserved0;
     int64_t num_page_entries; /* kv_indptr[batch]: entries of kv_indices the batch uses */
     int64_t items_offset;   /* byte offset of mla_work_item[num_items] */
     int64_t merges_offset;  /* byte offset of mla_merge_item[num_merges] */
-    int64_t plan_bytes;     /* bytes of the plan itself (header + items + merges) */
+    int64_t workers_offset; /* byte offset of int32_t workers[num_workers + 1] */
+    int64_t plan_bytes;     /* bytes of the plan itself (header + items + merges + workers) */
     int64_t partial_out_offset; /* workspace offset of [num_partials][H][512] partial outputs,
                                    bf16 (fp32 when out_dtype is MLA_DTYPE_FP32) */
     int64_t partial_lse_offset; /* workspace offset of float[num_partials][H] */

@@ -41,7 +41,7 @@ MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP32 = 1
 MLA_DTYPE_FP8_E4M3FN = 2
 MLA_PLAN_MAGIC = 0x504C4D41
-MLA_PLAN_VERSION = 1
+MLA_PLAN_VERSION = 2
 
 
 class mla_decode_params(ctypes.Structure):
@@ -58,8 +58,10 @@ class mla_plan_header(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("num_rows", ctypes.c_int32),
                 ("num_items", ctypes.c_int32), ("num_merges", ctypes.c_int32),
                 ("num_partials", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
+                ("num_workers", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("num_page_entries", ctypes.c_int64), ("items_offset", ctypes.c_int64),
-                ("merges_offset", ctypes.c_int64), ("plan_bytes", ctypes.c_int64),
+                ("merges_offset", ctypes.c_int64), ("workers_offset", ctypes.c_int64),
+                ("plan_bytes", ctypes.c_int64),
                 ("partial_out_offset", ctypes.c_int64), ("partial_lse_offset", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64)]
 
@@ -202,11 +204,14 @@ def mla_tree_suffix_compact(tree_mask_d, mask_stride, req_to_token_d, req_stride
 
 
 def read_plan(plan_h):
-    """(header, [work items], [merge items]) copied out of a host plan buffer."""
+    """(header, [work items], [merge items], [worker item offsets]) copied out of a
+    host plan buffer."""
     base = _ptr(plan_h)
     h = mla_plan_header.from_buffer_copy(ctypes.string_at(base, ctypes.sizeof(mla_plan_header)))
     items = (mla_work_item * h.num_items).from_buffer_copy(
         ctypes.string_at(base + h.items_offset, h.num_items * ctypes.sizeof(mla_work_item)))
     merges = (mla_merge_item * h.num_merges).from_buffer_copy(
         ctypes.string_at(base + h.merges_offset, h.num_merges * ctypes.sizeof(mla_merge_item)))
-    return h, list(items), list(merges)
+    workers = (ctypes.c_int32 * (h.num_workers + 1)).from_buffer_copy(
+        ctypes.string_at(base + h.workers_offset, (h.num_workers + 1) * 4))
+    return h, list(items), list(merges), list(workers)

@@ -120,6 +120,7 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
     const char* ws = static_cast<const char*>(workspace_d);
     DecodeArgs a{};
     a.items = reinterpret_cast<const mla_work_item*>(ws + h->items_offset);
+    a.workers = reinterpret_cast<const int32_t*>(ws + h->workers_offset);
     a.q_nope = static_cast<const uint16_t*>(q_nope_d);
     a.qn_sn = q_nope_stride_n;
     a.qn_sh = q_nope_stride_h;
@@ -141,7 +142,7 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
         if (params->page_size == (1 << b)) a.page_shift = b;
     a.scale_log2 = (float)((double)sm_scale * (double)kv_scale * 1.4426950408889634);
     a.out_scale = kv_scale;
-    int err = launch_decode(v, params->kv_dtype, params->out_dtype, a, h->num_items, stream);
+    int err = launch_decode(v, params->kv_dtype, params->out_dtype, a, h->num_workers, stream);
     if (err != 0) return MLA_ERR_HIP;
     if (h->num_merges > 0) {
         MergePartialsArgs m{};

@@ -71,330 +71,340 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
     __shared__ float l_sh[128];
     __shared__ int rerun_flag[HS];
 
-    const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const mla_work_item it = a.items[blockIdx.x];
-    const int ps = a.page_size;
-    const int kv_begin = it.kv_begin;
-    int kv_end = it.kv_end;
-    if (a.kv_lens) kv_end = min(kv_end, a.kv_lens[it.request]);
-    const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + kTile - 1) / kTile : 0;
-    const int hq = lane & 31, gq = lane >> 5;
-    const int head = it.head_begin + 32 * w + hq;  // this lane's head in the score phase
+    // Persistent worker: the plan's items [workers[w], workers[w+1]) in order.
+    const int item_end = a.workers[blockIdx.x + 1];
+    for (int item = a.workers[blockIdx.x]; item < item_end; ++item) {
+        // The thread index passes through an empty asm so that every per-lane
+        // address is computed anew for each item: hoisted out of the item loop
+        // they would be held across it, spilled, and reloaded behind waits that
+        // also drain the output stores in flight.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const mla_work_item it = a.items[item];
+        const int ps = a.page_size;
+        const int kv_begin = it.kv_begin;
+        int kv_end = it.kv_end;
+        if (a.kv_lens) kv_end = min(kv_end, a.kv_lens[it.request]);
+        const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + kTile - 1) / kTile : 0;
+        const int hq = lane & 31, gq = lane >> 5;
+        const int head = it.head_begin + 32 * w + hq;  // this lane's head in the score phase
 
-    // ---- tile loads ----
-    // Wave w loads token block tb of every tile (kLoads 1 KiB blocks). Its
-    // page-index slot holds the page of each of those tokens (tail tokens are
-    // clamped to the last valid one, so no load leaves the request's pages).
-    const int tb = w % L::kNTB;
-    const int32_t* page_table = a.kv_indices + it.page_base;
-    const int dma_lane_off = L::block_chunk(0, tb, lane) * 16;
-    auto page_of = [&](int tok) { return a.page_shift >= 0 ? tok >> a.page_shift : tok / ps; };
-    auto issue_idx = [&](int tile, int slot) {
-        const int tok = min(kv_begin + tile * kTile + tb * L::kTPB + min(lane, L::kTPB - 1), kv_end - 1);
-        dma4(page_table + page_of(tok), (LDS_AS int*)&idx_ring[slot][w][0]);
-    };
-    auto issue_tile = [&](int tile, int slot) {
-        const int tau = min(kv_begin + tile * kTile + L::block_token(tb, lane), kv_end - 1);
-        const int page = idx_ring[slot][w][lane / L::kCG];
-        const int row = a.page_shift >= 0 ? (tau & (ps - 1)) : tau % ps;
-        const uint8_t* rowp = a.cache + ((int64_t)page * ps + row) * L::kRowBytes + dma_lane_off;
-        LDS_AS char* buf = (LDS_AS char*)smem + slot * L::kTileBytes;
+        // ---- tile loads ----
+        // Wave w loads token block tb of every tile (kLoads 1 KiB blocks). Its
+        // page-index slot holds the page of each of those tokens (tail tokens are
+        // clamped to the last valid one, so no load leaves the request's pages).
+        const int tb = w % L::kNTB;
+        const int32_t* page_table = a.kv_indices + it.page_base;
+        const int dma_lane_off = L::block_chunk(0, tb, lane) * 16;
+        auto page_of = [&](int tok) { return a.page_shift >= 0 ? tok >> a.page_shift : tok / ps; };
+        auto issue_idx = [&](int tile, int slot) {
+            const int tok = min(kv_begin + tile * kTile + tb * L::kTPB + min(lane, L::kTPB - 1), kv_end - 1);
+            dma4(page_table + page_of(tok), (LDS_AS int*)&idx_ring[slot][w][0]);
+        };
+        auto issue_tile = [&](int tile, int slot) {
+            const int tau = min(kv_begin + tile * kTile + L::block_token(tb, lane), kv_end - 1);
+            const int page = idx_ring[slot][w][lane / L::kCG];
+            const int row = a.page_shift >= 0 ? (tau & (ps - 1)) : tau % ps;
+            const uint8_t* rowp = a.cache + ((int64_t)page * ps + row) * L::kRowBytes + dma_lane_off;
+            LDS_AS char* buf = (LDS_AS char*)smem + slot * L::kTileBytes;
 #pragma unroll
-        for (int i = 0; i < kLoadsMax; ++i) {
-            const int b = w + HS * i;
-            if (L::kNB % HS != 0 && b >= L::kNB) break;
-            dma16(rowp + (b / L::kNTB) * L::kCG * 16, buf + b * 1024);
+            for (int i = 0; i < kLoadsMax; ++i) {
+                const int b = w + HS * i;
+                if (L::kNB % HS != 0 && b >= L::kNB) break;
+                dma16(rowp + (b / L::kNTB) * L::kCG * 16, buf + b * 1024);
+            }
+        };
+        auto wrap = [](int x) { return x >= kStages ? x - kStages : x; };
+        // Tile t and its page indices live in slot t % kStages.
+        auto prologue_idx = [&] {
+#pragma unroll
+            for (int t = 0; t < kAhead; ++t)
+                if (t < ntiles) issue_idx(t, t);
+        };
+        // Page indices of the first tiles ride along with the query loads.
+        prologue_idx();
+
+        // ---- absorbed query -> registers ----
+        bf16x8 q[kSteps];
+        {
+            const uint16_t* qn = a.q_nope + (int64_t)it.row * a.qn_sn + (int64_t)head * a.qn_sh;
+            const uint16_t* qr = a.q_rope + (int64_t)it.row * a.qr_sn + (int64_t)head * a.qr_sh;
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                const int f = L::q_feature(u, gq);
+                q[u] = u < 32 ? load_bf16x8(qn + f) : load_bf16x8(qr + (f - kLatent));
+            }
+            // vmcnt(0), as a builtin the compiler accounts for: the query has landed
+            // (so the compiler places no waits of its own in the loop, where they
+            // would also drain the tiles in flight), and so have the page indices.
+            __builtin_amdgcn_s_waitcnt(0x0F70);
         }
-    };
-    auto wrap = [](int x) { return x >= kStages ? x - kStages : x; };
-    // Tile t and its page indices live in slot t % kStages.
-    auto prologue_idx = [&] {
-#pragma unroll
-        for (int t = 0; t < kAhead; ++t)
-            if (t < ntiles) issue_idx(t, t);
-    };
-    // Page indices of the first tiles ride along with the query loads.
-    prologue_idx();
 
-    // ---- absorbed query -> registers ----
-    bf16x8 q[kSteps];
-    {
-        const uint16_t* qn = a.q_nope + (int64_t)it.row * a.qn_sn + (int64_t)head * a.qn_sh;
-        const uint16_t* qr = a.q_rope + (int64_t)it.row * a.qr_sn + (int64_t)head * a.qr_sh;
+        int sbase[L::kScoreBases], pbase[L::kPvBases];
 #pragma unroll
-        for (int u = 0; u < kSteps; ++u) {
-            const int f = L::q_feature(u, gq);
-            q[u] = u < 32 ? load_bf16x8(qn + f) : load_bf16x8(qr + (f - kLatent));
-        }
-        // vmcnt(0), as a builtin the compiler accounts for: the query has landed
-        // (so the compiler places no waits of its own in the loop, where they
-        // would also drain the tiles in flight), and so have the page indices.
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
-
-    int sbase[L::kScoreBases], pbase[L::kPvBases];
+        for (int i = 0; i < L::kScoreBases; ++i) sbase[i] = L::score_ref(lane, i);
 #pragma unroll
-    for (int i = 0; i < L::kScoreBases; ++i) sbase[i] = L::score_ref(lane, i);
+        for (int i = 0; i < L::kPvBases; ++i) pbase[i] = L::pv_base(lane, w, i);
+        const int p_wr = PBuf::offset(32 * w + hq, 0, gq);  // this lane's probabilities, kk = 0
+        const int p_rd = PBuf::offset(hq, 0, gq);           // head block hb adds hb * 32 rows
+
+        f32x16 O[kDW][4];
+        float m_ref = -INFINITY, m_true = -INFINITY;
+        float l_part = 0.f;
+
+        for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int i = 0; i < L::kPvBases; ++i) pbase[i] = L::pv_base(lane, w, i);
-    const int p_wr = PBuf::offset(32 * w + hq, 0, gq);  // this lane's probabilities, kk = 0
-    const int p_rd = PBuf::offset(hq, 0, gq);           // head block hb adds hb * 32 rows
-
-    f32x16 O[kDW][4];
-    float m_ref = -INFINITY, m_true = -INFINITY;
-    float l_part = 0.f;
-
-    for (int pass = 0; pass < 2; ++pass) {
+            for (int i = 0; i < kDW; ++i)
 #pragma unroll
-        for (int i = 0; i < kDW; ++i)
+                for (int j = 0; j < 4; ++j) O[i][j] = f32x16{};
+            l_part = 0.f;
+
+            if (ntiles > 0) {
+                if (pass > 0) {
+                    prologue_idx();
+                    wait_vmcnt_barrier<0>();
+                }
+                // The product at j = 0 reads slot kStages-1 (first loaded at j = 1)
+                // and the probability buffer: both start as zeros.
+                {
+                    using V4 = __attribute__((__vector_size__(4 * sizeof(int)))) int;
+                    LDS_AS V4* z = (LDS_AS V4*)(smem + (kStages - 1) * L::kTileBytes);
+                    for (int k = tid; k < L::kTileBytes / 16; k += 256) z[k] = V4{0, 0, 0, 0};
+                    LDS_AS V4* zp = (LDS_AS V4*)pbuf;
+                    for (int k = tid; k < (OUT32 ? 2 : 1) * PBuf::kBytes / 16; k += 256) zp[k] = V4{0, 0, 0, 0};
+                }
+                // Fill: the data of tiles 0 .. kAhead-1, each preceded by the page
+                // indices of the tile kAhead later (as iteration t - kAhead would).
 #pragma unroll
-            for (int j = 0; j < 4; ++j) O[i][j] = f32x16{};
-        l_part = 0.f;
-
-        if (ntiles > 0) {
-            if (pass > 0) {
-                prologue_idx();
-                wait_vmcnt_barrier<0>();
-            }
-            // The product at j = 0 reads slot kStages-1 (first loaded at j = 1)
-            // and the probability buffer: both start as zeros.
-            {
-                using V4 = __attribute__((__vector_size__(4 * sizeof(int)))) int;
-                LDS_AS V4* z = (LDS_AS V4*)(smem + (kStages - 1) * L::kTileBytes);
-                for (int k = threadIdx.x; k < L::kTileBytes / 16; k += 256) z[k] = V4{0, 0, 0, 0};
-                LDS_AS V4* zp = (LDS_AS V4*)pbuf;
-                for (int k = threadIdx.x; k < (OUT32 ? 2 : 1) * PBuf::kBytes / 16; k += 256) zp[k] = V4{0, 0, 0, 0};
-            }
-            // Fill: the data of tiles 0 .. kAhead-1, each preceded by the page
-            // indices of the tile kAhead later (as iteration t - kAhead would).
-#pragma unroll
-            for (int t = 0; t < kAhead; ++t) {
-                if (t + kAhead < ntiles) issue_idx(t + kAhead, wrap(t + kAhead));
-                if (t < ntiles) issue_tile(t, t);
-            }
-
-            // Iterations j = 0 .. ntiles run one body: the score of tile j (slot
-            // cur) and the P . latent product of tile j-1 (slot prv). At j = 0
-            // the product reads a zeroed slot and a zeroed probability buffer and
-            // adds exact zeros; at j = ntiles every score is masked (no valid
-            // token) and the probabilities it writes are never read.
-            auto iteration = [&](int j, int cur) {
-                constexpr bool kScore = true, kPv = true;
-                const int prv = cur == 0 ? kStages - 1 : cur - 1;
-                // Tile j has landed; every wave is past iteration j-1, so P(j-1)
-                // is visible and the slot of tile j-2 is free.
-                if (j < ntiles)
-                    wait_tiles_barrier<kStages - 3, kLoadsMin>(min(kStages - 3, ntiles - 1 - j));
-                else
-                    lds_barrier();
-                if (j + kIdxAhead < ntiles) issue_idx(j + kIdxAhead, wrap(cur + kIdxAhead % kStages));
-                if (j + kAhead < ntiles) issue_tile(j + kAhead, wrap(cur + kAhead));
-
-                // ---- score of tile j: one accumulator chain ----
-                f32x16 S = {};
-                if (kScore) {
-                    const LDS_AS char* T = (const LDS_AS char*)smem + cur * L::kTileBytes;
-                    // fp8 codes are widened to bf16 at the MFMA, not at the read, so
-                    // that only the raw codes of the reads in flight occupy registers.
-                    auto load = [&](int s) {
-                        const int off = sbase[L::score_base_index(s)] + L::score_delta(s);
-                        if constexpr (KV8)
-                            return *(const LDS_AS u32x4*)(T + off);
-                        else
-                            return *(const LDS_AS bf16x8*)(T + off);
-                    };
-                    pipelined<L::kScoreReads, kPipe, 1, KV8 ? 2 : 1>(load, [&](int s, auto raw) {
-                        if constexpr (KV8) {
-                            S = mfma32(fp8x8_to_bf16(raw[0], raw[1]), q[2 * s], S);
-                            S = mfma32(fp8x8_to_bf16(raw[2], raw[3]), q[2 * s + 1], S);
-                        } else {
-                            S = mfma32(raw, q[s], S);
-                        }
-                    });
+                for (int t = 0; t < kAhead; ++t) {
+                    if (t + kAhead < ntiles) issue_idx(t + kAhead, wrap(t + kAhead));
+                    if (t < ntiles) issue_tile(t, t);
                 }
 
-                // ---- P . latent of tile j-1, with the softmax of tile j in its shadow ----
-                bf16x8 P[2], Plo[2];
-                auto softmax = [&] {
-                    const int nvalid = min(kTile, kv_end - (kv_begin + j * kTile));
-                    float sv[16];
-                    float tmax = -INFINITY;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int tok = 16 * (r >> 3) + 8 * gq + (r & 7);
-                        sv[r] = tok < nvalid ? S[r] * a.scale_log2 : -INFINITY;
-                        tmax = fmaxf(tmax, sv[r]);
-                    }
-                    tmax = max_xor32(tmax);
-                    if (j == 0 && pass == 0) m_ref = tmax;
-                    m_true = fmaxf(m_true, tmax);
-                    float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float pv = fast_exp2(sv[8 * kk + e] - m_ref);
-                            if (e & 1)
-                                ls1 += pv;
-                            else
-                                ls0 += pv;
-                            P[kk][e] = (__bf16)pv;
-                            if (OUT32) Plo[kk][e] = (__bf16)(pv - (float)P[kk][e]);
-                        }
-                    l_part += ls0 + ls1;
-                };
-                if (kPv) {
-                    const LDS_AS char* T = (const LDS_AS char*)smem + prv * L::kTileBytes;
-                    // step = 4 kk + md: one A operand (transposed read), four MFMAs (head blocks)
-                    auto load_pv = [&](int step) {
-                        const int kk = step >> 2, md = step & 3;
-                        if constexpr (KV8) {
-                            return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                                (LDS_AS i32x2*)(T + pbase[0] + L::pv_delta(md, kk)));
-                        } else {
-                            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (LDS_AS i16x4*)(T + pbase[0] + L::pv_delta(md, kk)));
-                            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (LDS_AS i16x4*)(T + pbase[1] + L::pv_delta(md, kk)));
-                            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                        }
-                    };
-                    // P(j-1) of token half kk for the four head blocks (B operands).
-                    bf16x8 Bp[4], Bl[4];
-                    auto load_p = [&](int kk) {
-#pragma unroll
-                        for (int hb = 0; hb < 4; ++hb) {
-                            const int off = p_rd + hb * 32 * PBuf::kRow + 32 * kk;
-                            Bp[hb] = *(const LDS_AS bf16x8*)((const LDS_AS char*)pbuf + off);
-                            if (OUT32) Bl[hb] = *(const LDS_AS bf16x8*)((const LDS_AS char*)pbuf + PBuf::kBytes + off);
-                        }
-                    };
-                    using Op = decltype(load_pv(0));
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        load_p(kk);
-                        Op buf[2] = {load_pv(4 * kk), load_pv(4 * kk + 1)};
-                        if (kScore && kk == 0) softmax();
-#pragma unroll
-                        for (int md = 0; md < 4; ++md) {
-                            const Op raw = buf[md & 1];
-                            bf16x8 A;
+                // Iterations j = 0 .. ntiles run one body: the score of tile j (slot
+                // cur) and the P . latent product of tile j-1 (slot prv). At j = 0
+                // the product reads a zeroed slot and a zeroed probability buffer and
+                // adds exact zeros; at j = ntiles every score is masked (no valid
+                // token) and the probabilities it writes are never read.
+                auto iteration = [&](int j, int cur) {
+                    constexpr bool kScore = true, kPv = true;
+                    const int prv = cur == 0 ? kStages - 1 : cur - 1;
+                    // Tile j has landed; every wave is past iteration j-1, so P(j-1)
+                    // is visible and the slot of tile j-2 is free.
+                    if (j < ntiles)
+                        wait_tiles_barrier<kStages - 3, kLoadsMin>(min(kStages - 3, ntiles - 1 - j));
+                    else
+                        lds_barrier();
+                    if (j + kIdxAhead < ntiles) issue_idx(j + kIdxAhead, wrap(cur + kIdxAhead % kStages));
+                    if (j + kAhead < ntiles) issue_tile(j + kAhead, wrap(cur + kAhead));
+
+                    // ---- score of tile j: one accumulator chain ----
+                    f32x16 S = {};
+                    if (kScore) {
+                        const LDS_AS char* T = (const LDS_AS char*)smem + cur * L::kTileBytes;
+                        // fp8 codes are widened to bf16 at the MFMA, not at the read, so
+                        // that only the raw codes of the reads in flight occupy registers.
+                        auto load = [&](int s) {
+                            const int off = sbase[L::score_base_index(s)] + L::score_delta(s);
                             if constexpr (KV8)
-                                A = fp8x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]);
+                                return *(const LDS_AS u32x4*)(T + off);
                             else
-                                A = raw;
-                            if (md + 2 < 4) buf[md & 1] = load_pv(4 * kk + md + 2);
+                                return *(const LDS_AS bf16x8*)(T + off);
+                        };
+                        pipelined<L::kScoreReads, kPipe, 1, KV8 ? 2 : 1>(load, [&](int s, auto raw) {
+                            if constexpr (KV8) {
+                                S = mfma32(fp8x8_to_bf16(raw[0], raw[1]), q[2 * s], S);
+                                S = mfma32(fp8x8_to_bf16(raw[2], raw[3]), q[2 * s + 1], S);
+                            } else {
+                                S = mfma32(raw, q[s], S);
+                            }
+                        });
+                    }
+
+                    // ---- P . latent of tile j-1, with the softmax of tile j in its shadow ----
+                    bf16x8 P[2], Plo[2];
+                    auto softmax = [&] {
+                        const int nvalid = min(kTile, kv_end - (kv_begin + j * kTile));
+                        float sv[16];
+                        float tmax = -INFINITY;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int tok = 16 * (r >> 3) + 8 * gq + (r & 7);
+                            sv[r] = tok < nvalid ? S[r] * a.scale_log2 : -INFINITY;
+                            tmax = fmaxf(tmax, sv[r]);
+                        }
+                        tmax = max_xor32(tmax);
+                        if (j == 0 && pass == 0) m_ref = tmax;
+                        m_true = fmaxf(m_true, tmax);
+                        float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const float pv = fast_exp2(sv[8 * kk + e] - m_ref);
+                                if (e & 1)
+                                    ls1 += pv;
+                                else
+                                    ls0 += pv;
+                                P[kk][e] = (__bf16)pv;
+                                if (OUT32) Plo[kk][e] = (__bf16)(pv - (float)P[kk][e]);
+                            }
+                        l_part += ls0 + ls1;
+                    };
+                    if (kPv) {
+                        const LDS_AS char* T = (const LDS_AS char*)smem + prv * L::kTileBytes;
+                        // step = 4 kk + md: one A operand (transposed read), four MFMAs (head blocks)
+                        auto load_pv = [&](int step) {
+                            const int kk = step >> 2, md = step & 3;
+                            if constexpr (KV8) {
+                                return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                    (LDS_AS i32x2*)(T + pbase[0] + L::pv_delta(md, kk)));
+                            } else {
+                                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                    (LDS_AS i16x4*)(T + pbase[0] + L::pv_delta(md, kk)));
+                                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                    (LDS_AS i16x4*)(T + pbase[1] + L::pv_delta(md, kk)));
+                                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                            }
+                        };
+                        // P(j-1) of token half kk for the four head blocks (B operands).
+                        bf16x8 Bp[4], Bl[4];
+                        auto load_p = [&](int kk) {
 #pragma unroll
                             for (int hb = 0; hb < 4; ++hb) {
-                                O[md][hb] = mfma32(A, Bp[hb], O[md][hb]);
-                                if (OUT32) O[md][hb] = mfma32(A, Bl[hb], O[md][hb]);
+                                const int off = p_rd + hb * 32 * PBuf::kRow + 32 * kk;
+                                Bp[hb] = *(const LDS_AS bf16x8*)((const LDS_AS char*)pbuf + off);
+                                if (OUT32) Bl[hb] = *(const LDS_AS bf16x8*)((const LDS_AS char*)pbuf + PBuf::kBytes + off);
+                            }
+                        };
+                        using Op = decltype(load_pv(0));
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) {
+                            load_p(kk);
+                            Op buf[2] = {load_pv(4 * kk), load_pv(4 * kk + 1)};
+                            if (kScore && kk == 0) softmax();
+#pragma unroll
+                            for (int md = 0; md < 4; ++md) {
+                                const Op raw = buf[md & 1];
+                                bf16x8 A;
+                                if constexpr (KV8)
+                                    A = fp8x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]);
+                                else
+                                    A = raw;
+                                if (md + 2 < 4) buf[md & 1] = load_pv(4 * kk + md + 2);
+#pragma unroll
+                                for (int hb = 0; hb < 4; ++hb) {
+                                    O[md][hb] = mfma32(A, Bp[hb], O[md][hb]);
+                                    if (OUT32) O[md][hb] = mfma32(A, Bl[hb], O[md][hb]);
+                                }
+                            }
+                            // Interleave: the softmax VALU work between the MFMAs, the
+                            // transposed reads two steps ahead.
+                            constexpr int kPReads = OUT32 ? 8 : 4, kARead = KV8 ? 1 : 2;
+                            __builtin_amdgcn_sched_group_barrier(0x100, kPReads + 2 * kARead, 0);
+#pragma unroll
+                            for (int md = 0; md < 4; ++md) {
+#pragma unroll
+                                for (int m = 0; m < (OUT32 ? 8 : 4); ++m) {
+                                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                                }
+                                if (md + 2 < 4) __builtin_amdgcn_sched_group_barrier(0x100, kARead, 0);
                             }
                         }
-                        // Interleave: the softmax VALU work between the MFMAs, the
-                        // transposed reads two steps ahead.
-                        constexpr int kPReads = OUT32 ? 8 : 4, kARead = KV8 ? 1 : 2;
-                        __builtin_amdgcn_sched_group_barrier(0x100, kPReads + 2 * kARead, 0);
+                    } else if (kScore) {
+                        softmax();
+                    }
+                    // Every wave is done reading P(j-1): the buffer takes P(j).
+                    if (kScore && kPv) lds_barrier();
+                    if (kScore) {
 #pragma unroll
-                        for (int md = 0; md < 4; ++md) {
-#pragma unroll
-                            for (int m = 0; m < (OUT32 ? 8 : 4); ++m) {
-                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                            }
-                            if (md + 2 < 4) __builtin_amdgcn_sched_group_barrier(0x100, kARead, 0);
+                        for (int kk = 0; kk < 2; ++kk) {
+                            *(LDS_AS bf16x8*)((LDS_AS char*)pbuf + p_wr + 32 * kk) = P[kk];
+                            if (OUT32) *(LDS_AS bf16x8*)((LDS_AS char*)pbuf + PBuf::kBytes + p_wr + 32 * kk) = Plo[kk];
                         }
                     }
-                } else if (kScore) {
-                    softmax();
+                };
+                int cur = 0;
+                for (int j = 0; j <= ntiles; ++j) {
+                    iteration(j, cur);
+                    cur = wrap(cur + 1);
                 }
-                // Every wave is done reading P(j-1): the buffer takes P(j).
-                if (kScore && kPv) lds_barrier();
-                if (kScore) {
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        *(LDS_AS bf16x8*)((LDS_AS char*)pbuf + p_wr + 32 * kk) = P[kk];
-                        if (OUT32) *(LDS_AS bf16x8*)((LDS_AS char*)pbuf + PBuf::kBytes + p_wr + 32 * kk) = Plo[kk];
-                    }
-                }
-            };
-            int cur = 0;
-            for (int j = 0; j <= ntiles; ++j) {
-                iteration(j, cur);
-                cur = wrap(cur + 1);
             }
-        }
-        // Did any head outgrow its reference? All waves must agree (the tiles are
-        // loaded cooperatively), so the flag goes through LDS.
-        const bool over = __builtin_amdgcn_ballot_w64(m_true > m_ref + kOverflowSlack) != 0;
-        if (lane == 0) rerun_flag[w] = over ? 1 : 0;
-        lds_barrier();
-        int any = 0;
+            // Did any head outgrow its reference? All waves must agree (the tiles are
+            // loaded cooperatively), so the flag goes through LDS.
+            const bool over = __builtin_amdgcn_ballot_w64(m_true > m_ref + kOverflowSlack) != 0;
+            if (lane == 0) rerun_flag[w] = over ? 1 : 0;
+            lds_barrier();
+            int any = 0;
 #pragma unroll
-        for (int k = 0; k < HS; ++k) any |= rerun_flag[k];
-        lds_barrier();
-        if (!any) break;
-        m_ref = m_true;  // second pass: every probability is at most 1
-    }
+            for (int k = 0; k < HS; ++k) any |= rerun_flag[k];
+            lds_barrier();
+            if (!any) break;
+            m_ref = m_true;  // second pass: every probability is at most 1
+        }
 
-    // ---- finalize ----
-    const float l = sum_xor32(l_part);
-    const int nh = a.num_heads;
-    const float lse = l > 0.f ? (m_ref + __log2f(l)) * kLn2 : -INFINITY;
-    if (gq == 0) {
-        l_sh[32 * w + hq] = l;
-        if (it.partial >= 0)
-            a.part_lse[(int64_t)it.partial * nh + head] = lse;
-        else if (a.lse)
-            a.lse[(int64_t)it.row * nh + head] = lse;
-    }
-    lds_barrier();
-    float inv[4];
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-        const float lh = l_sh[32 * hb + hq];
-        inv[hb] = lh > 0.f ? a.out_scale / lh : 0.f;
-    }
-    // Output rows of this item: [partial or row][head_begin + h][512].
-    const int64_t row0 = (it.partial >= 0 ? (int64_t)it.partial * nh : (int64_t)it.row * nh) + it.head_begin;
-    LDS_AS char* stage = (LDS_AS char*)smem;  // every wave is past its last tile read
-#pragma unroll
-    for (int md = 0; md < kDW; ++md) {
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x4 v = {O[md][hb][4 * r4] * inv[hb], O[md][hb][4 * r4 + 1] * inv[hb],
-                                 O[md][hb][4 * r4 + 2] * inv[hb], O[md][hb][4 * r4 + 3] * inv[hb]};
-                const int col = L::column(w, md, gq, 4 * r4) - 128 * md;
-                *(LDS_AS f32x4*)(stage + OutStage::offset(32 * hb + hq, col)) = v;
-            }
-        lds_barrier();
-        // 128 heads x 32 units of 4 columns; consecutive lanes take consecutive units.
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int u = threadIdx.x + 256 * j;
-            const int h = u >> 5, c4 = u & 31;
-            const f32x4 v = *(const LDS_AS f32x4*)(stage + OutStage::offset(h, 4 * c4));
-            const int64_t o = (row0 + h) * kLatent + 128 * md + 4 * c4;
-            // Partials are stored in the output's precision.
-            void* base = it.partial >= 0 ? a.part_out : a.out;
-            if constexpr (OUT32) {
-                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + o) = v;
-            } else {
-                const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-                *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(base) + o) = b;
-            }
+        // ---- finalize ----
+        const float l = sum_xor32(l_part);
+        const int nh = a.num_heads;
+        const float lse = l > 0.f ? (m_ref + __log2f(l)) * kLn2 : -INFINITY;
+        if (gq == 0) {
+            l_sh[32 * w + hq] = l;
+            if (it.partial >= 0)
+                a.part_lse[(int64_t)it.partial * nh + head] = lse;
+            else if (a.lse)
+                a.lse[(int64_t)it.row * nh + head] = lse;
         }
         lds_barrier();
+        float inv[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+            const float lh = l_sh[32 * hb + hq];
+            inv[hb] = lh > 0.f ? a.out_scale / lh : 0.f;
+        }
+        // Output rows of this item: [partial or row][head_begin + h][512].
+        const int64_t row0 = (it.partial >= 0 ? (int64_t)it.partial * nh : (int64_t)it.row * nh) + it.head_begin;
+        LDS_AS char* stage = (LDS_AS char*)smem;  // every wave is past its last tile read
+#pragma unroll
+        for (int md = 0; md < kDW; ++md) {
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x4 v = {O[md][hb][4 * r4] * inv[hb], O[md][hb][4 * r4 + 1] * inv[hb],
+                                     O[md][hb][4 * r4 + 2] * inv[hb], O[md][hb][4 * r4 + 3] * inv[hb]};
+                    const int col = L::column(w, md, gq, 4 * r4) - 128 * md;
+                    *(LDS_AS f32x4*)(stage + OutStage::offset(32 * hb + hq, col)) = v;
+                }
+            lds_barrier();
+            // 128 heads x 32 units of 4 columns; consecutive lanes take consecutive units.
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int u = tid + 256 * j;
+                const int h = u >> 5, c4 = u & 31;
+                const f32x4 v = *(const LDS_AS f32x4*)(stage + OutStage::offset(h, 4 * c4));
+                const int64_t o = (row0 + h) * kLatent + 128 * md + 4 * c4;
+                // Partials are stored in the output's precision.
+                void* base = it.partial >= 0 ? a.part_out : a.out;
+                if constexpr (OUT32) {
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + o) = v;
+                } else {
+                    const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+                    *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(base) + o) = b;
+                }
+            }
+            lds_barrier();
+        }
     }
 }
 
 }  // namespace
 
-int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num_items, void* stream) {
+int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num_workers, void* stream) {
     hipStream_t s = (hipStream_t)stream;
-    const dim3 grid(num_items), block(256);
+    const dim3 grid(num_workers), block(256);
     const bool kv8 = kv_dtype == MLA_DTYPE_FP8_E4M3FN;
     const bool o32 = out_dtype == MLA_DTYPE_FP32;
     if (kv8 && o32)

@@ -20,7 +20,7 @@ struct Variant {
     int hw;
     int hs;
     int wgs_per_cu;
-    int min_chunk;  // shortest chunk worth a partial (tokens)
+    int item_cost;  // fixed cost of one work item, in 32-token tiles (measured)
 };
 
 // Selects the kernel instantiation for these parameters. Returns false when the
@@ -37,6 +37,7 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
 
 struct DecodeArgs {
     const mla_work_item* items;
+    const int32_t* workers;  // worker w processes items [workers[w], workers[w+1])
     const uint16_t* q_nope;  // bf16 bits
     int64_t qn_sn, qn_sh;
     const uint16_t* q_rope;
@@ -67,9 +68,9 @@ struct MergePartialsArgs {
 
 // Kernel launchers (device code lives in mla_kernels.hip). Return hipError_t as int.
 int launch_decode(const Variant& v, int kv_dtype, int out_dtype, const DecodeArgs& a,
-                  int num_items, void* stream);
+                  int num_workers, void* stream);
 // The 128-head kernel (latent columns split across the waves), mla_decode_h128.hip.
-int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num_items,
+int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num_workers,
                        void* stream);
 int launch_merge_partials(int out_dtype, const MergePartialsArgs& a, int num_merges,
                           void* stream);

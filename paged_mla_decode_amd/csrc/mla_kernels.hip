@@ -63,294 +63,273 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const mla_work_item it = a.items[blockIdx.x];
-    const int ps = a.page_size;
-    const int kv_begin = it.kv_begin;
-    int kv_end = it.kv_end;
-    if (a.kv_lens) kv_end = min(kv_end, a.kv_lens[it.request]);
-    const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + kTile - 1) / kTile : 0;
+    // Persistent worker: the plan's items [workers[w], workers[w+1]) in order.
+    const int item_end = a.workers[blockIdx.x + 1];
+    for (int item = a.workers[blockIdx.x]; item < item_end; ++item) {
+        const mla_work_item it = a.items[item];
+        const int ps = a.page_size;
+        const int kv_begin = it.kv_begin;
+        int kv_end = it.kv_end;
+        if (a.kv_lens) kv_end = min(kv_end, a.kv_lens[it.request]);
+        const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + kTile - 1) / kTile : 0;
 
-    // Lane roles. hq: head (MFMA N index); gq: lane group along the K dim.
-    const int hq = HW == 32 ? (lane & 31) : (lane & 15);
-    const int gq = HW == 32 ? (lane >> 5) : (lane >> 4);
-    const int head = it.head_begin + w * HW + hq;
+        // Lane roles. hq: head (MFMA N index); gq: lane group along the K dim.
+        const int hq = HW == 32 ? (lane & 31) : (lane & 15);
+        const int gq = HW == 32 ? (lane >> 5) : (lane >> 4);
+        const int head = it.head_begin + w * HW + hq;
 
-    // ---- absorbed query -> registers (B operand of the score MFMA) ----
-    bf16x8 q[kSteps];
-    {
-        const uint16_t* qn = a.q_nope + (int64_t)it.row * a.qn_sn + (int64_t)head * a.qn_sh;
-        const uint16_t* qr = a.q_rope + (int64_t)it.row * a.qr_sn + (int64_t)head * a.qr_sh;
+        // ---- absorbed query -> registers (B operand of the score MFMA) ----
+        bf16x8 q[kSteps];
+        {
+            const uint16_t* qn = a.q_nope + (int64_t)it.row * a.qn_sn + (int64_t)head * a.qn_sh;
+            const uint16_t* qr = a.q_rope + (int64_t)it.row * a.qr_sn + (int64_t)head * a.qr_sh;
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            const int k0 = (HW == 32 ? 16 : 32) * s + 8 * gq;
-            q[s] = (s < kSteps * 8 / 9) ? load_bf16x8(qn + k0) : load_bf16x8(qr + (k0 - kLatent));
-        }
-        // Let the query land before any tile load is issued: the compiler does not
-        // see the tile loads, so its own waits for these registers inside the
-        // loop would otherwise also drain the tiles in flight.
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    }
-
-    // ---- per-lane LDS bases (see mla_tile_layout.h) ----
-    int sbase[SA::kBases], pbase[PA::kBases];
-#pragma unroll
-    for (int i = 0; i < SA::kBases; ++i) sbase[i] = SA::base(lane, i);
-#pragma unroll
-    for (int i = 0; i < PA::kBases; ++i) pbase[i] = PA::base(lane, i);
-    // Global byte offset of the chunk this lane loads, within its row (chunk group 0).
-    const int dma_lane_off = L::block_chunk(0, lane) * 16;
-
-    // ---- page-table lookups for the tokens this lane loads ----
-    // A wave's lanes load TPB consecutive tokens per token block, which span at
-    // most TPB consecutive page-table entries: one scalar buffer load fetches
-    // them, and each lane picks its own. Tail tokens are clamped to the last
-    // valid token, so no load ever leaves the request's pages.
-    using IdxVec = typename std::conditional<L::kTPB == 8, i32x8s, i32x16s>::type;
-    const i32x4s idx_rsrc = make_rsrc(a.kv_indices, a.num_indices);
-    IdxVec sidx[kNTok];
-    int p0[kNTok];
-    auto fetch_idx = [&](int tile) {  // issue the scalar loads for a tile
-        const int tstart = kv_begin + tile * kTile;
-#pragma unroll
-        for (int k = 0; k < kNTok; ++k) {
-            const int tb = HS >= L::kNTB ? (w % L::kNTB) : (w + HS * k);
-            const int first = min(tstart + tb * L::kTPB, kv_end - 1);
-            p0[k] = first / ps;
-            const int off = (it.page_base + p0[k]) * 4;
-            if constexpr (L::kTPB == 8)
-                sidx[k] = sbuffer_load_x8(idx_rsrc, off, 0);
-            else
-                sidx[k] = sbuffer_load_x16(idx_rsrc, off, 0);
-        }
-    };
-    auto resolve_rows = [&](int tile, const uint8_t** rowp) {  // lane row pointers of a tile
-        const int tstart = kv_begin + tile * kTile;
-#pragma unroll
-        for (int k = 0; k < kNTok; ++k) {
-            const int tb = HS >= L::kNTB ? (w % L::kNTB) : (w + HS * k);
-            const int tau = min(tstart + L::block_token(tb, lane), kv_end - 1);
-            const int pi = tau / ps;
-            const int page = select_lane<L::kTPB>(sidx[k], pi - p0[k]);
-            rowp[k] = a.cache + ((int64_t)page * ps + (tau - pi * ps)) * L::kRowBytes + dma_lane_off;
-        }
-    };
-    auto issue_tile = [&](LDS_AS char* base, const uint8_t* const* rowp) {
-#pragma unroll
-        for (int i = 0; i < kLoadsMax; ++i) {
-            const int b = w + HS * i;
-            if (L::kNB % HS != 0 && b >= L::kNB) break;
-            const int k = HS >= L::kNTB ? 0 : i % (L::kNTB / HS);
-            const int cg = b / L::kNTB;
-            dma16(rowp[k] + cg * L::kCG * 16, base + b * 1024);
-        }
-    };
-
-    // ---- accumulators ----
-    f32x16 O32[HW == 32 ? kDBlocks : 1];
-    f32x4 O16[HW == 16 ? kDBlocks : 1];
-    // Softmax reference point (log2 units) per head: the first tile's max. The
-    // running true max is tracked; if it ever exceeds the reference by more
-    // than kOverflowSlack the chunk is recomputed with the true max as the
-    // reference (which then bounds every probability by 1). O is only ever
-    // touched by MFMAs inside the loop.
-    float m_ref = -INFINITY, m_true = -INFINITY;
-    float l_part = 0.f;
-    __shared__ int rerun_flag[HS];
-
-    for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int i = 0; i < (HW == 32 ? kDBlocks : 1); ++i) O32[i] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < (HW == 16 ? kDBlocks : 1); ++i) O16[i] = f32x4{};
-    l_part = 0.f;
-
-    if (ntiles > 0) {
-        // One tile step. T is the buffer computed, N the one being filled;
-        // distinct restrict-qualified parameters tell the compiler the two
-        // never alias, so it adds no waits of its own for the direct-to-LDS
-        // loads: the explicit vmcnt waits order them. Step i = -1 only starts
-        // the pipeline (loads of tile 0). Every vector memory load in flight
-        // here is a tile load: the page table is read through the scalar path.
-        fetch_idx(0);
-        auto tile_step = [&](const LDS_AS char* __restrict__ T, LDS_AS char* __restrict__ N, int i) {
-            const int tstart = kv_begin + i * kTile;
-            const int ahead = i + kStages - 1;  // the tile whose loads this step issues
-            if (ahead < ntiles) {
-                const uint8_t* rowp[kNTok];
-                resolve_rows(ahead, rowp);
-                if (ahead + 1 < ntiles) fetch_idx(ahead + 1);
-                issue_tile(N, rowp);
+            for (int s = 0; s < kSteps; ++s) {
+                const int k0 = (HW == 32 ? 16 : 32) * s + 8 * gq;
+                q[s] = (s < kSteps * 8 / 9) ? load_bf16x8(qn + k0) : load_bf16x8(qr + (k0 - kLatent));
             }
-            if (i < 0) return;  // pipeline fill
-            // Tiles issued after tile i and still outstanding: min(kStages-1, ntiles-1-i).
-            wait_tiles_barrier<kStages - 1, kLoadsMin>(min(kStages - 1, ntiles - 1 - i));
+            // Let the query land before any tile load is issued: the compiler does not
+            // see the tile loads, so its own waits for these registers inside the
+            // loop would otherwise also drain the tiles in flight.
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
 
-            const int nvalid = min(kTile, kv_end - tstart);
+        // ---- per-lane LDS bases (see mla_tile_layout.h) ----
+        int sbase[SA::kBases], pbase[PA::kBases];
+#pragma unroll
+        for (int i = 0; i < SA::kBases; ++i) sbase[i] = SA::base(lane, i);
+#pragma unroll
+        for (int i = 0; i < PA::kBases; ++i) pbase[i] = PA::base(lane, i);
+        // Global byte offset of the chunk this lane loads, within its row (chunk group 0).
+        const int dma_lane_off = L::block_chunk(0, lane) * 16;
 
-            // ---- score: S^T = C . Q^T ----
-            float sv[NV];
-            if constexpr (HW == 32) {
-                f32x16 S = {};
-                auto load = [&](int s) -> bf16x8 {
-                    const int off = sbase[SA::base_index(s, 0)] + SA::delta(s);
+        // ---- page-table lookups for the tokens this lane loads ----
+        // A wave's lanes load TPB consecutive tokens per token block, which span at
+        // most TPB consecutive page-table entries: one scalar buffer load fetches
+        // them, and each lane picks its own. Tail tokens are clamped to the last
+        // valid token, so no load ever leaves the request's pages.
+        using IdxVec = typename std::conditional<L::kTPB == 8, i32x8s, i32x16s>::type;
+        const i32x4s idx_rsrc = make_rsrc(a.kv_indices, a.num_indices);
+        IdxVec sidx[kNTok];
+        int p0[kNTok];
+        auto fetch_idx = [&](int tile) {  // issue the scalar loads for a tile
+            const int tstart = kv_begin + tile * kTile;
+#pragma unroll
+            for (int k = 0; k < kNTok; ++k) {
+                const int tb = HS >= L::kNTB ? (w % L::kNTB) : (w + HS * k);
+                const int first = min(tstart + tb * L::kTPB, kv_end - 1);
+                p0[k] = first / ps;
+                const int off = (it.page_base + p0[k]) * 4;
+                if constexpr (L::kTPB == 8)
+                    sidx[k] = sbuffer_load_x8(idx_rsrc, off, 0);
+                else
+                    sidx[k] = sbuffer_load_x16(idx_rsrc, off, 0);
+            }
+        };
+        auto resolve_rows = [&](int tile, const uint8_t** rowp) {  // lane row pointers of a tile
+            const int tstart = kv_begin + tile * kTile;
+#pragma unroll
+            for (int k = 0; k < kNTok; ++k) {
+                const int tb = HS >= L::kNTB ? (w % L::kNTB) : (w + HS * k);
+                const int tau = min(tstart + L::block_token(tb, lane), kv_end - 1);
+                const int pi = tau / ps;
+                const int page = select_lane<L::kTPB>(sidx[k], pi - p0[k]);
+                rowp[k] = a.cache + ((int64_t)page * ps + (tau - pi * ps)) * L::kRowBytes + dma_lane_off;
+            }
+        };
+        auto issue_tile = [&](LDS_AS char* base, const uint8_t* const* rowp) {
+#pragma unroll
+            for (int i = 0; i < kLoadsMax; ++i) {
+                const int b = w + HS * i;
+                if (L::kNB % HS != 0 && b >= L::kNB) break;
+                const int k = HS >= L::kNTB ? 0 : i % (L::kNTB / HS);
+                const int cg = b / L::kNTB;
+                dma16(rowp[k] + cg * L::kCG * 16, base + b * 1024);
+            }
+        };
+
+        // ---- accumulators ----
+        f32x16 O32[HW == 32 ? kDBlocks : 1];
+        f32x4 O16[HW == 16 ? kDBlocks : 1];
+        // Softmax reference point (log2 units) per head: the first tile's max. The
+        // running true max is tracked; if it ever exceeds the reference by more
+        // than kOverflowSlack the chunk is recomputed with the true max as the
+        // reference (which then bounds every probability by 1). O is only ever
+        // touched by MFMAs inside the loop.
+        float m_ref = -INFINITY, m_true = -INFINITY;
+        float l_part = 0.f;
+        __shared__ int rerun_flag[HS];
+
+        for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int i = 0; i < (HW == 32 ? kDBlocks : 1); ++i) O32[i] = f32x16{};
+#pragma unroll
+        for (int i = 0; i < (HW == 16 ? kDBlocks : 1); ++i) O16[i] = f32x4{};
+        l_part = 0.f;
+
+        if (ntiles > 0) {
+            // One tile step. T is the buffer computed, N the one being filled;
+            // distinct restrict-qualified parameters tell the compiler the two
+            // never alias, so it adds no waits of its own for the direct-to-LDS
+            // loads: the explicit vmcnt waits order them. Step i = -1 only starts
+            // the pipeline (loads of tile 0). Every vector memory load in flight
+            // here is a tile load: the page table is read through the scalar path.
+            fetch_idx(0);
+            auto tile_step = [&](const LDS_AS char* __restrict__ T, LDS_AS char* __restrict__ N, int i) {
+                const int tstart = kv_begin + i * kTile;
+                const int ahead = i + kStages - 1;  // the tile whose loads this step issues
+                if (ahead < ntiles) {
+                    const uint8_t* rowp[kNTok];
+                    resolve_rows(ahead, rowp);
+                    if (ahead + 1 < ntiles) fetch_idx(ahead + 1);
+                    issue_tile(N, rowp);
+                }
+                if (i < 0) return;  // pipeline fill
+                // Tiles issued after tile i and still outstanding: min(kStages-1, ntiles-1-i).
+                wait_tiles_barrier<kStages - 1, kLoadsMin>(min(kStages - 1, ntiles - 1 - i));
+
+                const int nvalid = min(kTile, kv_end - tstart);
+
+                // ---- score: S^T = C . Q^T ----
+                float sv[NV];
+                if constexpr (HW == 32) {
+                    f32x16 S = {};
+                    auto load = [&](int s) -> bf16x8 {
+                        const int off = sbase[SA::base_index(s, 0)] + SA::delta(s);
+                        if constexpr (KV8) {
+                            const i32x2 raw = *(const LDS_AS i32x2*)(T + off);
+                            return fp8x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]);
+                        } else {
+                            return *(const LDS_AS bf16x8*)(T + off);
+                        }
+                    };
+                    pipelined<kSteps, kPipe, 1, 1>(load, [&](int s, bf16x8 A) { S = mfma32(A, q[s], S); });
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sv[r] = S[r];
+                } else {
+                    f32x4 S0 = {}, S1 = {};
+                    struct Pair { bf16x8 a0, a1; };
+                    auto load = [&](int s) -> Pair {
+                        const int off0 = sbase[SA::base_index(s, 0)] + SA::delta(s);
+                        const int off1 = sbase[SA::base_index(s, 1)] + SA::delta(s);
+                        if constexpr (KV8) {
+                            const i32x2 r0 = *(const LDS_AS i32x2*)(T + off0);
+                            const i32x2 r1 = *(const LDS_AS i32x2*)(T + off1);
+                            return {fp8x8_to_bf16((unsigned)r0[0], (unsigned)r0[1]),
+                                    fp8x8_to_bf16((unsigned)r1[0], (unsigned)r1[1])};
+                        } else {
+                            return {*(const LDS_AS bf16x8*)(T + off0), *(const LDS_AS bf16x8*)(T + off1)};
+                        }
+                    };
+                    pipelined<kSteps, kPipe, 2, 2>(load, [&](int s, Pair A) {
+                        S0 = mfma16(A.a0, q[s], S0);
+                        S1 = mfma16(A.a1, q[s], S1);
+                    });
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        sv[r] = S0[r];
+                        sv[4 + r] = S1[r];
+                    }
+                }
+
+                // ---- scale, mask the tail, tile max ----
+                float tmax = -INFINITY;
+#pragma unroll
+                for (int r = 0; r < NV; ++r) {
+                    // token of value r: HW32: 16*(r/8) + 8*g + r%8; HW16: 8*g + r
+                    const int tok = HW == 32 ? (16 * (r >> 3) + 8 * gq + (r & 7)) : (8 * gq + r);
+                    float v = sv[r] * a.scale_log2;
+                    v = tok < nvalid ? v : -INFINITY;
+                    sv[r] = v;
+                    tmax = fmaxf(tmax, v);
+                }
+                if (HW == 16) tmax = max_xor16(tmax);
+                tmax = max_xor32(tmax);
+                if (pass == 0 && i == 0) m_ref = tmax;
+                m_true = fmaxf(m_true, tmax);
+
+                // ---- probabilities relative to the reference ----
+                float p[NV];
+#pragma unroll
+                for (int r = 0; r < NV; ++r) {
+                    p[r] = fast_exp2(sv[r] - m_ref);
+                    l_part += p[r];
+                }
+
+                // ---- O^T += C^T . P^T ----
+                constexpr int kKK = HW == 32 ? 2 : 1;
+                bf16x8 P[kKK], Plo[kKK];
+#pragma unroll
+                for (int kk = 0; kk < kKK; ++kk)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        P[kk][e] = (__bf16)p[8 * kk + e];
+                        if (OUT32) Plo[kk][e] = (__bf16)(p[8 * kk + e] - (float)P[kk][e]);
+                    }
+                // Step j covers output block md = j % kDBlocks of token half kk = j / kDBlocks.
+                auto load_pv = [&](int j) -> bf16x8 {
+                    const int md = j % kDBlocks, kk = j / kDBlocks;
+                    const int pb = pbase[PA::base_index(md)];
                     if constexpr (KV8) {
-                        const i32x2 raw = *(const LDS_AS i32x2*)(T + off);
+                        const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                            (LDS_AS i32x2*)(T + pb + PA::delta(md, kk, 0)));
                         return fp8x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]);
                     } else {
-                        return *(const LDS_AS bf16x8*)(T + off);
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (LDS_AS i16x4*)(T + pb + PA::delta(md, kk, 0)));
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (LDS_AS i16x4*)(T + pb + PA::delta(md, kk, 1)));
+                        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     }
                 };
-                pipelined<kSteps, kPipe, 1, 1>(load, [&](int s, bf16x8 A) { S = mfma32(A, q[s], S); });
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sv[r] = S[r];
-            } else {
-                f32x4 S0 = {}, S1 = {};
-                struct Pair { bf16x8 a0, a1; };
-                auto load = [&](int s) -> Pair {
-                    const int off0 = sbase[SA::base_index(s, 0)] + SA::delta(s);
-                    const int off1 = sbase[SA::base_index(s, 1)] + SA::delta(s);
-                    if constexpr (KV8) {
-                        const i32x2 r0 = *(const LDS_AS i32x2*)(T + off0);
-                        const i32x2 r1 = *(const LDS_AS i32x2*)(T + off1);
-                        return {fp8x8_to_bf16((unsigned)r0[0], (unsigned)r0[1]),
-                                fp8x8_to_bf16((unsigned)r1[0], (unsigned)r1[1])};
+                pipelined<kKK * kDBlocks, kPipe, KV8 ? 1 : 2, OUT32 ? 2 : 1>(load_pv, [&](int j, bf16x8 A) {
+                    const int md = j % kDBlocks, kk = j / kDBlocks;
+                    if constexpr (HW == 32) {
+                        O32[md] = mfma32(A, P[kk], O32[md]);
+                        if (OUT32) O32[md] = mfma32(A, Plo[kk], O32[md]);
                     } else {
-                        return {*(const LDS_AS bf16x8*)(T + off0), *(const LDS_AS bf16x8*)(T + off1)};
+                        O16[md] = mfma16(A, P[kk], O16[md]);
+                        if (OUT32) O16[md] = mfma16(A, Plo[kk], O16[md]);
                     }
-                };
-                pipelined<kSteps, kPipe, 2, 2>(load, [&](int s, Pair A) {
-                    S0 = mfma16(A.a0, q[s], S0);
-                    S1 = mfma16(A.a1, q[s], S1);
                 });
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    sv[r] = S0[r];
-                    sv[4 + r] = S1[r];
-                }
-            }
-
-            // ---- scale, mask the tail, tile max ----
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < NV; ++r) {
-                // token of value r: HW32: 16*(r/8) + 8*g + r%8; HW16: 8*g + r
-                const int tok = HW == 32 ? (16 * (r >> 3) + 8 * gq + (r & 7)) : (8 * gq + r);
-                float v = sv[r] * a.scale_log2;
-                v = tok < nvalid ? v : -INFINITY;
-                sv[r] = v;
-                tmax = fmaxf(tmax, v);
-            }
-            if (HW == 16) tmax = max_xor16(tmax);
-            tmax = max_xor32(tmax);
-            if (pass == 0 && i == 0) m_ref = tmax;
-            m_true = fmaxf(m_true, tmax);
-
-            // ---- probabilities relative to the reference ----
-            float p[NV];
-#pragma unroll
-            for (int r = 0; r < NV; ++r) {
-                p[r] = fast_exp2(sv[r] - m_ref);
-                l_part += p[r];
-            }
-
-            // ---- O^T += C^T . P^T ----
-            constexpr int kKK = HW == 32 ? 2 : 1;
-            bf16x8 P[kKK], Plo[kKK];
-#pragma unroll
-            for (int kk = 0; kk < kKK; ++kk)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    P[kk][e] = (__bf16)p[8 * kk + e];
-                    if (OUT32) Plo[kk][e] = (__bf16)(p[8 * kk + e] - (float)P[kk][e]);
-                }
-            // Step j covers output block md = j % kDBlocks of token half kk = j / kDBlocks.
-            auto load_pv = [&](int j) -> bf16x8 {
-                const int md = j % kDBlocks, kk = j / kDBlocks;
-                const int pb = pbase[PA::base_index(md)];
-                if constexpr (KV8) {
-                    const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (LDS_AS i32x2*)(T + pb + PA::delta(md, kk, 0)));
-                    return fp8x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]);
-                } else {
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (LDS_AS i16x4*)(T + pb + PA::delta(md, kk, 0)));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (LDS_AS i16x4*)(T + pb + PA::delta(md, kk, 1)));
-                    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                }
+                lds_barrier();  // everyone is done with this buffer before it is refilled
             };
-            pipelined<kKK * kDBlocks, kPipe, KV8 ? 1 : 2, OUT32 ? 2 : 1>(load_pv, [&](int j, bf16x8 A) {
-                const int md = j % kDBlocks, kk = j / kDBlocks;
-                if constexpr (HW == 32) {
-                    O32[md] = mfma32(A, P[kk], O32[md]);
-                    if (OUT32) O32[md] = mfma32(A, Plo[kk], O32[md]);
-                } else {
-                    O16[md] = mfma16(A, P[kk], O16[md]);
-                    if (OUT32) O16[md] = mfma16(A, Plo[kk], O16[md]);
-                }
-            });
-            lds_barrier();  // everyone is done with this buffer before it is refilled
-        };
-        // Tile t lives in buffer t % kStages. Step i computes tile i and fills
-        // the buffer of tile i-1 (freed by the previous step) with tile
-        // i + kStages - 1; steps i < 0 only fill the pipeline.
-        int cur = 1 % kStages;  // buffer of tile -(kStages-1)
-        for (int i = -(kStages - 1); i < ntiles; ++i) {
-            const int nxt = cur == 0 ? kStages - 1 : cur - 1;  // buffer of tile i-1 = tile i+kStages-1
-            tile_step((const LDS_AS char*)smem + cur * L::kTileBytes,
-                      (LDS_AS char*)smem + nxt * L::kTileBytes, i);
-            cur = cur + 1 == kStages ? 0 : cur + 1;
-        }
-    }
-    // Did any head of the workgroup outgrow its reference? All waves must agree,
-    // since the tiles are loaded cooperatively.
-    const bool over = __builtin_amdgcn_ballot_w64(m_true > m_ref + kOverflowSlack) != 0;
-    if (lane == 0) rerun_flag[w] = over ? 1 : 0;
-    lds_barrier();
-    int any = 0;
-#pragma unroll
-    for (int k = 0; k < HS; ++k) any |= rerun_flag[k];
-    lds_barrier();
-    if (!any) break;
-    m_ref = m_true;  // second pass: every probability is at most 1
-    }
-
-    // ---- finalize: l across the lanes of a head, normalise, write ----
-    const float m_run = m_ref;
-    float l = l_part;
-    if (HW == 16) l = sum_xor16(l);
-    l = sum_xor32(l);
-    const bool empty = !(l > 0.f);
-    const float inv = empty ? 0.f : (a.out_scale / l);
-    const float lse = empty ? -INFINITY : (m_run + __log2f(l)) * kLn2;
-    const int nh = a.num_heads;
-
-    if (it.partial >= 0 && OUT32) {
-        float* po = reinterpret_cast<float*>(a.part_out) + ((int64_t)it.partial * nh + head) * kLatent;
-        if constexpr (HW == 32) {
-#pragma unroll
-            for (int md = 0; md < kDBlocks; ++md)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int d = 32 * md + 8 * r4 + 4 * gq;
-                    f32x4 v = {O32[md][4 * r4] * inv, O32[md][4 * r4 + 1] * inv,
-                               O32[md][4 * r4 + 2] * inv, O32[md][4 * r4 + 3] * inv};
-                    *reinterpret_cast<f32x4*>(po + d) = v;
-                }
-        } else {
-#pragma unroll
-            for (int md = 0; md < kDBlocks; ++md) {
-                const int d = 16 * md + 4 * gq;
-                *reinterpret_cast<f32x4*>(po + d) = O16[md] * inv;
+            // Tile t lives in buffer t % kStages. Step i computes tile i and fills
+            // the buffer of tile i-1 (freed by the previous step) with tile
+            // i + kStages - 1; steps i < 0 only fill the pipeline.
+            int cur = 1 % kStages;  // buffer of tile -(kStages-1)
+            for (int i = -(kStages - 1); i < ntiles; ++i) {
+                const int nxt = cur == 0 ? kStages - 1 : cur - 1;  // buffer of tile i-1 = tile i+kStages-1
+                tile_step((const LDS_AS char*)smem + cur * L::kTileBytes,
+                          (LDS_AS char*)smem + nxt * L::kTileBytes, i);
+                cur = cur + 1 == kStages ? 0 : cur + 1;
             }
         }
-        if (gq == 0) a.part_lse[(int64_t)it.partial * nh + head] = lse;
-    } else {
-        // bf16 partials (bf16 output) take the same path as the output itself.
-        const int64_t orow = it.partial >= 0 ? (int64_t)it.partial * nh + head : (int64_t)it.row * nh + head;
-        void* obase = it.partial >= 0 ? a.part_out : a.out;
-        if constexpr (OUT32) {
-            float* o = reinterpret_cast<float*>(obase) + orow * kLatent;
+        // Did any head of the workgroup outgrow its reference? All waves must agree,
+        // since the tiles are loaded cooperatively.
+        const bool over = __builtin_amdgcn_ballot_w64(m_true > m_ref + kOverflowSlack) != 0;
+        if (lane == 0) rerun_flag[w] = over ? 1 : 0;
+        lds_barrier();
+        int any = 0;
+#pragma unroll
+        for (int k = 0; k < HS; ++k) any |= rerun_flag[k];
+        lds_barrier();
+        if (!any) break;
+        m_ref = m_true;  // second pass: every probability is at most 1
+        }
+
+        // ---- finalize: l across the lanes of a head, normalise, write ----
+        const float m_run = m_ref;
+        float l = l_part;
+        if (HW == 16) l = sum_xor16(l);
+        l = sum_xor32(l);
+        const bool empty = !(l > 0.f);
+        const float inv = empty ? 0.f : (a.out_scale / l);
+        const float lse = empty ? -INFINITY : (m_run + __log2f(l)) * kLn2;
+        const int nh = a.num_heads;
+
+        if (it.partial >= 0 && OUT32) {
+            float* po = reinterpret_cast<float*>(a.part_out) + ((int64_t)it.partial * nh + head) * kLatent;
             if constexpr (HW == 32) {
 #pragma unroll
                 for (int md = 0; md < kDBlocks; ++md)
@@ -359,39 +338,64 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
                         const int d = 32 * md + 8 * r4 + 4 * gq;
                         f32x4 v = {O32[md][4 * r4] * inv, O32[md][4 * r4 + 1] * inv,
                                    O32[md][4 * r4 + 2] * inv, O32[md][4 * r4 + 3] * inv};
-                        *reinterpret_cast<f32x4*>(o + d) = v;
-                    }
-            } else {
-#pragma unroll
-                for (int md = 0; md < kDBlocks; ++md)
-                    *reinterpret_cast<f32x4*>(o + 16 * md + 4 * gq) = O16[md] * inv;
-            }
-        } else {
-            __bf16* o = reinterpret_cast<__bf16*>(obase) + orow * kLatent;
-            if constexpr (HW == 32) {
-#pragma unroll
-                for (int md = 0; md < kDBlocks; ++md)
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int d = 32 * md + 8 * r4 + 4 * gq;
-                        bf16x4 v = {(__bf16)(O32[md][4 * r4] * inv), (__bf16)(O32[md][4 * r4 + 1] * inv),
-                                    (__bf16)(O32[md][4 * r4 + 2] * inv), (__bf16)(O32[md][4 * r4 + 3] * inv)};
-                        *reinterpret_cast<bf16x4*>(o + d) = v;
+                        *reinterpret_cast<f32x4*>(po + d) = v;
                     }
             } else {
 #pragma unroll
                 for (int md = 0; md < kDBlocks; ++md) {
-                    const f32x4 x = O16[md] * inv;
-                    bf16x4 v = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-                    *reinterpret_cast<bf16x4*>(o + 16 * md + 4 * gq) = v;
+                    const int d = 16 * md + 4 * gq;
+                    *reinterpret_cast<f32x4*>(po + d) = O16[md] * inv;
                 }
             }
-        }
-        if (gq == 0) {
-            if (it.partial >= 0)
-                a.part_lse[orow] = lse;
-            else if (a.lse)
-                a.lse[orow] = lse;
+            if (gq == 0) a.part_lse[(int64_t)it.partial * nh + head] = lse;
+        } else {
+            // bf16 partials (bf16 output) take the same path as the output itself.
+            const int64_t orow = it.partial >= 0 ? (int64_t)it.partial * nh + head : (int64_t)it.row * nh + head;
+            void* obase = it.partial >= 0 ? a.part_out : a.out;
+            if constexpr (OUT32) {
+                float* o = reinterpret_cast<float*>(obase) + orow * kLatent;
+                if constexpr (HW == 32) {
+#pragma unroll
+                    for (int md = 0; md < kDBlocks; ++md)
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const int d = 32 * md + 8 * r4 + 4 * gq;
+                            f32x4 v = {O32[md][4 * r4] * inv, O32[md][4 * r4 + 1] * inv,
+                                       O32[md][4 * r4 + 2] * inv, O32[md][4 * r4 + 3] * inv};
+                            *reinterpret_cast<f32x4*>(o + d) = v;
+                        }
+                } else {
+#pragma unroll
+                    for (int md = 0; md < kDBlocks; ++md)
+                        *reinterpret_cast<f32x4*>(o + 16 * md + 4 * gq) = O16[md] * inv;
+                }
+            } else {
+                __bf16* o = reinterpret_cast<__bf16*>(obase) + orow * kLatent;
+                if constexpr (HW == 32) {
+#pragma unroll
+                    for (int md = 0; md < kDBlocks; ++md)
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const int d = 32 * md + 8 * r4 + 4 * gq;
+                            bf16x4 v = {(__bf16)(O32[md][4 * r4] * inv), (__bf16)(O32[md][4 * r4 + 1] * inv),
+                                        (__bf16)(O32[md][4 * r4 + 2] * inv), (__bf16)(O32[md][4 * r4 + 3] * inv)};
+                            *reinterpret_cast<bf16x4*>(o + d) = v;
+                        }
+                } else {
+#pragma unroll
+                    for (int md = 0; md < kDBlocks; ++md) {
+                        const f32x4 x = O16[md] * inv;
+                        bf16x4 v = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+                        *reinterpret_cast<bf16x4*>(o + 16 * md + 4 * gq) = v;
+                    }
+                }
+            }
+            if (gq == 0) {
+                if (it.partial >= 0)
+                    a.part_lse[orow] = lse;
+                else if (a.lse)
+                    a.lse[orow] = lse;
+            }
         }
     }
 }
@@ -543,14 +547,14 @@ static int launch_decode_hs(int kv_dtype, int out_dtype, const DecodeArgs& a, in
     return (int)hipGetLastError();
 }
 
-int launch_decode(const Variant& v, int kv_dtype, int out_dtype, const DecodeArgs& a, int num_items,
+int launch_decode(const Variant& v, int kv_dtype, int out_dtype, const DecodeArgs& a, int num_workers,
                   void* stream) {
     hipStream_t s = (hipStream_t)stream;
-    if (num_items <= 0) return 0;
-    if (v.hw == 32 && v.hs == 4) return launch_decode_h128(kv_dtype, out_dtype, a, num_items, stream);
-    if (v.hw == 16 && v.hs == 1) return launch_decode_hs<16, 1>(kv_dtype, out_dtype, a, num_items, s);
-    if (v.hw == 16 && v.hs == 2) return launch_decode_hs<16, 2>(kv_dtype, out_dtype, a, num_items, s);
-    if (v.hw == 16 && v.hs == 4) return launch_decode_hs<16, 4>(kv_dtype, out_dtype, a, num_items, s);
+    if (num_workers <= 0) return 0;
+    if (v.hw == 32 && v.hs == 4) return launch_decode_h128(kv_dtype, out_dtype, a, num_workers, stream);
+    if (v.hw == 16 && v.hs == 1) return launch_decode_hs<16, 1>(kv_dtype, out_dtype, a, num_workers, s);
+    if (v.hw == 16 && v.hs == 2) return launch_decode_hs<16, 2>(kv_dtype, out_dtype, a, num_workers, s);
+    if (v.hw == 16 && v.hs == 4) return launch_decode_hs<16, 4>(kv_dtype, out_dtype, a, num_workers, s);
     return (int)hipErrorInvalidValue;
 }
 

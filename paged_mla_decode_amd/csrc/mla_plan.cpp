@@ -7,18 +7,23 @@
 // split into, and balances long and short requests across the chip; the
 // result is reused by every layer. Pure host code: no HIP calls.
 //
-// Policy:
-//   * Total work T = sum over query rows of their token counts. With G
-//     workgroups resident at once (compute units x workgroups per CU), the
-//     target chunk is ceil(T / G) tokens, never below the variant's min_chunk
-//     (a partial costs H*512 values, bf16 or fp32, written and read back, plus a second load
-//     of the query), rounded up to the 32-token tile.
-//   * A row longer than the target is cut into equal tile-aligned chunks
-//     (at most max_splits). Short rows stay whole and write their output
-//     directly; only split rows use partial slots and a merge.
-//   * Work items are ordered longest first, so the hardware dispatcher, which
-//     hands workgroups to CUs as they free up, approximates longest-processing-
-//     time-first scheduling.
+// Policy: persistent workers with an equal-work fill.
+//   * The decode launch has one workgroup per worker: G = compute units x
+//     workgroups per CU, all resident at once. Each worker processes the list
+//     of work items the plan gives it, in order.
+//   * Work is measured in 32-token tiles. A work item (one query row, one
+//     contiguous token range) costs its tiles plus the kernel's item cost, the fixed cost of
+//     starting and finishing an item (query load, first-tile latency, output
+//     store).
+//   * Rows are taken longest first and poured into workers up to a capacity C:
+//     a row that does not fit is cut at the worker boundary and continues on
+//     the next worker. C is the smallest capacity (binary search) for which
+//     the fill needs at most G workers, so every worker gets about the same
+//     work and a row is split only where a worker boundary falls into it.
+//   * No piece is shorter than the item cost unless its row is (a worker may
+//     exceed C by that much rather than cut one off); a row is cut into at
+//     most max_splits pieces. A split row's pieces write
+//     partials (in the output precision) that one merge combines.
 #include <algorithm>
 #include <cstring>
 #include <vector>
@@ -41,10 +46,13 @@ bool select_variant(const mla_decode_params* p, Variant* v) {
     if (p->kv_dtype != MLA_DTYPE_BF16 && p->kv_dtype != MLA_DTYPE_FP8_E4M3FN) return false;
     if (p->out_dtype != MLA_DTYPE_BF16 && p->out_dtype != MLA_DTYPE_FP32) return false;
     switch (p->num_heads) {
-        case 128: *v = Variant{32, 4, 1, 512}; return true;
-        case 64: *v = Variant{16, 4, 1, 256}; return true;
-        case 32: *v = Variant{16, 2, 1, 128}; return true;
-        case 16: *v = Variant{16, 1, 2, 128}; return true;
+        // The 128-head kernel loads a 144 KiB query and stores a 128 KiB output
+        // per item, about as long as 8 tiles of its main loop; the smaller
+        // kernels' items cost about 4.
+        case 128: *v = Variant{32, 4, 1, 8}; return true;
+        case 64: *v = Variant{16, 4, 1, 4}; return true;
+        case 32: *v = Variant{16, 2, 1, 4}; return true;
+        case 16: *v = Variant{16, 1, 2, 4}; return true;
         default: return false;
     }
 }
@@ -72,11 +80,12 @@ const char* variant_name(const mla_decode_params* p) {
 // Partials are stored in the output's precision: bf16, or fp32 in the fp32 mode.
 static int64_t partial_elem_bytes(const mla_decode_params* p) { return p->out_dtype == MLA_DTYPE_FP32 ? 4 : 2; }
 
-static void layout(int32_t num_items, int32_t num_merges, int32_t num_partials, int32_t num_heads,
-                   int64_t elem_bytes, mla_plan_header* h) {
+static void layout(int32_t num_items, int32_t num_merges, int32_t num_workers, int32_t num_partials,
+                   int32_t num_heads, int64_t elem_bytes, mla_plan_header* h) {
     h->items_offset = align_up(sizeof(mla_plan_header), 64);
     h->merges_offset = align_up(h->items_offset + (int64_t)num_items * sizeof(mla_work_item), 64);
-    h->plan_bytes = align_up(h->merges_offset + (int64_t)num_merges * sizeof(mla_merge_item), 256);
+    h->workers_offset = align_up(h->merges_offset + (int64_t)num_merges * sizeof(mla_merge_item), 64);
+    h->plan_bytes = align_up(h->workers_offset + ((int64_t)num_workers + 1) * 4, 256);
     h->partial_out_offset = h->plan_bytes;
     h->partial_lse_offset =
         align_up(h->partial_out_offset + (int64_t)num_partials * num_heads * kLatent * elem_bytes, 256);
@@ -88,13 +97,13 @@ int32_t plan_bounds(const mla_decode_params* p, int32_t num_cus, int32_t batch, 
     Variant v;
     if (!p || batch < 0 || num_rows < 0 || num_cus <= 0) return MLA_ERR_INVALID_ARG;
     if (!select_variant(p, &v)) return MLA_ERR_UNSUPPORTED;
-    // Chunks: at most one per row plus ceil(T / chunk) <= G extra; split rows
-    // hold at most 2 * T / chunk <= 2G partials.
+    // Items: one per row plus at most one extra per worker boundary (G - 1);
+    // the pieces of split rows are at most 2 (G - 1).
     const int64_t G = (int64_t)num_cus * v.wgs_per_cu;
     const int64_t items = (int64_t)num_rows + G + 1;
     const int64_t partials = std::min<int64_t>(items, 2 * G + 2);
     mla_plan_header h{};
-    layout((int32_t)items, num_rows, (int32_t)partials, p->num_heads, partial_elem_bytes(p), &h);
+    layout((int32_t)items, num_rows, (int32_t)G, (int32_t)partials, p->num_heads, partial_elem_bytes(p), &h);
     if (plan_bytes) *plan_bytes = (size_t)h.plan_bytes;
     if (workspace_bytes) *workspace_bytes = (size_t)h.workspace_bytes;
     return MLA_OK;
@@ -131,43 +140,107 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
     }
     if (num_rows > INT32_MAX) return MLA_ERR_UNSUPPORTED;
 
-    const int64_t G = (int64_t)num_cus * v.wgs_per_cu;
-    int64_t chunk = std::max<int64_t>(v.min_chunk, (total + G - 1) / std::max<int64_t>(G, 1));
-    chunk = align_up(chunk, kTile);
+    const int64_t G = std::max<int64_t>(1, (int64_t)num_cus * v.wgs_per_cu);
     const int64_t max_splits = p->max_splits > 0 ? p->max_splits : kDefaultMaxSplits;
+    const int64_t item_cost = v.item_cost;
+    const int64_t min_piece = item_cost;  // a piece is at least as long as its fixed cost
 
-    std::vector<mla_work_item> items;
-    std::vector<mla_merge_item> merges;
-    items.reserve((size_t)(num_rows + G + 1));
-    int32_t num_partials = 0;
+    struct Row {
+        int32_t row, request;
+        int64_t len, tiles;
+    };
+    std::vector<Row> rows;
+    rows.reserve((size_t)num_rows);
     for (int32_t b = 0; b < batch; ++b) {
         const int64_t r0 = qo_indptr ? qo_indptr[b] : b;
         const int64_t r1 = qo_indptr ? qo_indptr[b + 1] : b + 1;
-        const int64_t L = len[b];
-        int64_t n = std::max<int64_t>(1, std::min<int64_t>(max_splits, (L + chunk - 1) / chunk));
-        const int64_t step = n > 1 ? align_up((L + n - 1) / n, kTile) : L;
-        if (n > 1) n = (L + step - 1) / step;  // tile alignment can drop a chunk
-        for (int64_t r = r0; r < r1; ++r) {
-            const int32_t first_partial = n > 1 ? num_partials : -1;
-            for (int64_t c = 0; c < n; ++c) {
-                mla_work_item it{};
-                it.row = (int32_t)r;
-                it.request = b;
-                it.page_base = kv_indptr[b];
-                it.kv_begin = (int32_t)(c * step);
-                it.kv_end = (int32_t)std::min<int64_t>(L, (c + 1) * step);
-                it.partial = n > 1 ? num_partials++ : -1;
-                it.head_begin = 0;
-                it.num_heads = p->num_heads;
-                items.push_back(it);
-            }
-            if (n > 1) merges.push_back(mla_merge_item{(int32_t)r, first_partial, (int32_t)n, 0});
-        }
+        for (int64_t r = r0; r < r1; ++r) rows.push_back(Row{(int32_t)r, b, len[b], (len[b] + kTile - 1) / kTile});
     }
-    // Longest chunks first (stable, so equal chunks keep row order).
-    std::stable_sort(items.begin(), items.end(), [](const mla_work_item& x, const mla_work_item& y) {
-        return (x.kv_end - x.kv_begin) > (y.kv_end - y.kv_begin);
-    });
+    std::stable_sort(rows.begin(), rows.end(), [](const Row& x, const Row& y) { return x.tiles > y.tiles; });
+
+    struct Piece {
+        int32_t row_index, worker;
+        int64_t t0, t1;  // tile range
+    };
+    // Pour the rows into workers of capacity C; false if more than G are needed.
+    auto fill = [&](int64_t C, std::vector<Piece>* out) {
+        if (out) out->clear();
+        int64_t w = 0, load = 0;
+        for (size_t i = 0; i < rows.size(); ++i) {
+            int64_t rem = rows[i].tiles, t = 0, pieces = 0;
+            for (;;) {  // at least one piece, also for an empty row
+                const bool last_allowed = pieces + 1 >= max_splits;  // this piece takes the rest
+                const int64_t cap = C - load - item_cost;
+                if (load > 0 && (cap < std::min(min_piece, rem) || (last_allowed && rem > cap))) {
+                    if (++w >= G) return false;
+                    load = 0;
+                    continue;
+                }
+                int64_t take = last_allowed ? rem : std::min(rem, std::max<int64_t>(cap, 1));
+                // Neither this piece nor the rest of the row shorter than min_piece,
+                // where the row allows it.
+                if (take < rem && rem - take < min_piece) take = rem >= 2 * min_piece ? rem - min_piece : rem;
+                if (take < rem && take < min_piece) take = std::min(rem, min_piece);
+                if (out) out->push_back(Piece{(int32_t)i, (int32_t)w, t, t + take});
+                t += take;
+                rem -= take;
+                load += take + item_cost;
+                ++pieces;
+                if (rem == 0) break;
+                if (++w >= G) return false;
+                load = 0;
+            }
+        }
+        return true;
+    };
+    int64_t hi = item_cost;
+    for (const Row& r : rows) hi += r.tiles + item_cost;
+    int64_t lo = 0;  // infeasible (no capacity)
+    while (hi - lo > 1) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (fill(mid, nullptr))
+            hi = mid;
+        else
+            lo = mid;
+    }
+    std::vector<Piece> pieces;
+    if (!fill(hi, &pieces)) return MLA_ERR_UNSUPPORTED;  // unreachable: hi is feasible
+
+    // Partial slots: the pieces of a split row take consecutive slots.
+    std::vector<int32_t> npieces(rows.size(), 0), first_slot(rows.size(), -1);
+    for (const Piece& pc : pieces) ++npieces[pc.row_index];
+    std::vector<mla_merge_item> merges;
+    int32_t num_partials = 0;
+    for (size_t i = 0; i < rows.size(); ++i)
+        if (npieces[i] > 1) {
+            first_slot[i] = num_partials;
+            merges.push_back(mla_merge_item{rows[i].row, num_partials, npieces[i], 0});
+            num_partials += npieces[i];
+        }
+    std::vector<int32_t> next_slot(first_slot);
+    std::vector<mla_work_item> items;
+    items.reserve(pieces.size());
+    int32_t num_workers = 0;
+    std::vector<int32_t> worker_begin;
+    for (const Piece& pc : pieces) {
+        const Row& r = rows[pc.row_index];
+        while (num_workers <= pc.worker) {
+            worker_begin.push_back((int32_t)items.size());
+            ++num_workers;
+        }
+        mla_work_item it{};
+        it.row = r.row;
+        it.request = r.request;
+        it.page_base = kv_indptr[r.request];
+        it.kv_begin = (int32_t)(pc.t0 * kTile);
+        it.kv_end = (int32_t)std::min<int64_t>(r.len, pc.t1 * kTile);
+        it.partial = npieces[pc.row_index] > 1 ? next_slot[pc.row_index]++ : -1;
+        it.head_begin = 0;
+        it.num_heads = p->num_heads;
+        items.push_back(it);
+    }
+    worker_begin.push_back((int32_t)items.size());
+    const int64_t chunk = hi * kTile;
 
     mla_plan_header h{};
     h.magic = MLA_PLAN_MAGIC;
@@ -181,9 +254,10 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
     h.num_items = (int32_t)items.size();
     h.num_merges = (int32_t)merges.size();
     h.num_partials = num_partials;
-    h.chunk_tokens = (int32_t)chunk;
+    h.chunk_tokens = (int32_t)std::min<int64_t>(chunk, INT32_MAX);
+    h.num_workers = num_workers;
     h.num_page_entries = kv_indptr[batch];
-    layout(h.num_items, h.num_merges, num_partials, p->num_heads, partial_elem_bytes(p), &h);
+    layout(h.num_items, h.num_merges, num_workers, num_partials, p->num_heads, partial_elem_bytes(p), &h);
     if ((size_t)h.plan_bytes > plan_h_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
     char* dst = static_cast<char*>(plan_h);
@@ -193,6 +267,7 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
         std::memcpy(dst + h.items_offset, items.data(), items.size() * sizeof(mla_work_item));
     if (!merges.empty())
         std::memcpy(dst + h.merges_offset, merges.data(), merges.size() * sizeof(mla_merge_item));
+    std::memcpy(dst + h.workers_offset, worker_begin.data(), worker_begin.size() * sizeof(int32_t));
     return MLA_OK;
 }
 

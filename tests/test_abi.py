@@ -3,6 +3,7 @@ arguments on the host with its documented status codes (no GPU work)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import numpy as np
 import pytest
@@ -10,8 +11,8 @@ import pytest
 import paged_mla_decode_amd as m
 from paged_mla_decode_amd import _binding as B
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
-                      "mla_decode.h")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
 FAKE = 1 << 40  # a non-null, 16-byte aligned stand-in address; never dereferenced
 
 
@@ -29,11 +30,25 @@ def test_library_exports_every_declared_symbol():
     assert sorted(B.EXPORTED_SYMBOLS) == names
 
 
-def test_struct_layouts_match_header():
-    assert ctypes.sizeof(B.mla_decode_params) == 32
-    assert ctypes.sizeof(B.mla_work_item) == 32
-    assert ctypes.sizeof(B.mla_merge_item) == 16
-    assert ctypes.sizeof(B.mla_plan_header) == 48 + 8 * 7
+def test_struct_layouts_match_header(tmp_path):
+    """The binding's ctypes structs have the C header's size and field offsets
+    (checked against the host compiler's view of include/mla_decode.h)."""
+    structs = [B.mla_decode_params, B.mla_plan_header, B.mla_work_item, B.mla_merge_item]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "mla_decode.h"', 'int main(void) {']
+    for st in structs:
+        lines.append(f'printf("{st.__name__} %zu\\n", sizeof({st.__name__}));')
+        for name, _ in st._fields_:
+            lines.append(f'printf("{st.__name__}.{name} %zu\\n", offsetof({st.__name__}, {name}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe)])
+    got = dict(l.split() for l in subprocess.check_output([str(exe)], text=True).splitlines())
+    for st in structs:
+        assert int(got[st.__name__]) == ctypes.sizeof(st), st.__name__
+        for name, _ in st._fields_:
+            assert int(got[f"{st.__name__}.{name}"]) == getattr(st, name).offset, (st.__name__, name)
 
 
 def test_status_strings():

@@ -10,6 +10,7 @@ import torch
 
 import oracle
 import workloads
+from paged_mla_decode_amd import _binding as binding
 from gpu_util import batch_to_device, compare, require_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -39,10 +40,11 @@ def run_full(batch, dev, out_dtype):
     dec = PagedMlaDecoder(batch.num_heads, batch.page_size, max_batch=batch.batch,
                           max_rows=batch.num_rows, kv_dtype=batch.cache_dtype, out_dtype=out_dtype,
                           device=dev)
-    h = dec.plan(batch.kv_indptr, batch.kv_last_page_len)
+    dec.plan(batch.kv_indptr, batch.kv_last_page_len)
+    plan = binding.read_plan(dec.plan_h)
     out, lse = dec.run(qn, qr, cache, idx, batch.sm_scale, batch.kv_scale)
     torch.cuda.synchronize()
-    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), h
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), plan
 
 
 @pytest.mark.parametrize("name,out_dtype,k", [
@@ -55,13 +57,15 @@ def test_config_sampled_rows(dev, name, out_dtype, k):
     batch = getattr(workloads, name)()
     say(f"config {name} out={out_dtype}: B={batch.batch} H={batch.num_heads} ps={batch.page_size} "
         f"tokens={int(batch.seq_lens.sum())}")
-    out, lse, h = run_full(batch, dev, out_dtype)
-    say(f"  plan: items={h.num_items} merges={h.num_merges} chunk={h.chunk_tokens}")
+    out, lse, (h, items, merges, workers) = run_full(batch, dev, out_dtype)
+    say(f"  plan: workers={h.num_workers} items={h.num_items} merges={h.num_merges} "
+        f"capacity={h.chunk_tokens} tokens")
     reqs = sampled_requests(batch, k, seed=11)
     sub = batch.subset(reqs)
     ref_out, ref_lse = oracle.decode_batch(sub)
     rows = np.concatenate([np.arange(batch.qo_indptr[b], batch.qo_indptr[b + 1]) for b in reqs])
-    split_rows = int(np.sum(batch.seq_lens[reqs] > h.chunk_tokens))
+    merged = {mi.row for mi in merges}
+    split_rows = sum(1 for r in rows if int(r) in merged)
     say(f"  sampled requests {reqs.tolist()} (lengths {batch.seq_lens[reqs].tolist()}, "
         f"{split_rows} split)")
     compare(out[rows], lse[rows], ref_out, ref_lse, out_dtype == "fp32", f"{name} sampled")

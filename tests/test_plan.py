@@ -1,9 +1,9 @@
 """Host planner invariants (no GPU): every (query row, token) is covered by
 exactly one work item, chunks stay inside their request and start on a tile
-boundary, split rows map to consistent partial slots and merges, and the
-items are ordered longest first. Several plans are correct; the kernel's
-result does not depend on which one is chosen, so the plan is pinned by these
-properties rather than by equality."""
+boundary, split rows map to consistent partial slots and merges, the worker
+table partitions the items, and the workers' loads are balanced. Several plans
+are correct; the kernel's result does not depend on which one is chosen, so
+the plan is pinned by these properties rather than by equality."""
 import numpy as np
 import pytest
 
@@ -22,7 +22,17 @@ def build(p, batch):
     return m.read_plan(plan)
 
 
-def check_invariants(p, batch, h, items, merges):
+def item_cost(num_heads):
+    """The planner's fixed cost per work item, in tiles (per kernel)."""
+    return 8 if num_heads == 128 else 4
+
+
+def worker_loads(items, workers, cost):
+    return [sum(-(-(it.kv_end - it.kv_begin) // TILE) + cost for it in items[workers[w]:workers[w + 1]])
+            for w in range(len(workers) - 1)]
+
+
+def check_invariants(p, batch, h, items, merges, workers):
     assert h.magic == m._binding.MLA_PLAN_MAGIC and h.num_items == len(items)
     assert h.num_rows == batch.num_rows and h.batch == batch.batch
     assert h.num_page_entries == batch.kv_indptr[-1]
@@ -58,10 +68,19 @@ def check_invariants(p, batch, h, items, merges):
         assert sorted((c.kv_begin, c.kv_end) for c in chunks) == sorted(covered[mi.row])
     for r, segs in covered.items():
         assert (len(segs) > 1) == (r in merged_rows)
-    # longest first
-    sizes = [it.kv_end - it.kv_begin for it in items]
-    assert sizes == sorted(sizes, reverse=True)
     assert h.num_merges == len(merges)
+    # the worker table partitions the items, at most one worker per resident workgroup
+    assert len(workers) == h.num_workers + 1 and workers[0] == 0 and workers[-1] == len(items)
+    assert all(a < b for a, b in zip(workers, workers[1:])), "every worker has an item"
+    assert h.num_workers <= max(1, p.num_cus) * 2
+    # no worker above the plan's capacity by more than a minimum piece, unless
+    # a single item (or an unsplittable row) forces it
+    cap = h.chunk_tokens // TILE
+    cost = item_cost(p.num_heads)
+    for w, load in enumerate(worker_loads(items, workers, cost)):
+        n = workers[w + 1] - workers[w]
+        if load > cap + cost:
+            assert n == 1 or p.max_splits > 0, (w, load, cap)
 
 
 @pytest.mark.parametrize("make,H,ps", [
@@ -74,8 +93,8 @@ def test_plan_invariants(make, H, ps):
     batch = make()
     for cus, splits in ((256, 0), (256, 1), (80, 3), (1, 0)):
         p = m.make_params(H, ps, num_cus=cus, max_splits=splits)
-        h, items, merges = build(p, batch)
-        check_invariants(p, batch, h, items, merges)
+        h, items, merges, workers = build(p, batch)
+        check_invariants(p, batch, h, items, merges, workers)
         if splits == 1:
             assert h.num_merges == 0 and h.num_partials == 0
 
@@ -83,20 +102,35 @@ def test_plan_invariants(make, H, ps):
 def test_skewed_batch_splits_the_long_request_across_the_chip():
     batch = workloads.skewed_fp8()
     p = m.make_params(128, 64, kv_dtype=m.MLA_DTYPE_FP8_E4M3FN, num_cus=256)
-    h, items, merges = build(p, batch)
-    check_invariants(p, batch, h, items, merges)
+    h, items, merges, workers = build(p, batch)
+    check_invariants(p, batch, h, items, merges, workers)
     long_row = int(np.argmax(batch.seq_lens))
     long_chunks = [it for it in items if it.row == long_row]
     assert len(long_chunks) >= 128
     # no chunk is much longer than the balanced share of the whole batch
     total = int(batch.seq_lens.sum())
-    assert max(it.kv_end - it.kv_begin for it in items) <= max(512, -(-total // 256)) + TILE
+    assert max(it.kv_end - it.kv_begin for it in items) <= max(512, -(-total // 256)) + 4 * TILE
+
+
+@pytest.mark.parametrize("name", ["v3", "v2_lite", "skewed_fp8"])
+def test_workers_are_balanced(name):
+    """The fill gives every worker nearly the same cost: the busiest is within
+    one item's fixed cost plus a few tiles of the mean."""
+    batch = getattr(workloads, name)()
+    kv = m.MLA_DTYPE_FP8_E4M3FN if batch.cache_dtype != "bf16" else m.MLA_DTYPE_BF16
+    p = m.make_params(batch.num_heads, batch.page_size, kv_dtype=kv, num_cus=256)
+    h, items, merges, workers = build(p, batch)
+    check_invariants(p, batch, h, items, merges, workers)
+    cost = item_cost(batch.num_heads)
+    loads = worker_loads(items, workers, cost)
+    mean = sum(loads) / len(loads)
+    assert max(loads) <= mean + cost + 8, (max(loads), mean)
 
 
 def test_empty_requests_get_an_empty_item():
     batch = workloads.random_decode_batch(3, [0, 5, 0], 16, 4)
     p = m.make_params(16, 4, num_cus=256)
-    h, items, merges = build(p, batch)
-    check_invariants(p, batch, h, items, merges)
+    h, items, merges, workers = build(p, batch)
+    check_invariants(p, batch, h, items, merges, workers)
     empty = [it for it in items if it.kv_begin == it.kv_end]
     assert sorted(it.row for it in empty) == [0, 2]
