@@ -185,7 +185,7 @@ int32_t mla_decode_plan(const mla_decode_params* params, int32_t batch, const in
  *              Request b then attends to min(kv_lens_d[b], planned length)
  *              tokens. This is how the tree-verify suffix uses the compacted
  *              table: its lengths come from mla_tree_suffix_compact.
- *   sm_scale   softmax scale applied to the raw scores.
+ *   sm_scale   softmax scale applied to the raw scores; finite and > 0.
  *   out_d      [N, H, 512] contiguous, out_dtype.
  *   lse_d      float [N, H] contiguous (natural log), or NULL.
  * The library never reads cache rows past a request's length, nor pool rows

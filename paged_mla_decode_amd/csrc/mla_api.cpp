@@ -114,7 +114,8 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
     if (q_nope_stride_n < 0 || q_nope_stride_h < 0 || q_rope_stride_n < 0 || q_rope_stride_h < 0 ||
         (q_nope_stride_n | q_nope_stride_h | q_rope_stride_n | q_rope_stride_h) % 8 != 0)
         return MLA_ERR_INVALID_ARG;
-    if (!std::isfinite(sm_scale) || !std::isfinite(kv_scale) || kv_scale <= 0.f) return MLA_ERR_INVALID_ARG;
+    if (!std::isfinite(sm_scale) || sm_scale <= 0.f || !std::isfinite(kv_scale) || kv_scale <= 0.f)
+        return MLA_ERR_INVALID_ARG;
     if (params->kv_dtype == MLA_DTYPE_BF16 && kv_scale != 1.f) return MLA_ERR_INVALID_ARG;
 
     const char* ws = static_cast<const char*>(workspace_d);

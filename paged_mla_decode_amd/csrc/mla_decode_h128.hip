@@ -34,6 +34,8 @@
 // whole rows (two heads x 512 bytes in fp32).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 #include "mla_tile_layout.h"
@@ -48,6 +50,23 @@ template <bool KV8, bool OUT32>
 struct H128Stages {
     static constexpr int value = KV8 ? 6 : (OUT32 ? 3 : 4);
 };
+
+// Wait states between the VALU accesses of the 16 output accumulators and the
+// inline-assembly MFMAs that accumulate into them (both directions; see
+// settle_v). One statement ties all 16, so no access can be scheduled across.
+template <int kNops>
+__device__ __forceinline__ void settle_o(f32x16 (&O)[4][4]) {
+    if constexpr (kNops == 3)
+        asm volatile("s_nop 2"
+                     : "+a"(O[0][0]), "+a"(O[0][1]), "+a"(O[0][2]), "+a"(O[0][3]), "+a"(O[1][0]), "+a"(O[1][1]),
+                       "+a"(O[1][2]), "+a"(O[1][3]), "+a"(O[2][0]), "+a"(O[2][1]), "+a"(O[2][2]), "+a"(O[2][3]),
+                       "+a"(O[3][0]), "+a"(O[3][1]), "+a"(O[3][2]), "+a"(O[3][3]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(O[0][0]), "+a"(O[0][1]), "+a"(O[0][2]), "+a"(O[0][3]), "+a"(O[1][0]), "+a"(O[1][1]),
+                       "+a"(O[1][2]), "+a"(O[1][3]), "+a"(O[2][0]), "+a"(O[2][1]), "+a"(O[2][2]), "+a"(O[2][3]),
+                       "+a"(O[3][0]), "+a"(O[3][1]), "+a"(O[3][2]), "+a"(O[3][3]));
+}
 
 template <bool KV8, bool OUT32>
 __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
@@ -159,6 +178,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
             for (int i = 0; i < kDW; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) O[i][j] = f32x16{};
+            settle_o<3>(O);
             l_part = 0.f;
 
             if (ntiles > 0) {
@@ -189,7 +209,6 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                 // adds exact zeros; at j = ntiles every score is masked (no valid
                 // token) and the probabilities it writes are never read.
                 auto iteration = [&](int j, int cur) {
-                    constexpr bool kScore = true, kPv = true;
                     const int prv = cur == 0 ? kStages - 1 : cur - 1;
                     // Tile j has landed; every wave is past iteration j-1, so P(j-1)
                     // is visible and the slot of tile j-2 is free.
@@ -200,50 +219,147 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                     if (j + kIdxAhead < ntiles) issue_idx(j + kIdxAhead, wrap(cur + kIdxAhead % kStages));
                     if (j + kAhead < ntiles) issue_tile(j + kAhead, wrap(cur + kAhead));
 
-                    // ---- score of tile j: one accumulator chain ----
-                    f32x16 S = {};
-                    if (kScore) {
-                        const LDS_AS char* T = (const LDS_AS char*)smem + cur * L::kTileBytes;
-                        // fp8 codes are widened to bf16 at the MFMA, not at the read, so
-                        // that only the raw codes of the reads in flight occupy registers.
-                        auto load = [&](int s) {
-                            const int off = sbase[L::score_base_index(s)] + L::score_delta(s);
-                            if constexpr (KV8)
-                                return *(const LDS_AS u32x4*)(T + off);
-                            else
-                                return *(const LDS_AS bf16x8*)(T + off);
-                        };
-                        pipelined<L::kScoreReads, kPipe, 1, KV8 ? 2 : 1>(load, [&](int s, auto raw) {
-                            if constexpr (KV8) {
-                                S = mfma32(fp8x8_to_bf16(raw[0], raw[1]), q[2 * s], S);
-                                S = mfma32(fp8x8_to_bf16(raw[2], raw[3]), q[2 * s + 1], S);
-                            } else {
-                                S = mfma32(raw, q[s], S);
-                            }
-                        });
-                    }
+                    const LDS_AS char* Ts = (const LDS_AS char*)smem + cur * L::kTileBytes;
+                    const LDS_AS char* Tp = (const LDS_AS char*)smem + prv * L::kTileBytes;
+                    const LDS_AS char* Pb = (const LDS_AS char*)pbuf;
 
-                    // ---- P . latent of tile j-1, with the softmax of tile j in its shadow ----
-                    bf16x8 P[2], Plo[2];
-                    auto softmax = [&] {
-                        const int nvalid = min(kTile, kv_end - (kv_begin + j * kTile));
-                        float sv[16];
-                        float tmax = -INFINITY;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int tok = 16 * (r >> 3) + 8 * gq + (r & 7);
-                            sv[r] = tok < nvalid ? S[r] * a.scale_log2 : -INFINITY;
-                            tmax = fmaxf(tmax, sv[r]);
+                    // Score operand s (one or two k-slices): raw tile bytes; fp8 codes
+                    // are widened to bf16 next to their MFMA.
+                    using SOp = std::conditional_t<KV8, u32x4, bf16x8>;
+                    auto sload = [&](int s) {
+                        return *(const LDS_AS SOp*)(Ts + sbase[L::score_base_index(s)] + L::score_delta(s));
+                    };
+                    // Product A operand of step a = 4 kk + md (transposed reads).
+                    using AOp = std::conditional_t<KV8, i32x2, i16x4[2]>;
+                    struct ARaw { AOp v; };
+                    auto aload = [&](int a) {
+                        const int kk = a >> 2, md = a & 3;
+                        ARaw r;
+                        if constexpr (KV8) {
+                            r.v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                (LDS_AS i32x2*)(Tp + pbase[0] + L::pv_delta(md, kk)));
+                        } else {
+                            r.v[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (LDS_AS i16x4*)(Tp + pbase[0] + L::pv_delta(md, kk)));
+                            r.v[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (LDS_AS i16x4*)(Tp + pbase[1] + L::pv_delta(md, kk)));
                         }
-                        tmax = max_xor32(tmax);
-                        if (j == 0 && pass == 0) m_ref = tmax;
-                        m_true = fmaxf(m_true, tmax);
-                        float ls0 = 0.f, ls1 = 0.f;
+                        return r;
+                    };
+                    auto awiden = [&](const ARaw& r) {
+                        if constexpr (KV8)
+                            return fp8x8_to_bf16((unsigned)r.v[0], (unsigned)r.v[1]);
+                        else
+                            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r.v[0], r.v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                    };
+                    // P(j-1) of token half kk, head block hb (B operands; lo parts for fp32 output).
+                    auto pload = [&](int kk, int hb, int lo) {
+                        return *(const LDS_AS bf16x8*)(Pb + lo * PBuf::kBytes + p_rd + hb * 32 * PBuf::kRow + 32 * kk);
+                    };
+
+                    // ---- schedule ----
+                    // 36 score MFMAs (one accumulator chain, in VGPRs) and kPM product
+                    // MFMAs (independent accumulators). The first kMix product MFMAs
+                    // are spread evenly between the score MFMAs, so the score's LDS
+                    // reads (each wave reads the whole tile) proceed under product
+                    // MFMAs; the last kTail products carry the softmax of tile j.
+                    constexpr int kSM = 36;
+                    constexpr int kPM = OUT32 ? 64 : 32;
+                    constexpr int kTail = OUT32 ? 16 : 8;
+                    constexpr int kMix = kPM - kTail;
+                    constexpr int kSR = L::kScoreReads;  // 36 | 18 reads
+                    constexpr int kMPR = kSM / kSR;      // MFMAs per score read
+                    constexpr int kPPS = OUT32 ? 8 : 4;  // product MFMAs per A step
+
+                    SOp sb[kPipe];
 #pragma unroll
-                        for (int kk = 0; kk < 2; ++kk)
+                    for (int i = 0; i < kPipe; ++i) sb[i] = sload(i);
+                    ARaw ab[2] = {aload(0), aload(1)};
+                    bf16x8 Bp[4], Bl[4];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const float pv = fast_exp2(sv[8 * kk + e] - m_ref);
+                    for (int hb = 0; hb < 4; ++hb) {
+                        Bp[hb] = pload(0, hb, 0);
+                        if (OUT32) Bl[hb] = pload(0, hb, 1);
+                    }
+                    f32x16 S;
+                    bf16x8 Acur;
+
+                    auto score_mfma = [&](int si) {
+                        const int s = si / kMPR, h = si % kMPR;
+                        bf16x8 A;
+                        if constexpr (KV8) A = fp8x8_to_bf16(sb[s % kPipe][2 * h], sb[s % kPipe][2 * h + 1]);
+                        else A = sb[s % kPipe];
+                        if (si == 0) mfma32_first_v(S, A, q[si]);
+                        else mfma32_acc_v(S, A, q[si]);
+                        if (h == kMPR - 1 && s + kPipe < kSR) sb[s % kPipe] = sload(s + kPipe);
+                    };
+                    auto product_mfma = [&](int pi) {
+                        const int a = pi / kPPS, hb = (pi % kPPS) / (OUT32 ? 2 : 1), lo = OUT32 ? pi % 2 : 0;
+                        const int kk = a >> 2, md = a & 3;
+                        if (pi % kPPS == 0) {
+                            Acur = awiden(ab[a & 1]);
+                            if (a + 2 < 8) ab[a & 1] = aload(a + 2);
+                        }
+                        const bf16x8 B = lo ? Bl[hb] : Bp[hb];
+                        mfma32_acc_a(O[md][hb], Acur, B);
+                        // P of token half 1 replaces each operand after its last use in
+                        // half 0.
+                        if (kk == 0 && md == 3 && lo == (OUT32 ? 1 : 0)) {
+                            Bp[hb] = pload(1, hb, 0);
+                            if (OUT32) Bl[hb] = pload(1, hb, 1);
+                        }
+                    };
+
+                    int si = 0, pi = 0;
+#pragma unroll
+                    for (int g = 0; g < kSM + kMix; ++g) {
+                        // Bresenham spread: slot g is a score MFMA when it advances the
+                        // score's share of the slots.
+                        if ((g + 1) * kSM / (kSM + kMix) != g * kSM / (kSM + kMix)) score_mfma(si++);
+                        else product_mfma(pi++);
+                    }
+                    settle_v(S);
+
+                    // ---- softmax of tile j, in eight pieces between the last products ----
+                    // Raw scores; the scale (positive) enters through one fma in the
+                    // exponent, and the maximum of the raw scores scales to the maximum
+                    // of the scaled ones. Only a tile with fewer than 32 valid tokens
+                    // (the last one, and the phantom iteration) masks: value r is token
+                    // 16 (r / 8) + 8 gq + r % 8.
+                    const int nvalid = min(kTile, kv_end - (kv_begin + j * kTile));
+                    float tmax = 0.f, ls0 = 0.f, ls1 = 0.f;
+                    bf16x8 P[2], Plo[2];
+                    // Each piece ends in an empty volatile statement that takes its
+                    // results: volatile statements keep program order with the
+                    // product MFMAs, so the piece is computed before the next one.
+                    auto soft = [&](int piece) {
+                        if (piece == 0) {
+                            if (nvalid < kTile) {
+                                const int lim = nvalid - 8 * gq;
+#pragma unroll
+                                for (int r = 0; r < 16; ++r)
+                                    if (16 * (r >> 3) + (r & 7) >= lim) S[r] = -INFINITY;
+                            }
+                            asm volatile("" : "+v"(S));
+                        } else if (piece == 1) {
+                            tmax = fmaxf(S[0], S[1]);
+#pragma unroll
+                            for (int r = 2; r < 8; ++r) tmax = fmaxf(tmax, S[r]);
+                            asm volatile("" : "+v"(tmax));
+                        } else if (piece == 2) {
+#pragma unroll
+                            for (int r = 8; r < 16; ++r) tmax = fmaxf(tmax, S[r]);
+                            asm volatile("" : "+v"(tmax));
+                        } else if (piece == 3) {
+                            tmax = max_xor32(tmax) * a.scale_log2;
+                            if (j == 0 && pass == 0) m_ref = tmax;
+                            m_true = fmaxf(m_true, tmax);
+                            asm volatile("" : "+v"(m_ref), "+v"(m_true));
+                        } else {
+                            const int kk = (piece - 4) >> 1, e0 = 4 * ((piece - 4) & 1);
+#pragma unroll
+                            for (int e = e0; e < e0 + 4; ++e) {
+                                const float pv = fast_exp2(fmaf(S[8 * kk + e], a.scale_log2, -m_ref));
                                 if (e & 1)
                                     ls1 += pv;
                                 else
@@ -251,80 +367,27 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                                 P[kk][e] = (__bf16)pv;
                                 if (OUT32) Plo[kk][e] = (__bf16)(pv - (float)P[kk][e]);
                             }
-                        l_part += ls0 + ls1;
+                            asm volatile("" : "+v"(ls0), "+v"(ls1));
+                            if ((piece & 1) == 1) {
+                                asm volatile("" : "+v"(P[kk]));
+                                if (OUT32) asm volatile("" : "+v"(Plo[kk]));
+                            }
+                        }
                     };
-                    if (kPv) {
-                        const LDS_AS char* T = (const LDS_AS char*)smem + prv * L::kTileBytes;
-                        // step = 4 kk + md: one A operand (transposed read), four MFMAs (head blocks)
-                        auto load_pv = [&](int step) {
-                            const int kk = step >> 2, md = step & 3;
-                            if constexpr (KV8) {
-                                return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                                    (LDS_AS i32x2*)(T + pbase[0] + L::pv_delta(md, kk)));
-                            } else {
-                                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                    (LDS_AS i16x4*)(T + pbase[0] + L::pv_delta(md, kk)));
-                                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                    (LDS_AS i16x4*)(T + pbase[1] + L::pv_delta(md, kk)));
-                                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                            }
-                        };
-                        // P(j-1) of token half kk for the four head blocks (B operands).
-                        bf16x8 Bp[4], Bl[4];
-                        auto load_p = [&](int kk) {
 #pragma unroll
-                            for (int hb = 0; hb < 4; ++hb) {
-                                const int off = p_rd + hb * 32 * PBuf::kRow + 32 * kk;
-                                Bp[hb] = *(const LDS_AS bf16x8*)((const LDS_AS char*)pbuf + off);
-                                if (OUT32) Bl[hb] = *(const LDS_AS bf16x8*)((const LDS_AS char*)pbuf + PBuf::kBytes + off);
-                            }
-                        };
-                        using Op = decltype(load_pv(0));
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) {
-                            load_p(kk);
-                            Op buf[2] = {load_pv(4 * kk), load_pv(4 * kk + 1)};
-                            if (kScore && kk == 0) softmax();
-#pragma unroll
-                            for (int md = 0; md < 4; ++md) {
-                                const Op raw = buf[md & 1];
-                                bf16x8 A;
-                                if constexpr (KV8)
-                                    A = fp8x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]);
-                                else
-                                    A = raw;
-                                if (md + 2 < 4) buf[md & 1] = load_pv(4 * kk + md + 2);
-#pragma unroll
-                                for (int hb = 0; hb < 4; ++hb) {
-                                    O[md][hb] = mfma32(A, Bp[hb], O[md][hb]);
-                                    if (OUT32) O[md][hb] = mfma32(A, Bl[hb], O[md][hb]);
-                                }
-                            }
-                            // Interleave: the softmax VALU work between the MFMAs, the
-                            // transposed reads two steps ahead.
-                            constexpr int kPReads = OUT32 ? 8 : 4, kARead = KV8 ? 1 : 2;
-                            __builtin_amdgcn_sched_group_barrier(0x100, kPReads + 2 * kARead, 0);
-#pragma unroll
-                            for (int md = 0; md < 4; ++md) {
-#pragma unroll
-                                for (int m = 0; m < (OUT32 ? 8 : 4); ++m) {
-                                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                                }
-                                if (md + 2 < 4) __builtin_amdgcn_sched_group_barrier(0x100, kARead, 0);
-                            }
-                        }
-                    } else if (kScore) {
-                        softmax();
+                    for (int t = 0; t < kTail; ++t) {
+                        product_mfma(pi++);
+                        if (t % (kTail / 8) == kTail / 8 - 1) soft(t / (kTail / 8));
+                        __builtin_amdgcn_sched_barrier(0);
                     }
+                    l_part += ls0 + ls1;
+
                     // Every wave is done reading P(j-1): the buffer takes P(j).
-                    if (kScore && kPv) lds_barrier();
-                    if (kScore) {
+                    lds_barrier();
 #pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) {
-                            *(LDS_AS bf16x8*)((LDS_AS char*)pbuf + p_wr + 32 * kk) = P[kk];
-                            if (OUT32) *(LDS_AS bf16x8*)((LDS_AS char*)pbuf + PBuf::kBytes + p_wr + 32 * kk) = Plo[kk];
-                        }
+                    for (int kk = 0; kk < 2; ++kk) {
+                        *(LDS_AS bf16x8*)((LDS_AS char*)pbuf + p_wr + 32 * kk) = P[kk];
+                        if (OUT32) *(LDS_AS bf16x8*)((LDS_AS char*)pbuf + PBuf::kBytes + p_wr + 32 * kk) = Plo[kk];
                     }
                 };
                 int cur = 0;
@@ -332,6 +395,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                     iteration(j, cur);
                     cur = wrap(cur + 1);
                 }
+                settle_o<24>(O);
             }
             // Did any head outgrow its reference? All waves must agree (the tiles are
             // loaded cooperatively), so the flag goes through LDS.

@@ -176,6 +176,34 @@ __device__ __forceinline__ void pipelined(Load load, Use use) {
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// 32x32x16 bf16 products issued as inline assembly. Volatile assembly keeps
+// program order against other volatile assembly and against memory accesses,
+// so a loop body can lay out its own interleave of independent MFMA chains and
+// LDS reads. The compiler does not know these are matrix-core instructions and
+// inserts none of their wait states, so:
+//   * each starts with two wait states (an operand written by a VALU
+//     instruction right before it is ready: the gfx950 VALU -> MFMA source
+//     requirement);
+//   * back-to-back products accumulating into the same registers need none;
+//   * readers (and VALU writers) of a result wait through settle(), at least
+//     19 wait states after the last product that wrote it (an 8-pass XDL
+//     write followed by a VALU access needs 11).
+__device__ __forceinline__ void mfma32_first_v(f32x16& c, bf16x8 a, bf16x8 b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_acc_v(f32x16& c, bf16x8 a, bf16x8 b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_acc_a(f32x16& c, bf16x8 a, bf16x8 b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void settle_v(f32x16& c) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
+}
+__device__ __forceinline__ void settle_a(f32x16& c) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(c));
+}
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

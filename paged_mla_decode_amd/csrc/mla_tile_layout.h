@@ -174,7 +174,14 @@ struct H128Layout {
     static constexpr int kTileBytes = G::kTileBytes;
     static constexpr int kTPL = 256 / (kCG * 16);  // tokens per 256-byte line: 2 | 4
 
-    static MLA_HD constexpr int swz(int t) { return (t / kTPL) % kCG; }
+    // Chunk swizzle of 256-byte line L = (t / kTPL) % kCG: a bijection (16
+    // tokens of a score read reach 16 distinct 16-byte bank groups) that sends
+    // lines 2m and 2m+1 to opposite halves of the chunk range (the 4 tokens of
+    // a transposed P . latent read, two lines, reach distinct banks).
+    static MLA_HD constexpr int swz(int t) {
+        const int l = (t / kTPL) % kCG;
+        return (l & 1) * (kCG / 2) + (l >> 1);
+    }
     static MLA_HD constexpr int chunk_offset(int t, int j) {
         return ((j / kCG) * kNTB + t / kTPB) * 1024 + ((t % kTPB) * kCG + ((j % kCG) ^ swz(t))) * 16;
     }

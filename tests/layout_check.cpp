@@ -138,6 +138,16 @@ void check_h128() {
                 }
             }
     CHECK(cols.size() == 512, "h128 columns cover the latent: %zu", cols.size());
+    // transposed reads: the 8-byte pieces of each 32-lane pass fill the 64 banks
+    for (int blk = 0; blk < 16; ++blk)
+        for (int kk = 0; kk < 2; ++kk)
+            for (int hi = 0; hi < L::kPvBases; ++hi)
+                for (int p = 0; p < 2; ++p) {
+                    std::set<int> pairs;
+                    for (int lane = 32 * p; lane < 32 * p + 32; ++lane) pairs.insert((L::pv_ref(lane, blk, kk, hi) / 8) % 32);
+                    CHECK(pairs.size() == 32, "h128 pv bank conflict kv8=%d blk=%d kk=%d hi=%d pass=%d (%zu)", KV8, blk, kk,
+                          hi, p, pairs.size());
+                }
 }
 
 void check_out_stage() {

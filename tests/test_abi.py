@@ -143,6 +143,8 @@ def test_decode_validates_before_launch():
     assert call(out_d=FAKE + 8) == m.MLA_ERR_INVALID_ARG  # misaligned
     assert call(q_nope_stride_h=500) == m.MLA_ERR_INVALID_ARG
     assert call(sm_scale=float("nan")) == m.MLA_ERR_INVALID_ARG
+    assert call(sm_scale=0.0) == m.MLA_ERR_INVALID_ARG
+    assert call(sm_scale=-0.1) == m.MLA_ERR_INVALID_ARG
     assert call(kv_scale=2.0) == m.MLA_ERR_INVALID_ARG  # bf16 cache takes no scale
     assert call(workspace_bytes=ws - 1) == m.MLA_ERR_WORKSPACE_TOO_SMALL
     other = m.make_params(32, 1, num_cus=256)
