@@ -84,6 +84,10 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
     static_assert(kStages >= 3, "tiles j-1 and j are in use while j+1 loads");
     static_assert(kAhead * (kLoadsMax + 1) < 64, "vmcnt budget");
     static_assert(OutStage::kBytes <= kStages * L::kTileBytes, "output staging reuses the tile ring");
+    // bf16 output: one staging round if the tile ring holds all 512 columns.
+    constexpr int kOutRounds = OutStageBf16<1>::kBytes <= kStages * L::kTileBytes ? 1 : 2;
+    using OS = OutStageBf16<kOutRounds>;
+    static_assert(OUT32 || OS::kBytes <= kStages * L::kTileBytes, "bf16 output staging reuses the tile ring");
     __shared__ __attribute__((aligned(1024))) char smem[kStages * L::kTileBytes];
     __shared__ __attribute__((aligned(16))) char pbuf[(OUT32 ? 2 : 1) * PBuf::kBytes];
     __shared__ __attribute__((aligned(16))) int idx_ring[kStages][HS][64];
@@ -431,35 +435,62 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         // Output rows of this item: [partial or row][head_begin + h][512].
         const int64_t row0 = (it.partial >= 0 ? (int64_t)it.partial * nh : (int64_t)it.row * nh) + it.head_begin;
         LDS_AS char* stage = (LDS_AS char*)smem;  // every wave is past its last tile read
+        // Partials are stored in the output's precision.
+        void* const obase = it.partial >= 0 ? a.part_out : a.out;
+        if constexpr (!OUT32) {
+            // bf16: [128 heads][512] in one round (two where the tile ring is
+            // smaller), then every store instruction writes whole head rows with
+            // 16 bytes per lane.
 #pragma unroll
-        for (int md = 0; md < kDW; ++md) {
+            for (int rd = 0; rd < kOutRounds; ++rd) {
 #pragma unroll
-            for (int hb = 0; hb < 4; ++hb)
+                for (int md = rd * kDW / kOutRounds; md < (rd + 1) * kDW / kOutRounds; ++md)
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const f32x4 v = {O[md][hb][4 * r4] * inv[hb], O[md][hb][4 * r4 + 1] * inv[hb],
-                                     O[md][hb][4 * r4 + 2] * inv[hb], O[md][hb][4 * r4 + 3] * inv[hb]};
-                    const int col = L::column(w, md, gq, 4 * r4) - 128 * md;
-                    *(LDS_AS f32x4*)(stage + OutStage::offset(32 * hb + hq, col)) = v;
+                    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const bf16x4 v = {(__bf16)(O[md][hb][4 * r4] * inv[hb]), (__bf16)(O[md][hb][4 * r4 + 1] * inv[hb]),
+                                              (__bf16)(O[md][hb][4 * r4 + 2] * inv[hb]), (__bf16)(O[md][hb][4 * r4 + 3] * inv[hb])};
+                            const int col = L::column(w, md, gq, 4 * r4) - rd * OS::kCols;
+                            *(LDS_AS bf16x4*)(stage + OS::offset(32 * hb + hq, col)) = v;
+                        }
+                lds_barrier();
+                // 128 heads x kCols / 8 units of 8 columns, consecutive lanes on
+                // consecutive units.
+                constexpr int kUnits = OS::kCols / 8;
+#pragma unroll
+                for (int jj = 0; jj < 128 * kUnits / 256; ++jj) {
+                    const int u = tid + 256 * jj;
+                    const int h = u / kUnits, c8 = u % kUnits;
+                    const bf16x8 v = *(const LDS_AS bf16x8*)(stage + OS::offset(h, 8 * c8));
+                    *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(obase) + (row0 + h) * kLatent + rd * OS::kCols + 8 * c8) = v;
                 }
-            lds_barrier();
-            // 128 heads x 32 units of 4 columns; consecutive lanes take consecutive units.
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int u = tid + 256 * j;
-                const int h = u >> 5, c4 = u & 31;
-                const f32x4 v = *(const LDS_AS f32x4*)(stage + OutStage::offset(h, 4 * c4));
-                const int64_t o = (row0 + h) * kLatent + 128 * md + 4 * c4;
-                // Partials are stored in the output's precision.
-                void* base = it.partial >= 0 ? a.part_out : a.out;
-                if constexpr (OUT32) {
-                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + o) = v;
-                } else {
-                    const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-                    *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(base) + o) = b;
-                }
+                lds_barrier();
             }
-            lds_barrier();
+        } else {
+#pragma unroll
+            for (int md = 0; md < kDW; ++md) {
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const f32x4 v = {O[md][hb][4 * r4] * inv[hb], O[md][hb][4 * r4 + 1] * inv[hb],
+                                         O[md][hb][4 * r4 + 2] * inv[hb], O[md][hb][4 * r4 + 3] * inv[hb]};
+                        const int col = L::column(w, md, gq, 4 * r4) - 128 * md;
+                        *(LDS_AS f32x4*)(stage + OutStage::offset(32 * hb + hq, col)) = v;
+                    }
+                lds_barrier();
+                // 128 heads x 32 units of 4 columns; consecutive lanes take consecutive units.
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int u = tid + 256 * j;
+                    const int h = u >> 5, c4 = u & 31;
+                    const f32x4 v = *(const LDS_AS f32x4*)(stage + OutStage::offset(h, 4 * c4));
+                    const int64_t o = (row0 + h) * kLatent + 128 * md + 4 * c4;
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(obase) + o) = v;
+                }
+                lds_barrier();
+            }
         }
     }
 }

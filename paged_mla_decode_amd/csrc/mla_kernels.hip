@@ -408,26 +408,49 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(const MergePartials
     const mla_merge_item mi = a.merges[blockIdx.x];
     const int lane = threadIdx.x & 63;
     const int nh = a.num_heads;
+    // Up to kBatch partials are loaded before any is combined (the loads of a
+    // batch are in flight together); a later batch rescales what came before
+    // when its maximum is larger (the pairwise LSE combination).
+    constexpr int kBatch = 8;
+    using V = std::conditional_t<OUT32, f32x8, bf16x8>;
     for (int h = blockIdx.y * 4 + (threadIdx.x >> 6); h < nh; h += gridDim.y * 4) {
-        float m = -INFINITY;
-        for (int p = 0; p < mi.num_partials; ++p)
-            m = fmaxf(m, a.part_lse[(int64_t)(mi.partial_begin + p) * nh + h]);
+        float m = -INFINITY, wsum = 0.f;
         f32x8 acc = {};
-        float wsum = 0.f;
-        if (m != -INFINITY) {
-            for (int p = 0; p < mi.num_partials; ++p) {
-                const int64_t slot = (int64_t)(mi.partial_begin + p) * nh + h;
-                const float wp = fast_exp2((a.part_lse[slot] - m) * kLog2e);
-                wsum += wp;
-                f32x8 v;
-                if constexpr (OUT32) {
-                    v = *reinterpret_cast<const f32x8*>(reinterpret_cast<const float*>(a.part_out) + slot * kLatent + 8 * lane);
-                } else {
-                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.part_out) + slot * kLatent + 8 * lane);
+        for (int p0 = 0; p0 < mi.num_partials; p0 += kBatch) {
+            const int nb = min(kBatch, mi.num_partials - p0);
+            float l[kBatch];
+            V v[kBatch];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = (float)b[e];
+            for (int k = 0; k < kBatch; ++k) {
+                if (k < nb) {
+                    const int64_t slot = (int64_t)(mi.partial_begin + p0 + k) * nh + h;
+                    l[k] = a.part_lse[slot];
+                    v[k] = *(reinterpret_cast<const V*>(a.part_out) + slot * (kLatent / 8) + lane);
                 }
-                acc += wp * v;
+            }
+            float mb = m;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                if (k < nb) mb = fmaxf(mb, l[k]);
+            if (mb == -INFINITY) continue;  // every partial so far is empty
+            const float r = m == -INFINITY ? 0.f : fast_exp2((m - mb) * kLog2e);
+            acc = acc * r;
+            wsum *= r;
+            m = mb;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                if (k < nb) {
+                    const float wp = fast_exp2((l[k] - m) * kLog2e);
+                    wsum += wp;
+                    f32x8 x;
+                    if constexpr (OUT32) {
+                        x = v[k];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) x[e] = (float)v[k][e];
+                    }
+                    acc += wp * x;
+                }
             }
         }
         const bool empty = !(wsum > 0.f);
@@ -436,10 +459,10 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(const MergePartials
         if constexpr (OUT32) {
             *reinterpret_cast<f32x8*>(reinterpret_cast<float*>(a.out) + orow * kLatent + 8 * lane) = acc * inv;
         } else {
-            bf16x8 v;
+            bf16x8 o;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (__bf16)(acc[e] * inv);
-            *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(a.out) + orow * kLatent + 8 * lane) = v;
+            for (int e = 0; e < 8; ++e) o[e] = (__bf16)(acc[e] * inv);
+            *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(a.out) + orow * kLatent + 8 * lane) = o;
         }
         if (a.lse && lane == 0) a.lse[orow] = empty ? -INFINITY : m + __logf(wsum);
     }

@@ -235,6 +235,17 @@ struct OutStage {
     static MLA_HD int offset(int h, int col) { return h * kRow + 4 * col; }
 };
 
+// bf16 output staging of the H=128 kernel: [128 heads][512 / kRounds
+// columns] per round, rows padded by 16 bytes (16-byte aligned; the 8-byte
+// writes of the 32 heads of one write pass meet at most two to a bank group).
+template <int kRounds>
+struct OutStageBf16 {
+    static constexpr int kCols = 512 / kRounds;
+    static constexpr int kRow = 2 * kCols + 16;
+    static constexpr int kBytes = 128 * kRow;
+    static MLA_HD int offset(int h, int col) { return h * kRow + 2 * col; }
+};
+
 // Probabilities shared between the waves of the H=128 kernel: bf16
 // [128 heads][32 tokens], rows padded to 80 bytes so that the 16-byte accesses
 // of 16 consecutive heads fall on distinct LDS banks.

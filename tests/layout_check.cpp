@@ -165,6 +165,25 @@ void check_out_stage() {
     CHECK(banks.size() == 16, "out stage bank spread %zu", banks.size());
 }
 
+template <int R>
+void check_out_stage_bf16() {
+    using S = OutStageBf16<R>;
+    // store pass: 16-byte units of 8 columns, row-major, every unit once
+    std::set<int> offs;
+    for (int h = 0; h < 128; ++h)
+        for (int c = 0; c < S::kCols; c += 8) {
+            const int o = S::offset(h, c);
+            CHECK(o % 16 == 0 && o + 16 <= S::kBytes, "bf16 out stage offset R=%d", R);
+            CHECK(offs.insert(o).second, "bf16 out stage overlap R=%d", R);
+        }
+    // write pass: 32 heads at one column, 8 bytes each, at most two per 8-byte bank pair
+    for (int c = 0; c < S::kCols; c += 4) {
+        int count[32] = {};
+        for (int h = 0; h < 32; ++h) ++count[(S::offset(h, c) / 8) % 32];
+        for (int b = 0; b < 32; ++b) CHECK(count[b] <= 2, "bf16 out stage write conflicts R=%d col=%d", R, c);
+    }
+}
+
 void check_pbuf() {
     std::set<int> offs;
     for (int h = 0; h < 128; ++h)
@@ -195,6 +214,8 @@ int main() {
     check_h128<true>();
     check_pbuf();
     check_out_stage();
+    check_out_stage_bf16<1>();
+    check_out_stage_bf16<2>();
     if (failures) {
         std::printf("FAILED: %d\n", failures);
         return 1;
