@@ -146,8 +146,29 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
             for (int t = 0; t < kAhead; ++t)
                 if (t < ntiles) issue_idx(t, t);
         };
-        // Page indices of the first tiles ride along with the query loads.
+        // The first tiles: the product at j = 0 reads slot kStages-1 (first
+        // loaded at j = 1) and the probability buffer, both zeroed; then the data
+        // of tiles 0 .. kAhead-1, each preceded by the page indices of the tile
+        // kAhead later (as iteration t - kAhead would).
+        auto start_tiles = [&] {
+            {
+                using V4 = __attribute__((__vector_size__(4 * sizeof(int)))) int;
+                LDS_AS V4* z = (LDS_AS V4*)(smem + (kStages - 1) * L::kTileBytes);
+                for (int k = tid; k < L::kTileBytes / 16; k += 256) z[k] = V4{0, 0, 0, 0};
+                LDS_AS V4* zp = (LDS_AS V4*)pbuf;
+                for (int k = tid; k < (OUT32 ? 2 : 1) * PBuf::kBytes / 16; k += 256) zp[k] = V4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int t = 0; t < kAhead; ++t) {
+                if (t + kAhead < ntiles) issue_idx(t + kAhead, wrap(t + kAhead));
+                if (t < ntiles) issue_tile(t, t);
+            }
+        };
+        // Page indices of the first tiles, then their data; the query loads go
+        // out behind them, so the latencies of the two overlap.
         prologue_idx();
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the page indices
+        if (ntiles > 0) start_tiles();
 
         // ---- absorbed query -> registers ----
         bf16x8 q[kSteps];
@@ -159,9 +180,10 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                 const int f = L::q_feature(u, gq);
                 q[u] = u < 32 ? load_bf16x8(qn + f) : load_bf16x8(qr + (f - kLatent));
             }
-            // vmcnt(0), as a builtin the compiler accounts for: the query has landed
-            // (so the compiler places no waits of its own in the loop, where they
-            // would also drain the tiles in flight), and so have the page indices.
+            // vmcnt(0), as a builtin the compiler accounts for: the query (the
+            // youngest loads) has landed, and with it the first tiles, so the
+            // compiler places no waits of its own in the loop, where they would
+            // also drain the tiles in flight.
             __builtin_amdgcn_s_waitcnt(0x0F70);
         }
 
@@ -178,35 +200,23 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         float l_part = 0.f;
 
         for (int pass = 0; pass < 2; ++pass) {
+            {
+                // Zeroed by the matrix core: a VALU zeroing of 256 AGPRs makes the
+                // compiler spill a zero vector and wait on its reload here.
+                const bf16x8 z = {};
 #pragma unroll
-            for (int i = 0; i < kDW; ++i)
+                for (int i = 0; i < kDW; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) O[i][j] = f32x16{};
-            settle_o<3>(O);
+                    for (int j = 0; j < 4; ++j) mfma32_zero_a(O[i][j], z);
+            }
             l_part = 0.f;
 
             if (ntiles > 0) {
                 if (pass > 0) {
                     prologue_idx();
                     wait_vmcnt_barrier<0>();
+                    start_tiles();
                 }
-                // The product at j = 0 reads slot kStages-1 (first loaded at j = 1)
-                // and the probability buffer: both start as zeros.
-                {
-                    using V4 = __attribute__((__vector_size__(4 * sizeof(int)))) int;
-                    LDS_AS V4* z = (LDS_AS V4*)(smem + (kStages - 1) * L::kTileBytes);
-                    for (int k = tid; k < L::kTileBytes / 16; k += 256) z[k] = V4{0, 0, 0, 0};
-                    LDS_AS V4* zp = (LDS_AS V4*)pbuf;
-                    for (int k = tid; k < (OUT32 ? 2 : 1) * PBuf::kBytes / 16; k += 256) zp[k] = V4{0, 0, 0, 0};
-                }
-                // Fill: the data of tiles 0 .. kAhead-1, each preceded by the page
-                // indices of the tile kAhead later (as iteration t - kAhead would).
-#pragma unroll
-                for (int t = 0; t < kAhead; ++t) {
-                    if (t + kAhead < ntiles) issue_idx(t + kAhead, wrap(t + kAhead));
-                    if (t < ntiles) issue_tile(t, t);
-                }
-
                 // Iterations j = 0 .. ntiles run one body: the score of tile j (slot
                 // cur) and the P . latent product of tile j-1 (slot prv). At j = 0
                 // the product reads a zeroed slot and a zeroed probability buffer and

@@ -194,6 +194,10 @@ __device__ __forceinline__ void mfma32_first_v(f32x16& c, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma32_acc_v(f32x16& c, bf16x8 a, bf16x8 b) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
+// c = 0 through the matrix core (0 . 0 + 0), so no VALU instruction writes c.
+__device__ __forceinline__ void mfma32_zero_a(f32x16& c, bf16x8 z) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(c) : "v"(z));
+}
 __device__ __forceinline__ void mfma32_acc_a(f32x16& c, bf16x8 a, bf16x8 b) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
