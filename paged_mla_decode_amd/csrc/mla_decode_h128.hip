@@ -1,6 +1,7 @@
 // gfx950 decode kernel for 128 query heads (DeepSeek-V2/V3 shapes).
 //
-// One workgroup of 4 waves per work item (a query row and a token chunk).
+// One workgroup of 4 waves (one per SIMD) per CU, persistent: it runs the
+// plan's list of work items for it (an item is a query row and a token chunk).
 // Per 32-token tile:
 //   * Score: wave w computes S^T = C . Q^T for heads 32w .. 32w+31 on the
 //     32x32x16 bf16 MFMA; its absorbed query (144 VGPRs) stays in registers.
@@ -13,12 +14,12 @@
 //     through the (slow) LDS transpose read once per workgroup instead of once
 //     per wave; the probabilities are read back with plain 16-byte reads.
 //
-// Software pipeline. Iteration j computes the score of tile j and the
-// P . latent product of tile j-1, with the softmax of tile j interleaved
-// between the latter's MFMAs: one wave per SIMD has no other wave to hide its
-// VALU work behind, so it hides it behind its own matrix-core work. P(j-1) is
-// read into registers at the top of the iteration; after a barrier the single
-// probability buffer is free for P(j).
+// Iteration j computes the score of tile j and the P . latent product of tile
+// j-1. The score MFMAs are spread between the product MFMAs (the score's LDS
+// reads, every wave reading the whole tile, then run under matrix-core work),
+// and the softmax of tile j rides between the last products: one wave per SIMD
+// has no other wave to hide its LDS waits or VALU work behind. The MFMAs are
+// volatile inline assembly so that this order holds.
 //
 // Memory pipeline. Tiles stream HBM -> LDS through a ring of kStages buffers
 // with direct 16-byte loads (tiles j+1 .. j+kStages-2 in flight while j and
@@ -29,9 +30,9 @@
 // waits on LDS reads (the compiler would make every LDS wait a full wait on
 // them), and no load of its own the compiler could wait on.
 //
-// Output. After the last tile, the normalised outputs go through LDS in four
-// rounds of 128 heads x 128 columns, so that every store instruction writes
-// whole rows (two heads x 512 bytes in fp32).
+// Output. After the last tile, the normalised outputs go through LDS (bf16:
+// all 512 columns at once where the ring holds them; fp32: four rounds of 128
+// columns), so that every store instruction writes whole head rows.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -51,21 +52,14 @@ struct H128Stages {
     static constexpr int value = KV8 ? 6 : (OUT32 ? 3 : 4);
 };
 
-// Wait states between the VALU accesses of the 16 output accumulators and the
-// inline-assembly MFMAs that accumulate into them (both directions; see
-// settle_v). One statement ties all 16, so no access can be scheduled across.
-template <int kNops>
+// Wait states between the last inline-assembly MFMAs that accumulate into the
+// 16 output accumulators and the VALU accesses that follow (see settle_v). One
+// statement ties all 16, so no access can be scheduled before it.
 __device__ __forceinline__ void settle_o(f32x16 (&O)[4][4]) {
-    if constexpr (kNops == 3)
-        asm volatile("s_nop 2"
-                     : "+a"(O[0][0]), "+a"(O[0][1]), "+a"(O[0][2]), "+a"(O[0][3]), "+a"(O[1][0]), "+a"(O[1][1]),
-                       "+a"(O[1][2]), "+a"(O[1][3]), "+a"(O[2][0]), "+a"(O[2][1]), "+a"(O[2][2]), "+a"(O[2][3]),
-                       "+a"(O[3][0]), "+a"(O[3][1]), "+a"(O[3][2]), "+a"(O[3][3]));
-    else
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                     : "+a"(O[0][0]), "+a"(O[0][1]), "+a"(O[0][2]), "+a"(O[0][3]), "+a"(O[1][0]), "+a"(O[1][1]),
-                       "+a"(O[1][2]), "+a"(O[1][3]), "+a"(O[2][0]), "+a"(O[2][1]), "+a"(O[2][2]), "+a"(O[2][3]),
-                       "+a"(O[3][0]), "+a"(O[3][1]), "+a"(O[3][2]), "+a"(O[3][3]));
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(O[0][0]), "+a"(O[0][1]), "+a"(O[0][2]), "+a"(O[0][3]), "+a"(O[1][0]), "+a"(O[1][1]),
+                   "+a"(O[1][2]), "+a"(O[1][3]), "+a"(O[2][0]), "+a"(O[2][1]), "+a"(O[2][2]), "+a"(O[2][3]),
+                   "+a"(O[3][0]), "+a"(O[3][1]), "+a"(O[3][2]), "+a"(O[3][3]));
 }
 
 template <bool KV8, bool OUT32>
@@ -409,7 +403,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                     iteration(j, cur);
                     cur = wrap(cur + 1);
                 }
-                settle_o<24>(O);
+                settle_o(O);
             }
             // Did any head outgrow its reference? All waves must agree (the tiles are
             // loaded cooperatively), so the flag goes through LDS.

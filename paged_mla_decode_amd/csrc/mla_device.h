@@ -185,7 +185,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 //     instruction right before it is ready: the gfx950 VALU -> MFMA source
 //     requirement);
 //   * back-to-back products accumulating into the same registers need none;
-//   * readers (and VALU writers) of a result wait through settle(), at least
+//   * readers (and VALU writers) of a result wait through a settle statement, at least
 //     19 wait states after the last product that wrote it (an 8-pass XDL
 //     write followed by a VALU access needs 11).
 __device__ __forceinline__ void mfma32_first_v(f32x16& c, bf16x8 a, bf16x8 b) {
@@ -203,9 +203,6 @@ __device__ __forceinline__ void mfma32_acc_a(f32x16& c, bf16x8 a, bf16x8 b) {
 }
 __device__ __forceinline__ void settle_v(f32x16& c) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
-}
-__device__ __forceinline__ void settle_a(f32x16& c) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(c));
 }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
