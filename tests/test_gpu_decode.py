@@ -139,3 +139,31 @@ def test_deterministic(dev):
     a, la, _ = run_decode(batch, dev, "bf16", num_cus=8)
     b, lb, _ = run_decode(batch, dev, "bf16", num_cus=8)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8_e4m3fn"])
+def test_one_worker_runs_every_item(dev, cache_dtype):
+    """Plans for one and two compute units: a persistent workgroup runs many
+    items in turn (empty requests, partial tiles, a piece of a split row and,
+    for the bf16 cache, a row whose score spread forces the exact rerun), so
+    every piece of per-item state must start fresh."""
+    lens = [0, 1, 31, 32, 33, 700, 0, 65, 2000, 300]
+    batch = workloads.random_decode_batch(31, lens, num_heads=128, page_size=64, cache_dtype=cache_dtype)
+    if cache_dtype == "bf16":
+        # Request 9: one token far past the first tile scores ~150 (log2) above the rest.
+        rows = workloads.token_rows(batch.kv_indptr, batch.kv_indices, batch.seq_lens, 64)
+        hot = workloads.bf16_bits_to_f32(batch.cache.reshape(-1, 576)[rows[int(np.sum(batch.seq_lens[:9])) + 250]])
+        qn = workloads.bf16_bits_to_f32(batch.q_nope).copy()
+        qn[9, :, :] = hot[:512] * 10.0
+        batch.q_nope = workloads.f32_to_bf16_bits(qn)
+    say(f"one worker {cache_dtype}")
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    if cache_dtype == "bf16":
+        assert ref_lse[9].min() - math.log(2) * 64 > 0  # the rerun path is taken
+    # One compute unit: one worker runs all ten items. Two: the second worker runs
+    # nine of them, the first of which is the tail piece of a split row.
+    for cus in (1, 2):
+        out, lse, dec = run_decode(batch, dev, "bf16", num_cus=cus, max_splits=3)
+        h = dec.header()
+        assert h.num_workers == cus and (cus == 1 or h.num_merges > 0)
+        compare(out, lse, ref_out, ref_lse, False, f"{cus} worker(s) {cache_dtype}")
