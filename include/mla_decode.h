@@ -88,7 +88,7 @@ typedef struct {
                                a fixed per-item cost counted as tokens) */
     int32_t num_workers;    /* workgroups of the decode launch; worker w processes
                                items [workers[w], workers[w+1]) in order */
-    int32_t reserved0;
+    int32_t max_merge_partials; /* most partials any one merged row has (0 without merges) */
     int64_t num_page_entries; /* kv_indptr[batch]: entries of kv_indices the batch uses */
     int64_t items_offset;   /* byte offset of mla_work_item[num_items] */
     int64_t merges_offset;  /* byte offset of mla_merge_item[num_merges] */

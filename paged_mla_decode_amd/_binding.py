@@ -58,7 +58,7 @@ class mla_plan_header(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("num_rows", ctypes.c_int32),
                 ("num_items", ctypes.c_int32), ("num_merges", ctypes.c_int32),
                 ("num_partials", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
-                ("num_workers", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("num_workers", ctypes.c_int32), ("max_merge_partials", ctypes.c_int32),
                 ("num_page_entries", ctypes.c_int64), ("items_offset", ctypes.c_int64),
                 ("merges_offset", ctypes.c_int64), ("workers_offset", ctypes.c_int64),
                 ("plan_bytes", ctypes.c_int64),

@@ -153,7 +153,12 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
         m.out = out_d;
         m.lse = lse_d;
         m.num_heads = params->num_heads;
-        err = launch_merge_partials(params->out_dtype, m, h->num_merges, stream);
+        // Merges come most partials first (planner); the leading wide ones.
+        const mla_merge_item* hm =
+            reinterpret_cast<const mla_merge_item*>(reinterpret_cast<const char*>(plan_h) + h->merges_offset);
+        int num_wide = 0;
+        while (num_wide < h->num_merges && hm[num_wide].num_partials >= kWideMergePartials) ++num_wide;
+        err = launch_merge_partials(params->out_dtype, m, h->num_merges, num_wide, stream);
         if (err != 0) return MLA_ERR_HIP;
     }
     return MLA_OK;

@@ -403,69 +403,122 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // Merge of split-KV partials (one wave per (row, head)).
 // ---------------------------------------------------------------------------
+// Running LSE combination of one head's partials: m (max lse so far), wsum
+// (sum of e^{lse - m}) and acc (sum of e^{lse - m} v, 8 columns per lane).
+struct MergeState {
+    float m = -INFINITY, wsum = 0.f;
+    f32x8 acc = {};
+};
+
+// Folds partials [p0, p0 + nb) (nb <= kBatch) of merge `mi`, head h, into st.
+// The batch's loads are all in flight before any is combined; a larger
+// maximum rescales what came before.
+template <bool OUT32, int kBatch>
+__device__ __forceinline__ void merge_batch(const MergePartialsArgs& a, const mla_merge_item& mi, int h,
+                                            int lane, int p0, int nb, MergeState& st) {
+    using V = std::conditional_t<OUT32, f32x8, bf16x8>;
+    const int nh = a.num_heads;
+    float l[kBatch];
+    V v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+        if (k < nb) {
+            const int64_t slot = (int64_t)(mi.partial_begin + p0 + k) * nh + h;
+            l[k] = a.part_lse[slot];
+            v[k] = *(reinterpret_cast<const V*>(a.part_out) + slot * (kLatent / 8) + lane);
+        }
+    }
+    float mb = st.m;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+        if (k < nb) mb = fmaxf(mb, l[k]);
+    if (mb == -INFINITY) return;  // every partial so far is empty
+    const float r = st.m == -INFINITY ? 0.f : fast_exp2((st.m - mb) * kLog2e);
+    st.acc = st.acc * r;
+    st.wsum *= r;
+    st.m = mb;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+        if (k < nb) {
+            const float wp = fast_exp2((l[k] - st.m) * kLog2e);
+            st.wsum += wp;
+            f32x8 x;
+            if constexpr (OUT32) {
+                x = v[k];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = (float)v[k][e];
+            }
+            st.acc += wp * x;
+        }
+    }
+}
+
+template <bool OUT32>
+__device__ __forceinline__ void merge_store(const MergePartialsArgs& a, const mla_merge_item& mi, int h, int lane,
+                                            const MergeState& st) {
+    const int nh = a.num_heads;
+    const bool empty = !(st.wsum > 0.f);
+    const float inv = empty ? 0.f : 1.f / st.wsum;
+    const int64_t orow = (int64_t)mi.row * nh + h;
+    if constexpr (OUT32) {
+        *reinterpret_cast<f32x8*>(reinterpret_cast<float*>(a.out) + orow * kLatent + 8 * lane) = st.acc * inv;
+    } else {
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (__bf16)(st.acc[e] * inv);
+        *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(a.out) + orow * kLatent + 8 * lane) = o;
+    }
+    if (a.lse && lane == 0) a.lse[orow] = empty ? -INFINITY : st.m + __logf(st.wsum);
+}
+
+// Few partials per row: one wave per (row, head) folds them all.
 template <bool OUT32>
 __global__ __launch_bounds__(256) void merge_partials_kernel(const MergePartialsArgs a) {
+    constexpr int kBatch = 8;
     const mla_merge_item mi = a.merges[blockIdx.x];
     const int lane = threadIdx.x & 63;
-    const int nh = a.num_heads;
-    // Up to kBatch partials are loaded before any is combined (the loads of a
-    // batch are in flight together); a later batch rescales what came before
-    // when its maximum is larger (the pairwise LSE combination).
-    constexpr int kBatch = 8;
-    using V = std::conditional_t<OUT32, f32x8, bf16x8>;
-    for (int h = blockIdx.y * 4 + (threadIdx.x >> 6); h < nh; h += gridDim.y * 4) {
-        float m = -INFINITY, wsum = 0.f;
-        f32x8 acc = {};
-        for (int p0 = 0; p0 < mi.num_partials; p0 += kBatch) {
-            const int nb = min(kBatch, mi.num_partials - p0);
-            float l[kBatch];
-            V v[kBatch];
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k) {
-                if (k < nb) {
-                    const int64_t slot = (int64_t)(mi.partial_begin + p0 + k) * nh + h;
-                    l[k] = a.part_lse[slot];
-                    v[k] = *(reinterpret_cast<const V*>(a.part_out) + slot * (kLatent / 8) + lane);
-                }
-            }
-            float mb = m;
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k)
-                if (k < nb) mb = fmaxf(mb, l[k]);
-            if (mb == -INFINITY) continue;  // every partial so far is empty
-            const float r = m == -INFINITY ? 0.f : fast_exp2((m - mb) * kLog2e);
-            acc = acc * r;
-            wsum *= r;
-            m = mb;
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k) {
-                if (k < nb) {
-                    const float wp = fast_exp2((l[k] - m) * kLog2e);
-                    wsum += wp;
-                    f32x8 x;
-                    if constexpr (OUT32) {
-                        x = v[k];
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) x[e] = (float)v[k][e];
-                    }
-                    acc += wp * x;
-                }
-            }
-        }
-        const bool empty = !(wsum > 0.f);
-        const float inv = empty ? 0.f : 1.f / wsum;
-        const int64_t orow = (int64_t)mi.row * nh + h;
-        if constexpr (OUT32) {
-            *reinterpret_cast<f32x8*>(reinterpret_cast<float*>(a.out) + orow * kLatent + 8 * lane) = acc * inv;
-        } else {
-            bf16x8 o;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = (__bf16)(acc[e] * inv);
-            *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(a.out) + orow * kLatent + 8 * lane) = o;
-        }
-        if (a.lse && lane == 0) a.lse[orow] = empty ? -INFINITY : m + __logf(wsum);
+    for (int h = blockIdx.y * 4 + (threadIdx.x >> 6); h < a.num_heads; h += gridDim.y * 4) {
+        MergeState st;
+        for (int p0 = 0; p0 < mi.num_partials; p0 += kBatch)
+            merge_batch<OUT32, kBatch>(a, mi, h, lane, p0, min(kBatch, mi.num_partials - p0), st);
+        merge_store<OUT32>(a, mi, h, lane, st);
     }
+}
+
+// Many partials per row (a very long request cut into hundreds of pieces): a
+// workgroup of kWaves waves per (row, head), each folding its own batches, the
+// wave states combined through LDS. One wave alone would wait out hundreds of
+// dependent memory round trips.
+template <bool OUT32>
+__global__ __launch_bounds__(1024) void merge_partials_wide_kernel(const MergePartialsArgs a) {
+    constexpr int kWaves = 16, kBatch = 8;
+    const mla_merge_item mi = a.merges[blockIdx.x];
+    const int h = blockIdx.y;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    MergeState st;
+    for (int p0 = wv * kBatch; p0 < mi.num_partials; p0 += kWaves * kBatch)
+        merge_batch<OUT32, kBatch>(a, mi, h, lane, p0, min(kBatch, mi.num_partials - p0), st);
+    __shared__ float sm[kWaves], sw[kWaves];
+    __shared__ f32x8 sacc[kWaves][64];
+    if (lane == 0) {
+        sm[wv] = st.m;
+        sw[wv] = st.wsum;
+    }
+    sacc[wv][lane] = st.acc;
+    __syncthreads();
+    if (wv != 0) return;
+    MergeState t;
+    for (int k = 0; k < kWaves; ++k) t.m = fmaxf(t.m, sm[k]);
+    if (t.m != -INFINITY) {
+        for (int k = 0; k < kWaves; ++k) {
+            if (sm[k] == -INFINITY) continue;
+            const float r = fast_exp2((sm[k] - t.m) * kLog2e);
+            t.wsum += r * sw[k];
+            t.acc += r * sacc[k][lane];
+        }
+    }
+    merge_store<OUT32>(a, mi, h, lane, t);
 }
 
 // ---------------------------------------------------------------------------
@@ -581,14 +634,27 @@ int launch_decode(const Variant& v, int kv_dtype, int out_dtype, const DecodeArg
     return (int)hipErrorInvalidValue;
 }
 
-int launch_merge_partials(int out_dtype, const MergePartialsArgs& a, int num_merges, void* stream) {
+int launch_merge_partials(int out_dtype, const MergePartialsArgs& a, int num_merges, int num_wide,
+                          void* stream) {
     if (num_merges <= 0) return 0;
     hipStream_t s = (hipStream_t)stream;
-    const dim3 grid(num_merges, (a.num_heads + 3) / 4), block(256);
-    if (out_dtype == MLA_DTYPE_FP32)
-        merge_partials_kernel<true><<<grid, block, 0, s>>>(a);
-    else
-        merge_partials_kernel<false><<<grid, block, 0, s>>>(a);
+    const bool o32 = out_dtype == MLA_DTYPE_FP32;
+    if (num_wide > 0) {
+        const dim3 grid(num_wide, a.num_heads), block(1024);
+        if (o32)
+            merge_partials_wide_kernel<true><<<grid, block, 0, s>>>(a);
+        else
+            merge_partials_wide_kernel<false><<<grid, block, 0, s>>>(a);
+    }
+    if (num_merges > num_wide) {
+        MergePartialsArgs rest = a;
+        rest.merges = a.merges + num_wide;
+        const dim3 grid(num_merges - num_wide, (a.num_heads + 3) / 4), block(256);
+        if (o32)
+            merge_partials_kernel<true><<<grid, block, 0, s>>>(rest);
+        else
+            merge_partials_kernel<false><<<grid, block, 0, s>>>(rest);
+    }
     return (int)hipGetLastError();
 }
 

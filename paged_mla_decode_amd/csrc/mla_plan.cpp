@@ -217,6 +217,10 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
             merges.push_back(mla_merge_item{rows[i].row, num_partials, npieces[i], 0});
             num_partials += npieces[i];
         }
+    // Rows with the most partials first: the launch merges the leading ones
+    // (at least kWideMergePartials each) with the wide kernel.
+    std::stable_sort(merges.begin(), merges.end(),
+                     [](const mla_merge_item& x, const mla_merge_item& y) { return x.num_partials > y.num_partials; });
     std::vector<int32_t> next_slot(first_slot);
     std::vector<mla_work_item> items;
     items.reserve(pieces.size());
@@ -256,6 +260,8 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
     h.num_partials = num_partials;
     h.chunk_tokens = (int32_t)std::min<int64_t>(chunk, INT32_MAX);
     h.num_workers = num_workers;
+    h.max_merge_partials = 0;
+    for (const mla_merge_item& mi : merges) h.max_merge_partials = std::max(h.max_merge_partials, mi.num_partials);
     h.num_page_entries = kv_indptr[batch];
     layout(h.num_items, h.num_merges, num_workers, num_partials, p->num_heads, partial_elem_bytes(p), &h);
     if ((size_t)h.plan_bytes > plan_h_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;

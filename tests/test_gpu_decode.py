@@ -167,3 +167,17 @@ def test_one_worker_runs_every_item(dev, cache_dtype):
         h = dec.header()
         assert h.num_workers == cus and (cus == 1 or h.num_merges > 0)
         compare(out, lse, ref_out, ref_lse, False, f"{cus} worker(s) {cache_dtype}")
+
+
+@pytest.mark.parametrize("H", [16, 128])
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp32"])
+def test_many_partials_take_the_wide_merge(dev, H, out_dtype):
+    """A long request cut into dozens of pieces: its partials are merged by the
+    wide merge kernel (a workgroup per row and head), the short rows' by the
+    one-wave kernel in the same launch."""
+    batch = workloads.random_decode_batch(41 + H, [20000, 300, 5, 2600], num_heads=H, page_size=16)
+    say(f"wide merge H={H} out={out_dtype}")
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    out, lse, dec = run_decode(batch, dev, out_dtype, num_cus=64)
+    assert dec.header().max_merge_partials >= 16
+    compare(out, lse, ref_out, ref_lse, out_dtype == "fp32", f"wide merge H={H} out={out_dtype}")

@@ -69,6 +69,8 @@ def check_invariants(p, batch, h, items, merges, workers):
     for r, segs in covered.items():
         assert (len(segs) > 1) == (r in merged_rows)
     assert h.num_merges == len(merges)
+    assert h.max_merge_partials == max((mi.num_partials for mi in merges), default=0)
+    assert all(a.num_partials >= b.num_partials for a, b in zip(merges, merges[1:])), "most partials first"
     # the worker table partitions the items, at most one worker per resident workgroup
     assert len(workers) == h.num_workers + 1 and workers[0] == 0 and workers[-1] == len(items)
     assert all(a < b for a, b in zip(workers, workers[1:])), "every worker has an item"
