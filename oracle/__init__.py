@@ -6,6 +6,8 @@ Python binding never import it, and it imports neither of them.
 
 * ``mla_decode``: plain fp64 attention (``mla_oracle.c``), built with gcc.
 * ``merge_states``: the two-state log-sum-exp merge (``mla_oracle.c``).
+* ``absorb_query`` / ``project_output``: the per-head W_UK and W_UV products on
+  either side of the latent attention (numpy matrix products in float64).
 * ``tree_suffix_compact``: the pre-PR definition of the suffix page table from
   section 1 of the SGLang PR 49477 analysis: sort the keys "column if visible,
   column + W if not" with a stable sort, gather the draft slots in that order,
@@ -135,6 +137,40 @@ def decode_batch(batch):
     return mla_decode(batch.q_nope, batch.q_rope, batch.cache, batch.kv_indptr, batch.kv_indices,
                       batch.page_size, batch.sm_scale, kv_last_page_len=batch.kv_last_page_len,
                       qo_indptr=batch.qo_indptr, kv_scale=batch.kv_scale)
+
+
+def absorb_query(q_nope, w_uk):
+    """W_UK absorption into the query (SGLang v0.3 MLA page, weight absorption;
+    sglang-jax MLA gap page, section 2.1): per head, the 128-wide nope query
+    times W_UK^T gives the 512-wide query that scores directly against the
+    latent. q_nope [N, H, D], w_uk [A, H, D] (the [A, N, H] layout of the gap
+    page's MLAEinsum split, section 2.2) -> q_abs [N, H, A] float64.
+    q_abs[n, h, a] = sum_d q_nope[n, h, d] * w_uk[a, h, d]."""
+    q = np.asarray(q_nope, dtype=np.float64)
+    w = np.asarray(w_uk, dtype=np.float64)
+    N, H, D = q.shape
+    A = w.shape[0]
+    assert w.shape == (A, H, D)
+    out = np.empty((N, H, A))
+    for h in range(H):  # one matrix product per head
+        out[:, h, :] = q[:, h, :] @ w[:, h, :].T
+    return out
+
+
+def project_output(out_latent, w_uv):
+    """W_UV applied after the latent attention (the same pages: W_UV moves to the
+    output side): per head, the 512-wide latent output times W_UV gives the
+    head_dim-wide value output. out_latent [N, H, A], w_uv [A, H, D] ->
+    o [N, H, D] float64. o[n, h, d] = sum_a out_latent[n, h, a] * w_uv[a, h, d]."""
+    x = np.asarray(out_latent, dtype=np.float64)
+    w = np.asarray(w_uv, dtype=np.float64)
+    N, H, A = x.shape
+    D = w.shape[2]
+    assert w.shape == (A, H, D)
+    o = np.empty((N, H, D))
+    for h in range(H):
+        o[:, h, :] = x[:, h, :] @ w[:, h, :]
+    return o
 
 
 def merge_states(v_a, s_a, v_b, s_b):

@@ -77,11 +77,11 @@ def test_absorption_identity_against_decompressed_mha():
     w_uv = rng.standard_normal((A, H, D)) / math.sqrt(A)
     q_nope_heads = rng.standard_normal((batch.num_rows, H, D)) * 0.5
     _, q_rope = _q(batch)
-    # Absorbed query: per head, q_nope (128) times W_UK^T -> 512.
-    q_abs = np.einsum("nhd,ahd->nha", q_nope_heads, w_uk)
+    # Absorbed query: per head, q_nope (128) times W_UK^T -> 512; W_UV on the output.
+    q_abs = oracle.absorb_query(q_nope_heads, w_uk)
     out_lat, lse = oracle.mla_decode(q_abs, q_rope, batch.cache, batch.kv_indptr, batch.kv_indices,
                                      1, SM_SCALE, kv_last_page_len=batch.kv_last_page_len)
-    out_abs = np.einsum("nha,ahd->nhd", out_lat, w_uv)
+    out_abs = oracle.project_output(out_lat, w_uv)
 
     for b in range(batch.batch):
         c = _tokens(batch, b)  # [L, 576]
@@ -306,3 +306,35 @@ def test_compaction_on_tree_workload_and_padding_rows():
         assert seqlens[r] <= tv.max_tree_depth
         slots = tv.req_to_token[req, tv.prefix_lens[req]:tv.prefix_lens[req] + tv.width]
         assert table[r].tolist() == _partition_by_hand(tv.tree_mask[r], slots)
+
+
+# ---------------------------------------------------------------------------
+# The projections by brute force on a tiny case (one multiply-add at a time),
+# and the identity that ties them together: with W_UV = W_UK, projecting the
+# absorbed query back gives q_nope times the head's Gram matrix W^T W.
+# ---------------------------------------------------------------------------
+
+def test_projections_brute_force_and_gram_identity():
+    rng = np.random.Generator(np.random.PCG64(12))
+    N, H, A, D = 3, 2, 6, 4
+    q = rng.standard_normal((N, H, D))
+    w = rng.standard_normal((A, H, D))
+    x = rng.standard_normal((N, H, A))
+    qa = oracle.absorb_query(q, w)
+    o = oracle.project_output(x, w)
+    for n in range(N):
+        for h in range(H):
+            for a in range(A):
+                acc = 0.0
+                for d in range(D):
+                    acc += q[n, h, d] * w[a, h, d]
+                assert abs(qa[n, h, a] - acc) < 1e-12
+            for d in range(D):
+                acc = 0.0
+                for a in range(A):
+                    acc += x[n, h, a] * w[a, h, d]
+                assert abs(o[n, h, d] - acc) < 1e-12
+    back = oracle.project_output(qa, w)
+    for h in range(H):
+        gram = w[:, h, :].T @ w[:, h, :]
+        np.testing.assert_allclose(back[:, h, :], q[:, h, :] @ gram, rtol=1e-12, atol=1e-12)
