@@ -249,6 +249,57 @@ int32_t mla_tree_suffix_compact(const uint8_t* tree_mask_d, int64_t mask_stride,
                                 int64_t table_stride, int32_t* cache_seqlens_d, void* stream);
 
 /*
+ * mla_absorb_query - the query side of weight absorption: fold W_UK into the
+ * no-rope query so that scores are taken directly against the cached latent
+ * (SGLang v0.3 MLA page, weight absorption; sglang-jax MLA gap page, sections
+ * 2.1-2.2):
+ *   q_abs[n,h,a] = sum_d q[n,h,d] * W_UK[a,h,d]        (a < 512, d < head_dim)
+ * where the per-head key is k_nope[t,h,d] = sum_a c[t,a] * W_UK[a,h,d], so
+ * q_abs[n,h,:] . c_t = q[n,h,:] . k_nope[t,h,:]. bf16 in and out, fp32
+ * accumulation, one rounding to bf16 per output.
+ *
+ *   q_d       bf16 [N, H, head_dim]; element (n, h, d) at n*q_stride_n + h*q_stride_h + d.
+ *   w_uk_d    bf16 W_UK; element (a, h, d) at a*w_uk_stride_a + h*w_uk_stride_h + d
+ *             (d contiguous: [512, H, head_dim] or [H, 512, head_dim] both fit).
+ *   q_abs_d   bf16 [N, H, 512]; element (n, h, a) at n*q_abs_stride_n + h*q_abs_stride_h + a.
+ *             Writing into a concatenated [N, H, 576] decode query (strides
+ *             H*576 and 576) leaves its rope part untouched.
+ *   head_dim  must be 128. num_heads in [1, 65535], num_rows in [0, 2097120].
+ * All strides in elements, non-negative multiples of 8; bases 16-byte aligned.
+ * q_abs_d must not overlap q_d or w_uk_d. Returns MLA_OK, MLA_ERR_INVALID_ARG,
+ * MLA_ERR_UNSUPPORTED or MLA_ERR_HIP.
+ */
+int32_t mla_absorb_query(const void* q_d, int64_t q_stride_n, int64_t q_stride_h, const void* w_uk_d,
+                         int64_t w_uk_stride_a, int64_t w_uk_stride_h, void* q_abs_d,
+                         int64_t q_abs_stride_n, int64_t q_abs_stride_h, int32_t num_rows,
+                         int32_t num_heads, int32_t head_dim, void* stream);
+
+/*
+ * mla_project_output - the output side of weight absorption: map the per-head
+ * attention result over latents (what mla_decode writes) to the value head
+ * dimension with W_UV (SGLang v0.3 MLA page, weight absorption; sglang-jax MLA
+ * gap page, section 2.2):
+ *   o[n,h,d] = sum_a x[n,h,a] * W_UV[a,h,d]             (a < 512, d < head_dim)
+ * the same result as attending over the decompressed values
+ * v[t,h,d] = sum_a c[t,a] * W_UV[a,h,d]. bf16 in and out, fp32 accumulation.
+ *
+ *   x_d       bf16 [N, H, 512]; element (n, h, a) at n*x_stride_n + h*x_stride_h + a.
+ *   w_uv_d    bf16 W_UV; element (a, h, d) at h*w_uv_stride_h + d*w_uv_stride_d + a
+ *             (a contiguous: the value rows of a kv_b_proj weight stored
+ *             [H*(dn+dv), 512] fit with stride_h (dn+dv)*512, stride_d 512, base
+ *             advanced by dn*512).
+ *   o_d       bf16 [N, H, head_dim]; element (n, h, d) at n*o_stride_n + h*o_stride_h + d.
+ *   head_dim  must be 128. num_heads in [1, 65535], num_rows in [0, 2097120].
+ * All strides in elements, non-negative multiples of 8; bases 16-byte aligned.
+ * o_d must not overlap x_d or w_uv_d. Returns MLA_OK, MLA_ERR_INVALID_ARG,
+ * MLA_ERR_UNSUPPORTED or MLA_ERR_HIP.
+ */
+int32_t mla_project_output(const void* x_d, int64_t x_stride_n, int64_t x_stride_h, const void* w_uv_d,
+                           int64_t w_uv_stride_h, int64_t w_uv_stride_d, void* o_d,
+                           int64_t o_stride_n, int64_t o_stride_h, int32_t num_rows,
+                           int32_t num_heads, int32_t head_dim, void* stream);
+
+/*
  * Name of the decode kernel instantiation these parameters select (static
  * storage), e.g. "mla_decode<hw32,hs4,kv_bf16,out_bf16>"; NULL if unsupported.
  * Tests use it to prove which branch ran.

@@ -97,10 +97,13 @@ _lib.mla_merge_states.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _p]
 _lib.mla_tree_suffix_compact.restype = _i32
 _lib.mla_tree_suffix_compact.argtypes = [_p, _i64, _p, _i64, _p, _i32, _i32, _i32, _p, _i64, _p,
                                          _p]
+for _fn in (_lib.mla_absorb_query, _lib.mla_project_output):
+    _fn.restype = _i32
+    _fn.argtypes = [_p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i32, _i32, _i32, _p]
 
 EXPORTED_SYMBOLS = ("mla_status_string", "mla_decode_variant", "mla_decode_workspace_size",
                     "mla_decode_plan", "mla_decode", "mla_merge_states",
-                    "mla_tree_suffix_compact")
+                    "mla_tree_suffix_compact", "mla_absorb_query", "mla_project_output")
 
 
 class MlaError(RuntimeError):
@@ -201,6 +204,22 @@ def mla_tree_suffix_compact(tree_mask_d, mask_stride, req_to_token_d, req_stride
                                         int(num_rows), int(num_actual_rows), _ptr(page_table_d),
                                         int(table_stride), _ptr(cache_seqlens_d),
                                         _stream(stream))
+
+
+def mla_absorb_query(q_d, q_stride_n, q_stride_h, w_uk_d, w_uk_stride_a, w_uk_stride_h, q_abs_d,
+                     q_abs_stride_n, q_abs_stride_h, num_rows, num_heads, head_dim, stream=None):
+    return _lib.mla_absorb_query(_ptr(q_d), int(q_stride_n), int(q_stride_h), _ptr(w_uk_d),
+                                 int(w_uk_stride_a), int(w_uk_stride_h), _ptr(q_abs_d),
+                                 int(q_abs_stride_n), int(q_abs_stride_h), int(num_rows),
+                                 int(num_heads), int(head_dim), _stream(stream))
+
+
+def mla_project_output(x_d, x_stride_n, x_stride_h, w_uv_d, w_uv_stride_h, w_uv_stride_d, o_d,
+                       o_stride_n, o_stride_h, num_rows, num_heads, head_dim, stream=None):
+    return _lib.mla_project_output(_ptr(x_d), int(x_stride_n), int(x_stride_h), _ptr(w_uv_d),
+                                   int(w_uv_stride_h), int(w_uv_stride_d), _ptr(o_d),
+                                   int(o_stride_n), int(o_stride_h), int(num_rows),
+                                   int(num_heads), int(head_dim), _stream(stream))
 
 
 def read_plan(plan_h):

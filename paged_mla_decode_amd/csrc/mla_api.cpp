@@ -180,6 +180,69 @@ int32_t mla_merge_states(const void* v_a_d, const float* s_a_d, const void* v_b_
                : MLA_ERR_HIP;
 }
 
+namespace {
+
+bool strides_ok(int64_t a, int64_t b) { return a >= 0 && b >= 0 && a % 8 == 0 && b % 8 == 0; }
+
+// Shared checks of the two projections: bf16 operands, head_dim 128, every
+// 16-byte operand run aligned.
+int32_t check_projection(const void* x, int64_t xn, int64_t xh, const void* w, int64_t w0,
+                         int64_t w1, const void* y, int64_t yn, int64_t yh, int32_t num_rows,
+                         int32_t num_heads, int32_t head_dim) {
+    if (num_rows < 0 || num_heads <= 0 || head_dim <= 0) return MLA_ERR_INVALID_ARG;
+    if (head_dim != 128 || num_heads > 65535 || num_rows > 32 * 65535) return MLA_ERR_UNSUPPORTED;
+    if (num_rows == 0) return MLA_OK;
+    if (!x || !w || !y || !aligned16(x) || !aligned16(w) || !aligned16(y)) return MLA_ERR_INVALID_ARG;
+    if (!strides_ok(xn, xh) || !strides_ok(w0, w1) || !strides_ok(yn, yh)) return MLA_ERR_INVALID_ARG;
+    return MLA_OK;
+}
+
+}  // namespace
+
+int32_t mla_absorb_query(const void* q_d, int64_t q_stride_n, int64_t q_stride_h, const void* w_uk_d,
+                         int64_t w_uk_stride_a, int64_t w_uk_stride_h, void* q_abs_d,
+                         int64_t q_abs_stride_n, int64_t q_abs_stride_h, int32_t num_rows,
+                         int32_t num_heads, int32_t head_dim, void* stream) {
+    const int32_t err = check_projection(q_d, q_stride_n, q_stride_h, w_uk_d, w_uk_stride_a,
+                                         w_uk_stride_h, q_abs_d, q_abs_stride_n, q_abs_stride_h,
+                                         num_rows, num_heads, head_dim);
+    if (err != MLA_OK || num_rows == 0) return err;
+    HeadGemmArgs g;
+    g.a = static_cast<const uint16_t*>(w_uk_d);
+    g.a_head = w_uk_stride_h;
+    g.a_row = w_uk_stride_a;
+    g.b = static_cast<const uint16_t*>(q_d);
+    g.b_head = q_stride_h;
+    g.b_row = q_stride_n;
+    g.d = q_abs_d;
+    g.d_head = q_abs_stride_h;
+    g.d_row = q_abs_stride_n;
+    g.n_rows = num_rows;
+    return launch_head_gemm(g, num_heads, 512, head_dim, stream) == 0 ? MLA_OK : MLA_ERR_HIP;
+}
+
+int32_t mla_project_output(const void* x_d, int64_t x_stride_n, int64_t x_stride_h, const void* w_uv_d,
+                           int64_t w_uv_stride_h, int64_t w_uv_stride_d, void* o_d,
+                           int64_t o_stride_n, int64_t o_stride_h, int32_t num_rows,
+                           int32_t num_heads, int32_t head_dim, void* stream) {
+    const int32_t err = check_projection(x_d, x_stride_n, x_stride_h, w_uv_d, w_uv_stride_h,
+                                         w_uv_stride_d, o_d, o_stride_n, o_stride_h, num_rows,
+                                         num_heads, head_dim);
+    if (err != MLA_OK || num_rows == 0) return err;
+    HeadGemmArgs g;
+    g.a = static_cast<const uint16_t*>(w_uv_d);
+    g.a_head = w_uv_stride_h;
+    g.a_row = w_uv_stride_d;
+    g.b = static_cast<const uint16_t*>(x_d);
+    g.b_head = x_stride_h;
+    g.b_row = x_stride_n;
+    g.d = o_d;
+    g.d_head = o_stride_h;
+    g.d_row = o_stride_n;
+    g.n_rows = num_rows;
+    return launch_head_gemm(g, num_heads, head_dim, 512, stream) == 0 ? MLA_OK : MLA_ERR_HIP;
+}
+
 int32_t mla_tree_suffix_compact(const uint8_t* tree_mask_d, int64_t mask_stride,
                                 const int32_t* req_to_token_d, int64_t req_stride,
                                 const int32_t* prefix_lens_d, int32_t width, int32_t num_rows,

@@ -79,6 +79,20 @@ int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num
 constexpr int kWideMergePartials = 16;
 int launch_merge_partials(int out_dtype, const MergePartialsArgs& a, int num_merges, int num_wide,
                           void* stream);
+// Per-head product D[h][n][m] = sum_k A[h][m][k] B[h][n][k] in bf16 (fp32
+// accumulation): element (h, m, k) of A at a[h*a_head + m*a_row + k], of B at
+// b[h*b_head + n*b_row + k]; D at d[h*d_head + n*d_row + m]. Element strides.
+struct HeadGemmArgs {
+    const uint16_t* a;
+    int64_t a_head, a_row;
+    const uint16_t* b;
+    int64_t b_head, b_row;
+    void* d;
+    int64_t d_head, d_row;
+    int32_t n_rows;
+};
+// m_len a multiple of 128; k_len 128 or 512. mla_proj.hip.
+int launch_head_gemm(const HeadGemmArgs& g, int num_heads, int m_len, int k_len, void* stream);
 int launch_merge_states(const void* v_a, const float* s_a, const void* v_b, const float* s_b,
                         void* v_out, float* s_out, int64_t num_rows, int32_t head_dim,
                         int32_t v_dtype, void* stream);

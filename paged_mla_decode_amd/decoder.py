@@ -108,3 +108,35 @@ def tree_suffix_compact(tree_mask, req_to_token, prefix_lens, width, num_rows=No
     if st != B.MLA_OK:
         raise B.MlaError("mla_tree_suffix_compact", st)
     return table, seqlens
+
+
+def absorb_query(q, w_uk, out=None, stream=None):
+    """q [N, H, D] bf16 (D contiguous), w_uk [512, H, D] or any strided view with D
+    contiguous, indexed (a, h, d) -> q_abs [N, H, 512] bf16 (or written into `out`,
+    e.g. the first 512 columns of a [N, H, 576] query)."""
+    N, H, D = q.shape
+    assert w_uk.shape == (512, H, D) and q.stride(2) == 1 and w_uk.stride(2) == 1
+    out = torch.empty((N, H, 512), dtype=torch.bfloat16, device=q.device) if out is None else out
+    assert out.shape == (N, H, 512) and out.stride(2) == 1
+    st = B.mla_absorb_query(q, q.stride(0), q.stride(1), w_uk, w_uk.stride(0), w_uk.stride(1),
+                            out, out.stride(0), out.stride(1), N, H, D,
+                            stream or torch.cuda.current_stream(q.device))
+    if st != B.MLA_OK:
+        raise B.MlaError("mla_absorb_query", st)
+    return out
+
+
+def project_output(x, w_uv, out=None, stream=None):
+    """x [N, H, 512] bf16 (latent contiguous), w_uv any view indexed (a, h, d) with a
+    contiguous (e.g. kv_b_proj's value rows viewed as [512, H, D]) -> o [N, H, D] bf16."""
+    N, H, A = x.shape
+    D = w_uv.shape[2]
+    assert A == 512 and w_uv.shape == (512, H, D) and x.stride(2) == 1 and w_uv.stride(0) == 1
+    out = torch.empty((N, H, D), dtype=torch.bfloat16, device=x.device) if out is None else out
+    assert out.shape == (N, H, D) and out.stride(2) == 1
+    st = B.mla_project_output(x, x.stride(0), x.stride(1), w_uv, w_uv.stride(1), w_uv.stride(2),
+                              out, out.stride(0), out.stride(1), N, H, D,
+                              stream or torch.cuda.current_stream(x.device))
+    if st != B.MLA_OK:
+        raise B.MlaError("mla_project_output", st)
+    return out

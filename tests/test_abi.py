@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 7
+    assert len(names) == 9
     lib = ctypes.CDLL(m.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -171,3 +171,30 @@ def test_merge_and_compact_validate():
     assert c(FAKE, 32, FAKE, 80, FAKE, 64, 8, 8, FAKE, 64, FAKE, 0) == m.MLA_ERR_INVALID_ARG
     assert c(None, 64, FAKE, 80, FAKE, 64, 8, 8, FAKE, 64, FAKE, 0) == m.MLA_ERR_INVALID_ARG
     assert c(FAKE, 64, FAKE, 80, FAKE, 64, 0, 0, FAKE, 64, FAKE, 0) == m.MLA_OK
+
+
+@pytest.mark.parametrize("fn", ["mla_absorb_query", "mla_project_output"])
+def test_projections_validate(fn):
+    f = getattr(m, fn)
+    # (x, xn, xh, w, w0, w1, y, yn, yh, rows, heads, head_dim, stream)
+    good = [FAKE, 128 * 128, 128, FAKE, 128 * 128, 128, FAKE, 128 * 512, 512, 4, 128, 128, 0]
+
+    def call(**kw):
+        a = list(good)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return f(*a)
+
+    assert call(a9=0) == m.MLA_OK  # nothing to do: no launch
+    assert call(a9=-1) == m.MLA_ERR_INVALID_ARG
+    assert call(a10=0) == m.MLA_ERR_INVALID_ARG
+    assert call(a11=64) == m.MLA_ERR_UNSUPPORTED
+    assert call(a11=0) == m.MLA_ERR_INVALID_ARG
+    assert call(a9=32 * 65535 + 1) == m.MLA_ERR_UNSUPPORTED
+    assert call(a10=65536) == m.MLA_ERR_UNSUPPORTED
+    for i in (0, 3, 6):
+        assert call(**{f"a{i}": None}) == m.MLA_ERR_INVALID_ARG
+        assert call(**{f"a{i}": FAKE + 8}) == m.MLA_ERR_INVALID_ARG  # 8-byte aligned only
+    for i in (1, 2, 4, 5, 7, 8):
+        assert call(**{f"a{i}": 12}) == m.MLA_ERR_INVALID_ARG
+        assert call(**{f"a{i}": -8}) == m.MLA_ERR_INVALID_ARG

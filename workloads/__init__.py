@@ -344,6 +344,42 @@ def random_decode_batch(seed: int, seq_lens, num_heads: int, page_size: int,
         cache_dtype=cache_dtype, rows_per_request=rows_per_request)
 
 
+@dataclasses.dataclass
+class ProjectionInputs:
+    """Inputs of the two per-head projections of weight absorption, bf16 bits.
+
+    q     [N, H, D]  the no-rope query of each head, before absorption
+    w_uk  [A, H, D]  latent -> key-nope map (element (a, h, d))
+    w_uv  [A, H, D]  latent -> value map
+    x     [N, H, A]  a latent attention output, as decode writes it
+    """
+    q: np.ndarray
+    w_uk: np.ndarray
+    w_uv: np.ndarray
+    x: np.ndarray
+
+
+def projection_inputs(seed: int, num_rows: int, num_heads: int,
+                      head_dim: int = 128) -> ProjectionInputs:
+    """Seeded projection inputs. Draw order q, w_uk, w_uv, x. Activations are
+    N(0,1)*0.5 like every other input here; the weights map the 512-wide latent
+    out, so they are N(0,1)/sqrt(512) (unit-variance outputs for unit inputs).
+    All rounded to bfloat16 (RNE)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    A = KV_LORA_RANK
+    w_scale = np.float32(1.0 / math.sqrt(A))
+
+    def weights():
+        return f32_to_bf16_bits(
+            rng.standard_normal(size=(A, num_heads, head_dim), dtype=np.float32) * w_scale)
+
+    q = _draw_bf16(rng, (num_rows, num_heads, head_dim))
+    w_uk = weights()
+    w_uv = weights()
+    x = _draw_bf16(rng, (num_rows, num_heads, A))
+    return ProjectionInputs(q=q, w_uk=w_uk, w_uv=w_uv, x=x)
+
+
 CONFIGS = {
     "tiny": tiny,
     "v2_lite": v2_lite,
