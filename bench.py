@@ -17,7 +17,14 @@ also reported: decode tokens/s (query rows / step time) and the fraction of
 MI355X's 8 TB/s HBM peak. The CPU oracle is timed on the host's cores on a
 bounded prefix of the same batch (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+With --workload projections it instead times the two per-head projections of
+weight absorption at the same decode shape (128 query rows, 128 heads):
+mla_absorb_query (W_UK into the query) then mla_project_output (W_UV on the
+latent output), cycling over 8 distinct weight and activation sets (about 600
+MB) so that no step is served from the Infinity Cache. value = their
+algorithmic bytes (weights, inputs and outputs, each once) / step time.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -31,6 +38,8 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+from paged_mla_decode_amd import costs  # noqa: E402  (host arithmetic only)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
@@ -51,21 +60,22 @@ def kernel_source_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none for this workload or the kernels changed since."""
-    path = os.path.join(ROOT, "profiles", f"mla_decode_{workload}_counters.md")
+def measured_traffic(summary, key="traffic_bytes_per_launch"):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    profiles/<summary>_counters.md, or None when there is none or the kernels
+    changed since."""
+    path = os.path.join(ROOT, "profiles", f"{summary}_counters.md")
     if not os.path.exists(path):
         return None
     fields = {}
     with open(path) as fh:
         for line in fh:
-            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+            if ":" in line and line.split(":")[0] in (key, "kernel_source_sha256"):
                 k, v = line.split(":", 1)
                 fields[k] = v.strip()
     if fields.get("kernel_source_sha256") != kernel_source_sha256():
         return None
-    return int(fields["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in fields else None
+    return int(fields[key]) if key in fields else None
 
 
 def cpu_baseline(batch, target_s=12.0):
@@ -102,7 +112,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="v3", choices=["v3", "v2_lite", "skewed_fp8"])
+    ap.add_argument("--workload", default="v3",
+                    choices=["v3", "v2_lite", "skewed_fp8", "projections"])
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -112,6 +123,9 @@ def main():
               "(this build runs on a single MI355X; sharding is described, not built).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "projections":
+        return bench_projections(args)
 
     import torch
 
@@ -180,8 +194,9 @@ def main():
     launch_ms = np.array([a.elapsed_time(b) for a, b in events])
 
     tokens = int(batch.seq_lens.sum())
-    latent_bytes = tokens * batch.cache_bytes_per_token
-    flops = 2.0 * batch.num_heads * (576 + 512) * tokens
+    latent_bytes = costs.mla_decode_latent_bytes(tokens, 1 if batch.cache_dtype != "bf16" else 2)
+    assert latent_bytes == tokens * batch.cache_bytes_per_token
+    flops = float(costs.mla_decode_flops(tokens, batch.num_heads))
     ms_per_step = elapsed * 1e3 / args.steps
     gbs = latent_bytes / (ms_per_step * 1e-3) / 1e9
     launch_avg_ms = float(launch_ms.mean())
@@ -225,7 +240,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload),
+            "traffic": measured_traffic(f"mla_decode_{args.workload}"),
             "algorithmic_bytes_per_launch": latent_bytes,
             "launch_avg_us": round(launch_avg_ms * 1e3, 2),
             "mfma_tflops": round(flops / (launch_avg_ms * 1e-3) / 1e12, 1),
@@ -235,6 +250,148 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(batch)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_projections(p, target_s=10.0):
+    """Oracle absorb + project GB/s, repeated on the full shape for about target_s."""
+    import oracle
+    import threadpoolctl
+    import workloads
+
+    f = workloads.bf16_bits_to_f32
+    q, w_uk, w_uv, x = (f(a).astype(np.float64) for a in (p.q, p.w_uk, p.w_uv, p.x))
+    N, H, D = q.shape
+    nbytes = costs.absorb_bytes(N, H, D) + costs.project_bytes(N, H, D)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.absorb_query(q, w_uk)
+        oracle.project_output(x, w_uv)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    return {"value": reps * nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} repetitions of the full shape (N={N}, H={H}), fp64 numpy per-head "
+                      f"products, {dt:.1f} s"}
+
+
+def bench_projections(args):
+    import torch
+
+    import workloads
+    from paged_mla_decode_amd import absorb_query, project_output
+
+    dev = torch.device("cuda:0")
+    N, H, D, A, SETS = 128, 128, 128, 512, 8
+    p = workloads.projection_inputs(3, N, H, D)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = {"q": to_dev(p.q), "w_uk": to_dev(p.w_uk), "x": to_dev(p.x),
+            # W_UV with the latent contiguous, as kv_b_proj stores it: [H, D, A], viewed (a, h, d)
+            "w_uv_t": to_dev(np.ascontiguousarray(p.w_uv.transpose(1, 2, 0)))}
+    sets = []
+    for i in range(SETS):
+        s = {k: (v if i == 0 else v.clone()) for k, v in base.items()}
+        s["q_abs"] = torch.empty((N, H, A), dtype=torch.bfloat16, device=dev)
+        s["o"] = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+        sets.append(s)
+    stream = torch.cuda.current_stream(dev)
+
+    def absorb(i):
+        s = sets[i % SETS]
+        absorb_query(s["q"], s["w_uk"], out=s["q_abs"], stream=stream)
+
+    def project(i):
+        s = sets[i % SETS]
+        project_output(s["x"], s["w_uv_t"].permute(2, 0, 1), out=s["o"], stream=stream)
+
+    def step(i):
+        absorb(i)
+        project(i)
+
+    if args.copy_mb:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # Per-kernel launch duration: the two kernels are a few microseconds each, so
+    # events between them would cost as much as they measure. Each is timed
+    # instead over `steps` back-to-back launches on the same rotating sets, with
+    # one pair of HIP events on the launch stream around them.
+    def launch_avg_us(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    absorb_us = launch_avg_us(absorb)
+    project_us = launch_avg_us(project)
+
+    # Algorithmic bytes, each tensor once: weight + input + output of each projection.
+    absorb_bytes = costs.absorb_bytes(N, H, D, A)
+    project_bytes = costs.project_bytes(N, H, D, A)
+    step_bytes = absorb_bytes + project_bytes
+    ms_per_step = elapsed * 1e3 / args.steps
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    kern = {"absorb": (absorb_us, absorb_bytes, "head_gemm_kernel<64, 1> (mla_absorb_query)"),
+            "project": (project_us, project_bytes, "head_gemm_kernel<64, 4> (mla_project_output)")}
+    dom = max(kern, key=lambda k: kern[k][0])
+    us, nbytes, kname = kern[dom]
+    achieved = nbytes / (us * 1e-6) / 1e9
+    log(f"step {ms_per_step * 1e3:.2f} us; absorb {absorb_us:.2f} us "
+        f"({absorb_bytes / absorb_us / 1e3:.0f} GB/s), project {project_us:.2f} us "
+        f"({project_bytes / project_us / 1e3:.0f} GB/s)")
+    res = {
+        "metric": "W_UK absorption + W_UV projection GB/s (% of HBM peak), DeepSeek-V3 decode shape",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"projections: N={N} query rows, H={H} heads, head_dim {D}, latent {A}, "
+                               f"bf16, {SETS} rotating weight sets, seed 3",
+                   "query_rows": N, "num_heads": H, "head_dim": D, "kv_lora_rank": A,
+                   "parallelism": "single GPU"},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "kernels_us": {"absorb": round(absorb_us, 2), "project": round(project_us, 2)},
+        "roofline": {
+            "kernel": kname,
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("mla_projections_v3", f"traffic_bytes_per_launch_{dom}"),
+            "algorithmic_bytes_per_launch": nbytes,
+            "launch_avg_us": round(us, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline_projections(p)
     print(json.dumps(res), flush=True)
 
 
