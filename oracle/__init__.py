@@ -8,6 +8,9 @@ Python binding never import it, and it imports neither of them.
 * ``merge_states``: the two-state log-sum-exp merge (``mla_oracle.c``).
 * ``absorb_query`` / ``project_output``: the per-head W_UK and W_UV products on
   either side of the latent attention (numpy matrix products in float64).
+* ``e4m3fn_encode`` / ``append_then_decode``: the fused KV-cache update, written
+  as what it must equal: store the new token's row (bf16, or e4m3fn codes
+  chosen as the nearest code to value / scale), then decode.
 * ``tree_suffix_compact``: the pre-PR definition of the suffix page table from
   section 1 of the SGLang PR 49477 analysis: sort the keys "column if visible,
   column + W if not" with a stable sort, gather the draft slots in that order,
@@ -137,6 +140,61 @@ def decode_batch(batch):
     return mla_decode(batch.q_nope, batch.q_rope, batch.cache, batch.kv_indptr, batch.kv_indices,
                       batch.page_size, batch.sm_scale, kv_last_page_len=batch.kv_last_page_len,
                       qo_indptr=batch.qo_indptr, kv_scale=batch.kv_scale)
+
+
+def e4m3fn_encode(x) -> np.ndarray:
+    """Nearest OCP e4m3fn code to each value, ties to the code with an even
+    mantissa (round to nearest even), by direct search over the decoded values
+    of the 127 non-negative finite codes. Values must be finite with
+    |x| <= 448; the sign bit of x (including -0.0) becomes the code's sign."""
+    x = np.asarray(x, dtype=np.float64)
+    assert np.isfinite(x).all() and (np.abs(x) <= 448.0).all()
+    codes = np.arange(0x7F, dtype=np.uint8)  # 0x00 .. 0x7E, ascending in value
+    vals = e4m3fn_to_double(codes)
+    a = np.abs(x).ravel()
+    hi = np.minimum(np.searchsorted(vals, a, side="left"), 0x7E)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    pick = np.where(d_hi < d_lo, hi, lo)
+    tie = (d_hi == d_lo) & (hi != lo)
+    pick = np.where(tie, np.where(hi % 2 == 0, hi, lo), pick)
+    pick = np.where(a == vals[hi], hi, pick)
+    sign = np.signbit(x).ravel().astype(np.uint8) << 7
+    return (pick.astype(np.uint8) | sign).reshape(x.shape)
+
+
+def append_then_decode(q_nope, q_rope, cache, kv_indptr, kv_indices, kv_last_page_len, page_size,
+                       sm_scale, c_new, k_pe_new, kv_scale=1.0):
+    """The fused append (sglang-jax MLA gap page, section 2.4: the kernel
+    updates the cache with the new token; section 3.1: latent and rope parts
+    written separately) as its definition: each request b (one query row per
+    request) stores its new token at position L_b - 1, where L_b counts it,
+    then attends over all L_b tokens. For a bf16 cache the row is the bf16
+    inputs; for an e4m3fn cache each value is v / kv_scale (a float32
+    division), clamped to +-448 and encoded by ``e4m3fn_encode``.
+
+    ``c_new`` [B, 512] and ``k_pe_new`` [B, 64] are bf16 bit patterns. Returns
+    (out, lse, cache_after) with cache_after a new array."""
+    cache = np.array(cache, copy=True)
+    kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
+    kv_indices = np.asarray(kv_indices, dtype=np.int64)
+    last = np.asarray(kv_last_page_len, dtype=np.int64)
+    B = len(kv_indptr) - 1
+    npages = kv_indptr[1:] - kv_indptr[:-1]
+    lens = np.where(npages > 0, (npages - 1) * page_size + last, 0)
+    assert (lens >= 1).all(), "every request holds its new token"
+    row_bits = np.concatenate([np.asarray(c_new, np.uint16), np.asarray(k_pe_new, np.uint16)], axis=1)
+    for b in range(B):
+        tok = int(lens[b]) - 1
+        page = int(kv_indices[kv_indptr[b] + tok // page_size])
+        if cache.dtype == np.uint16:
+            cache[page, tok % page_size, :] = row_bits[b]
+        else:
+            v = bf16_to_double(row_bits[b]).astype(np.float32) / np.float32(kv_scale)
+            cache[page, tok % page_size, :] = e4m3fn_encode(np.clip(v, -448.0, 448.0))
+    out, lse = mla_decode(q_nope, q_rope, cache, kv_indptr, kv_indices, page_size, sm_scale,
+                          kv_last_page_len=last, kv_scale=kv_scale)
+    return out, lse, cache
 
 
 def absorb_query(q_nope, w_uk):

@@ -338,3 +338,94 @@ def test_projections_brute_force_and_gram_identity():
     for h in range(H):
         gram = w[:, h, :].T @ w[:, h, :]
         np.testing.assert_allclose(back[:, h, :], q[:, h, :] @ gram, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Fused KV append (sglang-jax MLA gap page, sections 2.4 and 3.1). The encoder
+# against torch's float8_e4m3fn cast (a library routine, round to nearest
+# even) on every tie between neighbouring codes, every code value and random
+# values; the append against closed forms and an invariance.
+# ---------------------------------------------------------------------------
+
+def _torch_e4m3fn(x32):
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3fn_encoder_matches_torch_on_ties_codes_and_random_values():
+    vals = oracle.e4m3fn_to_double(np.arange(0x7F, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2  # exact in float32: few significant bits
+    rng = np.random.Generator(np.random.PCG64(21))
+    rand = np.exp(rng.uniform(np.log(2.0 ** -13), np.log(448.0), size=200_000))
+    x = np.concatenate([vals, mids, rand, [0.0, 448.0]]).astype(np.float32)
+    x = np.concatenate([x, -x])
+    assert np.array_equal(oracle.e4m3fn_encode(x), _torch_e4m3fn(x))
+    # Ties go to the even code: the midpoint of 0x01 and 0x02 is 0x02, of 0x02 and 0x03 is 0x02.
+    assert oracle.e4m3fn_encode(np.float32(1.5 * 2.0 ** -9)) == 0x02
+    assert oracle.e4m3fn_encode(np.float32(2.5 * 2.0 ** -9)) == 0x02
+    assert oracle.e4m3fn_encode(np.float32(-0.0)) == 0x80
+
+
+def test_e4m3fn_encode_decode_round_trip_all_finite_codes():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    back = oracle.e4m3fn_encode(oracle.e4m3fn_to_double(codes))
+    # 0x80 (-0.0) decodes to -0.0 and comes back as 0x80.
+    assert np.array_equal(back, codes)
+
+
+def _last_rows(batch):
+    """Latent and rope bits of each request's last token, gathered by numpy."""
+    c, r = [], []
+    for b in range(batch.batch):
+        t = int(batch.seq_lens[b]) - 1
+        page = batch.kv_indices[batch.kv_indptr[b] + t // batch.page_size]
+        row = batch.cache[page, t % batch.page_size]
+        c.append(row[:512])
+        r.append(row[512:])
+    return np.stack(c), np.stack(r)
+
+
+def _append(batch, c_new, k_pe_new):
+    return oracle.append_then_decode(batch.q_nope, batch.q_rope, batch.cache, batch.kv_indptr,
+                                     batch.kv_indices, batch.kv_last_page_len, batch.page_size,
+                                     batch.sm_scale, c_new, k_pe_new, batch.kv_scale)
+
+
+def test_append_of_the_stored_row_changes_nothing():
+    batch = workloads.random_decode_batch(31, [1, 5, 64, 65, 130], num_heads=16, page_size=16)
+    c, r = _last_rows(batch)
+    out, lse, cache = _append(batch, c, r)
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    assert np.array_equal(cache, batch.cache)
+    assert np.array_equal(out, ref_out) and np.array_equal(lse, ref_lse)
+
+
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8_e4m3fn"])
+def test_append_single_token_requests_return_the_new_row(cache_dtype):
+    """L = 1: the softmax has one token, so out is the new latent as stored and
+    lse its score. Only the new rows change in the cache."""
+    batch = workloads.random_decode_batch(32, [1, 1, 1], num_heads=16, page_size=4,
+                                          cache_dtype=cache_dtype)
+    rng = np.random.Generator(np.random.PCG64(33))
+    c = workloads.f32_to_bf16_bits(rng.standard_normal((3, 512), dtype=np.float32))
+    r = workloads.f32_to_bf16_bits(rng.standard_normal((3, 64), dtype=np.float32))
+    c[0, 0] = workloads.f32_to_bf16_bits(np.array([1e4], np.float32))[0]  # clamped to 448 in fp8
+    out, lse, cache = _append(batch, c, r)
+    row = np.concatenate([c, r], axis=1)
+    vals = oracle.bf16_to_double(row)
+    if cache_dtype == "fp8_e4m3fn":
+        s = np.float32(batch.kv_scale)
+        codes = _torch_e4m3fn(np.clip(vals.astype(np.float32) / s, -448, 448))
+        vals = oracle.e4m3fn_to_double(codes) * batch.kv_scale
+        assert codes[0, 0] == 0x7E
+    qn, qr = _q(batch)
+    for b in range(3):
+        page = batch.kv_indices[batch.kv_indptr[b]]
+        stored = cache[page, 0]
+        expect = row[b] if cache_dtype == "bf16" else codes[b]
+        assert np.array_equal(stored, expect)
+        np.testing.assert_allclose(out[b], np.broadcast_to(vals[b, :512], (16, 512)), rtol=0, atol=1e-12)
+        score = (qn[b] @ vals[b, :512] + qr[b] @ vals[b, 512:]) * SM_SCALE
+        np.testing.assert_allclose(lse[b], score, rtol=1e-12, atol=1e-12)
+    changed = np.nonzero((cache != batch.cache).any(axis=-1).ravel())[0]
+    assert set(changed) <= {int(batch.kv_indices[batch.kv_indptr[b]]) * 4 for b in range(3)}
