@@ -73,7 +73,7 @@ const char* mla_status_string(int32_t status);
  * of the device workspace. It is plain data: tests may read it.
  */
 #define MLA_PLAN_MAGIC 0x504C4D41u /* "AMLP" */
-#define MLA_PLAN_VERSION 2
+#define MLA_PLAN_VERSION 3
 
 typedef struct {
     uint32_t magic;
@@ -108,8 +108,12 @@ typedef struct {
     int32_t kv_end;    /* one past the last token (the request's length for the last chunk) */
     int32_t partial;   /* -1: write out/lse directly; else the partial slot */
     int32_t head_begin;
-    int32_t num_heads;
+    uint32_t flags;    /* MLA_ITEM_* bits */
 } mla_work_item;
+
+/* The item's chunk ends at its request's planned length (kv_end == L >= 1): the
+   item that reads the request's last token, which mla_decode_append writes. */
+#define MLA_ITEM_LAST_CHUNK 1u
 
 typedef struct {
     int32_t row;           /* query row n */
@@ -199,6 +203,43 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
                    int64_t q_rope_stride_h, const void* kv_cache_d, float kv_scale,
                    const int32_t* kv_indices_d, const int32_t* kv_lens_d, float sm_scale,
                    void* out_d, float* lse_d, void* stream);
+
+/*
+ * mla_decode_append - mla_decode with the new token's cache row written in the
+ * same launch (the fused KV-cache update of the tpu-inference V2 MLA kernel,
+ * sglang-jax MLA gap page, section 2.4; the nope and rope parts are written
+ * separately as the MLA token pool's set_mla_kv_buffer does, section 3.1).
+ *
+ * Each request b has exactly one query row n (qo_indptr was NULL or the
+ * identity) and a planned length L_b >= 1 that already counts the new token.
+ * Before any of its tokens is read, the row of token L_b - 1 (page
+ * kv_indices[kv_indptr[b] + (L_b-1)/page_size], in-page row (L_b-1) % page_size)
+ * becomes
+ *   latent = c_new[n, 0:512], rope = k_pe_new[n, 0:64]        (bf16 cache), or
+ *   code(v) = e4m3fn_rne(clamp(v / kv_scale, -448, 448))      (fp8 cache),
+ * with v / kv_scale an IEEE fp32 division and e4m3fn_rne the round-to-nearest-
+ * even OCP e4m3fn encoding. The attention then runs as mla_decode over all
+ * L_b tokens, the new one read back from the cache as stored. The result is
+ * that of writing the row first and calling mla_decode, without a separate
+ * launch or a read of the row through another kernel.
+ *
+ *   kv_cache_d   as for mla_decode, but written: only the L_b - 1 row of each
+ *                request changes.
+ *   c_new_d      bf16 [N, 512], row n at n*c_new_stride (elements, multiple of 8);
+ *                16-byte aligned. Finite values.
+ *   k_pe_new_d   bf16 [N, 64], row n at n*k_pe_new_stride, same conventions
+ *                (a concatenated [N, 576] row is c_new_d with k_pe_new_d = c_new_d + 512).
+ *   kv_lens_d    not taken: the planned lengths are the lengths.
+ * Other arguments as for mla_decode. Returns those of mla_decode, and
+ * MLA_ERR_INVALID_ARG when a request has no token or more than one query row.
+ */
+int32_t mla_decode_append(const mla_decode_params* params, const void* plan_h,
+                          const void* workspace_d, size_t workspace_bytes, const void* q_nope_d,
+                          int64_t q_nope_stride_n, int64_t q_nope_stride_h, const void* q_rope_d,
+                          int64_t q_rope_stride_n, int64_t q_rope_stride_h, void* kv_cache_d,
+                          float kv_scale, const int32_t* kv_indices_d, const void* c_new_d,
+                          int64_t c_new_stride, const void* k_pe_new_d, int64_t k_pe_new_stride,
+                          float sm_scale, void* out_d, float* lse_d, void* stream);
 
 /*
  * mla_merge_states - merge two attention states over disjoint token sets:

@@ -8,8 +8,8 @@ management with torch allocations.
 from ._binding import (  # noqa: F401
     EXPORTED_SYMBOLS, LIB_PATH, MLA_DTYPE_BF16, MLA_DTYPE_FP8_E4M3FN, MLA_DTYPE_FP32,
     MLA_ERR_HIP, MLA_ERR_INVALID_ARG, MLA_ERR_PLAN_MISMATCH, MLA_ERR_UNSUPPORTED,
-    MLA_ERR_WORKSPACE_TOO_SMALL, MLA_OK, MlaError, make_params, mla_absorb_query, mla_decode,
-    mla_decode_plan, mla_decode_variant, mla_decode_workspace_size, mla_merge_states,
+    MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ITEM_LAST_CHUNK, MLA_OK, MlaError, make_params,
+    mla_absorb_query, mla_decode, mla_decode_append, mla_decode_plan, mla_decode_variant, mla_decode_workspace_size, mla_merge_states,
     mla_project_output, mla_status_string, mla_tree_suffix_compact, read_plan)
 
 

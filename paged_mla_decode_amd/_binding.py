@@ -41,7 +41,8 @@ MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP32 = 1
 MLA_DTYPE_FP8_E4M3FN = 2
 MLA_PLAN_MAGIC = 0x504C4D41
-MLA_PLAN_VERSION = 2
+MLA_PLAN_VERSION = 3
+MLA_ITEM_LAST_CHUNK = 1
 
 
 class mla_decode_params(ctypes.Structure):
@@ -68,8 +69,8 @@ class mla_plan_header(ctypes.Structure):
 
 class mla_work_item(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("row", "request", "page_base", "kv_begin", "kv_end", "partial", "head_begin",
-                 "num_heads")]
+                ("row", "request", "page_base", "kv_begin", "kv_end", "partial", "head_begin")] + \
+        [("flags", ctypes.c_uint32)]
 
 
 class mla_merge_item(ctypes.Structure):
@@ -92,6 +93,9 @@ _lib.mla_decode_plan.argtypes = [_PARAMS, _i32, _p, _p, _p, _p, _sz, _p, _sz, _p
 _lib.mla_decode.restype = _i32
 _lib.mla_decode.argtypes = [_PARAMS, _p, _p, _sz, _p, _i64, _i64, _p, _i64, _i64, _p, _f32, _p,
                             _p, _f32, _p, _p, _p]
+_lib.mla_decode_append.restype = _i32
+_lib.mla_decode_append.argtypes = [_PARAMS, _p, _p, _sz, _p, _i64, _i64, _p, _i64, _i64, _p, _f32,
+                                   _p, _p, _i64, _p, _i64, _f32, _p, _p, _p]
 _lib.mla_merge_states.restype = _i32
 _lib.mla_merge_states.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _p]
 _lib.mla_tree_suffix_compact.restype = _i32
@@ -102,7 +106,7 @@ for _fn in (_lib.mla_absorb_query, _lib.mla_project_output):
     _fn.argtypes = [_p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i32, _i32, _i32, _p]
 
 EXPORTED_SYMBOLS = ("mla_status_string", "mla_decode_variant", "mla_decode_workspace_size",
-                    "mla_decode_plan", "mla_decode", "mla_merge_states",
+                    "mla_decode_plan", "mla_decode", "mla_decode_append", "mla_merge_states",
                     "mla_tree_suffix_compact", "mla_absorb_query", "mla_project_output")
 
 
@@ -187,6 +191,19 @@ def mla_decode(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_st
                            int(q_rope_stride_h), _ptr(kv_cache_d), float(kv_scale),
                            _ptr(kv_indices_d), _ptr(kv_lens_d), float(sm_scale), _ptr(out_d),
                            _ptr(lse_d), _stream(stream))
+
+
+def mla_decode_append(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_stride_n,
+                      q_nope_stride_h, q_rope_d, q_rope_stride_n, q_rope_stride_h, kv_cache_d,
+                      kv_scale, kv_indices_d, c_new_d, c_new_stride, k_pe_new_d, k_pe_new_stride,
+                      sm_scale, out_d, lse_d, stream=None):
+    return _lib.mla_decode_append(ctypes.byref(params), _ptr(plan_h), _ptr(workspace_d),
+                                  int(workspace_bytes), _ptr(q_nope_d), int(q_nope_stride_n),
+                                  int(q_nope_stride_h), _ptr(q_rope_d), int(q_rope_stride_n),
+                                  int(q_rope_stride_h), _ptr(kv_cache_d), float(kv_scale),
+                                  _ptr(kv_indices_d), _ptr(c_new_d), int(c_new_stride),
+                                  _ptr(k_pe_new_d), int(k_pe_new_stride), float(sm_scale),
+                                  _ptr(out_d), _ptr(lse_d), _stream(stream))
 
 
 def mla_merge_states(v_a_d, s_a_d, v_b_d, s_b_d, v_out_d, s_out_d, num_rows, head_dim, v_dtype,

@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "mla_decode.h"
 #include "mla_internal.h"
@@ -91,12 +92,41 @@ int32_t mla_decode_plan(const mla_decode_params* params, int32_t batch, const in
     return MLA_OK;
 }
 
-int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const void* workspace_d,
-                   size_t workspace_bytes, const void* q_nope_d, int64_t q_nope_stride_n,
-                   int64_t q_nope_stride_h, const void* q_rope_d, int64_t q_rope_stride_n,
-                   int64_t q_rope_stride_h, const void* kv_cache_d, float kv_scale,
-                   const int32_t* kv_indices_d, const int32_t* kv_lens_d, float sm_scale,
-                   void* out_d, float* lse_d, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The new-token inputs of mla_decode_append.
+struct AppendIn {
+    const void* c_new;
+    int64_t c_new_stride;
+    const void* k_pe_new;
+    int64_t k_pe_new_stride;
+};
+
+// Every request has exactly one query row and a last-chunk item (length >= 1).
+bool append_batch_ok(const mla_plan_header* h, const void* plan_h) {
+    if (h->num_rows != h->batch) return false;
+    const mla_work_item* items =
+        reinterpret_cast<const mla_work_item*>(static_cast<const char*>(plan_h) + h->items_offset);
+    std::vector<char> seen((size_t)h->batch, 0);
+    int32_t n = 0;
+    for (int32_t i = 0; i < h->num_items; ++i) {
+        if (!(items[i].flags & MLA_ITEM_LAST_CHUNK)) continue;
+        const int32_t b = items[i].request;
+        if (b < 0 || b >= h->batch || seen[(size_t)b]) return false;
+        seen[(size_t)b] = 1;
+        ++n;
+    }
+    return n == h->batch;
+}
+
+int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const void* workspace_d,
+                    size_t workspace_bytes, const void* q_nope_d, int64_t q_nope_stride_n,
+                    int64_t q_nope_stride_h, const void* q_rope_d, int64_t q_rope_stride_n,
+                    int64_t q_rope_stride_h, const void* kv_cache_d, float kv_scale,
+                    const int32_t* kv_indices_d, const int32_t* kv_lens_d, const AppendIn* app,
+                    float sm_scale, void* out_d, float* lse_d, void* stream) {
     if (!params || !plan_h || !workspace_d) return MLA_ERR_INVALID_ARG;
     Variant v;
     if (!select_variant(params, &v)) return MLA_ERR_UNSUPPORTED;
@@ -117,6 +147,13 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
     if (!std::isfinite(sm_scale) || sm_scale <= 0.f || !std::isfinite(kv_scale) || kv_scale <= 0.f)
         return MLA_ERR_INVALID_ARG;
     if (params->kv_dtype == MLA_DTYPE_BF16 && kv_scale != 1.f) return MLA_ERR_INVALID_ARG;
+    if (app) {
+        if (!app->c_new || !app->k_pe_new || !aligned16(app->c_new) || !aligned16(app->k_pe_new) ||
+            app->c_new_stride < 0 || app->k_pe_new_stride < 0 ||
+            (app->c_new_stride | app->k_pe_new_stride) % 8 != 0)
+            return MLA_ERR_INVALID_ARG;
+        if (!append_batch_ok(h, plan_h)) return MLA_ERR_INVALID_ARG;
+    }
 
     const char* ws = static_cast<const char*>(workspace_d);
     DecodeArgs a{};
@@ -143,6 +180,14 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
         if (params->page_size == (1 << b)) a.page_shift = b;
     a.scale_log2 = (float)((double)sm_scale * (double)kv_scale * 1.4426950408889634);
     a.out_scale = kv_scale;
+    if (app) {
+        a.c_new = static_cast<const uint16_t*>(app->c_new);
+        a.c_new_sn = app->c_new_stride;
+        a.k_pe_new = static_cast<const uint16_t*>(app->k_pe_new);
+        a.k_pe_new_sn = app->k_pe_new_stride;
+        a.cache_w = static_cast<uint8_t*>(const_cast<void*>(kv_cache_d));
+        a.kv_scale = kv_scale;
+    }
     int err = launch_decode(v, params->kv_dtype, params->out_dtype, a, h->num_workers, stream);
     if (err != 0) return MLA_ERR_HIP;
     if (h->num_merges > 0) {
@@ -162,6 +207,34 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
         if (err != 0) return MLA_ERR_HIP;
     }
     return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const void* workspace_d,
+                   size_t workspace_bytes, const void* q_nope_d, int64_t q_nope_stride_n,
+                   int64_t q_nope_stride_h, const void* q_rope_d, int64_t q_rope_stride_n,
+                   int64_t q_rope_stride_h, const void* kv_cache_d, float kv_scale,
+                   const int32_t* kv_indices_d, const int32_t* kv_lens_d, float sm_scale,
+                   void* out_d, float* lse_d, void* stream) {
+    return decode_impl(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_stride_n,
+                       q_nope_stride_h, q_rope_d, q_rope_stride_n, q_rope_stride_h, kv_cache_d,
+                       kv_scale, kv_indices_d, kv_lens_d, nullptr, sm_scale, out_d, lse_d, stream);
+}
+
+int32_t mla_decode_append(const mla_decode_params* params, const void* plan_h,
+                          const void* workspace_d, size_t workspace_bytes, const void* q_nope_d,
+                          int64_t q_nope_stride_n, int64_t q_nope_stride_h, const void* q_rope_d,
+                          int64_t q_rope_stride_n, int64_t q_rope_stride_h, void* kv_cache_d,
+                          float kv_scale, const int32_t* kv_indices_d, const void* c_new_d,
+                          int64_t c_new_stride, const void* k_pe_new_d, int64_t k_pe_new_stride,
+                          float sm_scale, void* out_d, float* lse_d, void* stream) {
+    const AppendIn app{c_new_d, c_new_stride, k_pe_new_d, k_pe_new_stride};
+    return decode_impl(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_stride_n,
+                       q_nope_stride_h, q_rope_d, q_rope_stride_n, q_rope_stride_h, kv_cache_d,
+                       kv_scale, kv_indices_d, nullptr, &app, sm_scale, out_d, lse_d, stream);
 }
 
 int32_t mla_merge_states(const void* v_a_d, const float* s_a_d, const void* v_b_d,

@@ -37,6 +37,7 @@
 
 #include <type_traits>
 
+#include "mla_append.h"
 #include "mla_device.h"
 #include "mla_internal.h"
 #include "mla_tile_layout.h"
@@ -62,7 +63,7 @@ __device__ __forceinline__ void settle_o(f32x16 (&O)[4][4]) {
                    "+a"(O[3][0]), "+a"(O[3][1]), "+a"(O[3][2]), "+a"(O[3][3]));
 }
 
-template <bool KV8, bool OUT32>
+template <bool KV8, bool OUT32, bool APPEND>
 __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
     constexpr int HS = 4;
     using L = H128Layout<KV8>;
@@ -162,6 +163,13 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         // out behind them, so the latencies of the two overlap.
         prologue_idx();
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the page indices
+        if (APPEND && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
+            // Fused append: the request's new row goes to the cache before any
+            // wave loads a tile that holds it.
+            append_row<KV8>(a, it, tid, 256);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the row's stores are done
+            __syncthreads();
+        }
         if (ntiles > 0) start_tiles();
 
         // ---- absorbed query -> registers ----
@@ -506,14 +514,21 @@ int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num
     const dim3 grid(num_workers), block(256);
     const bool kv8 = kv_dtype == MLA_DTYPE_FP8_E4M3FN;
     const bool o32 = out_dtype == MLA_DTYPE_FP32;
+    // The fused append is its own instantiation, so the plain decode carries
+    // none of its arguments or branches.
+    const bool app = a.c_new != nullptr;
     if (kv8 && o32)
-        decode_h128_kernel<true, true><<<grid, block, 0, s>>>(a);
+        app ? decode_h128_kernel<true, true, true><<<grid, block, 0, s>>>(a)
+            : decode_h128_kernel<true, true, false><<<grid, block, 0, s>>>(a);
     else if (kv8)
-        decode_h128_kernel<true, false><<<grid, block, 0, s>>>(a);
+        app ? decode_h128_kernel<true, false, true><<<grid, block, 0, s>>>(a)
+            : decode_h128_kernel<true, false, false><<<grid, block, 0, s>>>(a);
     else if (o32)
-        decode_h128_kernel<false, true><<<grid, block, 0, s>>>(a);
+        app ? decode_h128_kernel<false, true, true><<<grid, block, 0, s>>>(a)
+            : decode_h128_kernel<false, true, false><<<grid, block, 0, s>>>(a);
     else
-        decode_h128_kernel<false, false><<<grid, block, 0, s>>>(a);
+        app ? decode_h128_kernel<false, false, true><<<grid, block, 0, s>>>(a)
+            : decode_h128_kernel<false, false, false><<<grid, block, 0, s>>>(a);
     return (int)hipGetLastError();
 }
 

@@ -55,6 +55,15 @@ struct DecodeArgs {
     int32_t page_shift;  // log2(page_size) when it is a power of two, else -1
     float scale_log2;    // sm_scale * kv_scale * log2(e)
     float out_scale;   // kv_scale (fp8 cache) or 1
+    // Fused append (null c_new: none). The item flagged MLA_ITEM_LAST_CHUNK writes
+    // its request's row L-1 from c_new/k_pe_new (bf16, row it.row) into cache_w
+    // (the same memory as cache) before any of its tile loads.
+    const uint16_t* c_new;
+    int64_t c_new_sn;
+    const uint16_t* k_pe_new;
+    int64_t k_pe_new_sn;
+    uint8_t* cache_w;
+    float kv_scale;  // fp8 encoding divides by it
 };
 
 struct MergePartialsArgs {

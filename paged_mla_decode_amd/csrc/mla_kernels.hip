@@ -30,6 +30,7 @@
 
 #include <type_traits>
 
+#include "mla_append.h"
 #include "mla_device.h"
 #include "mla_internal.h"
 #include "mla_tile_layout.h"
@@ -41,7 +42,7 @@ using namespace dev;
 // ---------------------------------------------------------------------------
 // The decode kernel
 // ---------------------------------------------------------------------------
-template <int HW, int HS, bool KV8, bool OUT32>
+template <int HW, int HS, bool KV8, bool OUT32, bool APPEND>
 __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
     using L = TileLayout<KV8>;
     using SA = ScoreAddr<HW, KV8>;
@@ -92,6 +93,13 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
             // see the tile loads, so its own waits for these registers inside the
             // loop would otherwise also drain the tiles in flight.
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
+        if (APPEND && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
+            // Fused append: the request's new row goes to the cache before any
+            // wave loads a tile that holds it.
+            append_row<KV8>(a, it, threadIdx.x, 64 * HS);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the row's stores are done
+            __syncthreads();
         }
 
         // ---- per-lane LDS bases (see mla_tile_layout.h) ----
@@ -612,14 +620,19 @@ static int launch_decode_hs(int kv_dtype, int out_dtype, const DecodeArgs& a, in
     const dim3 grid(n), block(64 * HS);
     const bool kv8 = kv_dtype == MLA_DTYPE_FP8_E4M3FN;
     const bool o32 = out_dtype == MLA_DTYPE_FP32;
+    const bool app = a.c_new != nullptr;  // the fused append: its own instantiation
     if (kv8 && o32)
-        decode_kernel<HW, HS, true, true><<<grid, block, 0, s>>>(a);
+        app ? decode_kernel<HW, HS, true, true, true><<<grid, block, 0, s>>>(a)
+            : decode_kernel<HW, HS, true, true, false><<<grid, block, 0, s>>>(a);
     else if (kv8)
-        decode_kernel<HW, HS, true, false><<<grid, block, 0, s>>>(a);
+        app ? decode_kernel<HW, HS, true, false, true><<<grid, block, 0, s>>>(a)
+            : decode_kernel<HW, HS, true, false, false><<<grid, block, 0, s>>>(a);
     else if (o32)
-        decode_kernel<HW, HS, false, true><<<grid, block, 0, s>>>(a);
+        app ? decode_kernel<HW, HS, false, true, true><<<grid, block, 0, s>>>(a)
+            : decode_kernel<HW, HS, false, true, false><<<grid, block, 0, s>>>(a);
     else
-        decode_kernel<HW, HS, false, false><<<grid, block, 0, s>>>(a);
+        app ? decode_kernel<HW, HS, false, false, true><<<grid, block, 0, s>>>(a)
+            : decode_kernel<HW, HS, false, false, false><<<grid, block, 0, s>>>(a);
     return (int)hipGetLastError();
 }
 

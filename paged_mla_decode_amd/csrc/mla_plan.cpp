@@ -240,7 +240,7 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
         it.kv_end = (int32_t)std::min<int64_t>(r.len, pc.t1 * kTile);
         it.partial = npieces[pc.row_index] > 1 ? next_slot[pc.row_index]++ : -1;
         it.head_begin = 0;
-        it.num_heads = p->num_heads;
+        it.flags = (r.len > 0 && it.kv_end == r.len) ? MLA_ITEM_LAST_CHUNK : 0u;
         items.push_back(it);
     }
     worker_begin.push_back((int32_t)items.size());

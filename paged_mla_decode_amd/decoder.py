@@ -78,6 +78,31 @@ class PagedMlaDecoder:
         return out, lse
 
 
+    def run_append(self, q_nope, q_rope, kv_cache, kv_indices, c_new, k_pe_new, sm_scale,
+                   kv_scale=1.0, out=None, lse=None, stream=None):
+        """``run`` with each request's new token written into its cache row L-1
+        first, in the same launch (mla_decode_append). c_new [N, 512] and
+        k_pe_new [N, 64] bf16, unit last stride; one query row per request."""
+        h = self.header()
+        N, H = h.num_rows, self.num_heads
+        if out is None:
+            dt = torch.float32 if self.out_dtype == "fp32" else torch.bfloat16
+            out = torch.empty((N, H, 512), dtype=dt, device=self.device)
+        if lse is None:
+            lse = torch.empty((N, H), dtype=torch.float32, device=self.device)
+        assert q_nope.stride(-1) == 1 and q_rope.stride(-1) == 1
+        assert c_new.stride(-1) == 1 and k_pe_new.stride(-1) == 1
+        stream = stream or torch.cuda.current_stream(self.device)
+        st = B.mla_decode_append(self.params, self.plan_h, self.workspace, self.workspace.numel(),
+                                 q_nope, q_nope.stride(0), q_nope.stride(1), q_rope,
+                                 q_rope.stride(0), q_rope.stride(1), kv_cache, kv_scale,
+                                 kv_indices, c_new, c_new.stride(0), k_pe_new, k_pe_new.stride(0),
+                                 sm_scale, out, lse, stream)
+        if st != B.MLA_OK:
+            raise B.MlaError("mla_decode_append", st)
+        return out, lse
+
+
 def merge_states(v_a, s_a, v_b, s_b, out=None, s_out=None, stream=None):
     """LSE merge of two states (bf16 or fp32 v of shape [..., D], fp32 s of shape [...])."""
     assert v_a.dtype == v_b.dtype and v_a.shape == v_b.shape

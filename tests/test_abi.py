@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     lib = ctypes.CDLL(m.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -152,6 +152,38 @@ def test_decode_validates_before_launch():
     bad = plan.copy()
     bad[:4] = 0
     assert call(plan_h=bad) == m.MLA_ERR_INVALID_ARG
+
+
+def test_decode_append_validates_before_launch():
+    """Every check runs on the host; the fake device pointers are never touched."""
+    p = m.make_params(16, 1, num_cus=256)
+
+    def call(plan, **over):
+        h = m.read_plan(plan)[0]
+        args = dict(params=p, plan_h=plan, workspace_d=FAKE, workspace_bytes=h.workspace_bytes,
+                    q_nope_d=FAKE, q_nope_stride_n=16 * 512, q_nope_stride_h=512, q_rope_d=FAKE,
+                    q_rope_stride_n=16 * 64, q_rope_stride_h=64, kv_cache_d=FAKE, kv_scale=1.0,
+                    kv_indices_d=FAKE, c_new_d=FAKE, c_new_stride=576, k_pe_new_d=FAKE + 1024,
+                    k_pe_new_stride=576, sm_scale=0.1, out_d=FAKE, lse_d=None, stream=0)
+        args.update(over)
+        return m.mla_decode_append(**args)
+
+    st, empty_req = _plan(p, [0, 0, 5])  # request 0 has no token to hold the new one
+    assert st == m.MLA_OK
+    assert call(empty_req) == m.MLA_ERR_INVALID_ARG
+    st, good = _plan(p, [0, 3, 8])
+    assert st == m.MLA_OK
+    assert call(good, c_new_d=None) == m.MLA_ERR_INVALID_ARG
+    assert call(good, k_pe_new_d=FAKE + 8) == m.MLA_ERR_INVALID_ARG
+    assert call(good, c_new_stride=570) == m.MLA_ERR_INVALID_ARG
+    assert call(good, k_pe_new_stride=-8) == m.MLA_ERR_INVALID_ARG
+    assert call(good, sm_scale=0.0) == m.MLA_ERR_INVALID_ARG
+    # Two query rows on one request: one new token per request is not defined.
+    pb, _ = m.mla_decode_workspace_size(p, 2, 3)
+    plan2 = np.zeros(pb, dtype=np.uint8)
+    assert m.mla_decode_plan(p, 2, np.array([0, 2, 3], np.int32), np.array([0, 3, 8], np.int32),
+                             None, plan2, pb) == m.MLA_OK
+    assert call(plan2) == m.MLA_ERR_INVALID_ARG
 
 
 def test_merge_and_compact_validate():

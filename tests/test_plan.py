@@ -46,7 +46,10 @@ def check_invariants(p, batch, h, items, merges, workers):
         assert it.page_base == batch.kv_indptr[it.request]
         assert 0 <= it.kv_begin <= it.kv_end <= lens[it.row]
         assert it.kv_begin % TILE == 0
-        assert it.head_begin == 0 and it.num_heads == p.num_heads
+        assert it.head_begin == 0
+        # The last-chunk flag marks exactly the item that ends at a non-empty row's length.
+        assert bool(it.flags & m.MLA_ITEM_LAST_CHUNK) == (lens[it.row] > 0 and it.kv_end == lens[it.row])
+        assert it.flags & ~m.MLA_ITEM_LAST_CHUNK == 0
         covered.setdefault(it.row, []).append((it.kv_begin, it.kv_end))
         if it.partial >= 0:
             assert it.partial not in partial_of
