@@ -114,6 +114,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="v3",
                     choices=["v3", "v2_lite", "skewed_fp8", "projections"])
+    ap.add_argument("--append", action="store_true",
+                    help="decode workloads: time mla_decode_append (each request's new token "
+                         "written into its cache row in the same launch) instead of mla_decode")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -164,13 +167,24 @@ def main():
             for _ in sets]
 
     stream = torch.cuda.current_stream(dev)
+    if args.append:
+        # The new tokens (one per request), drawn like every other input.
+        rng = np.random.Generator(np.random.PCG64(batch.seed + 1000))
+        c_new = to_dev_bf16(workloads.f32_to_bf16_bits(
+            rng.standard_normal((batch.num_rows, 512), dtype=np.float32) * np.float32(0.5)))
+        k_pe_new = to_dev_bf16(workloads.f32_to_bf16_bits(
+            rng.standard_normal((batch.num_rows, 64), dtype=np.float32) * np.float32(0.5)))
 
     def step(i, ev=None):
         s = sets[i % 2]
         if ev is not None:
             ev[0].record(stream)
-        dec.run(s[0], s[1], s[2], s[3], batch.sm_scale, batch.kv_scale, out=outs[i % 2],
-                lse=lses[i % 2], stream=stream)
+        if args.append:
+            dec.run_append(s[0], s[1], s[2], s[3], c_new, k_pe_new, batch.sm_scale, batch.kv_scale,
+                           out=outs[i % 2], lse=lses[i % 2], stream=stream)
+        else:
+            dec.run(s[0], s[1], s[2], s[3], batch.sm_scale, batch.kv_scale, out=outs[i % 2],
+                    lse=lses[i % 2], stream=stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -227,6 +241,7 @@ def main():
             "batch": batch.batch, "num_heads": batch.num_heads, "kv_lora_rank": 512,
             "qk_rope_head_dim": 64, "page_size": batch.page_size, "kv_tokens": tokens,
             "query_rows": batch.num_rows, "parallelism": "single GPU",
+            "fused_append": bool(args.append),
         },
         "tokens_per_s": round(batch.num_rows / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -234,13 +249,14 @@ def main():
         "plan": {"workers": h.num_workers, "items": h.num_items, "merges": h.num_merges,
                  "partials": h.num_partials, "capacity_tokens": h.chunk_tokens},
         "roofline": {
-            "kernel": "mla_decode launch (decode kernel + split-KV merge kernel)",
+            "kernel": ("mla_decode_append" if args.append else "mla_decode") +
+                      " launch (decode kernel + split-KV merge kernel)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(f"mla_decode_{args.workload}"),
+            "traffic": None if args.append else measured_traffic(f"mla_decode_{args.workload}"),
             "algorithmic_bytes_per_launch": latent_bytes,
             "launch_avg_us": round(launch_avg_ms * 1e3, 2),
             "mfma_tflops": round(flops / (launch_avg_ms * 1e-3) / 1e12, 1),
