@@ -242,6 +242,35 @@ int32_t mla_decode_append(const mla_decode_params* params, const void* plan_h,
                           float sm_scale, void* out_d, float* lse_d, void* stream);
 
 /*
+ * mla_decode_suffix_merge - mla_decode whose result is merged by LSE with a
+ * given state over other tokens, in the same call: the fused suffix-attention
+ * + merge of the tree-verify cascade (PR 49477 analysis, section 3), where the
+ * suffix attention over the compacted draft slots meets the prefix state.
+ * With (v_p, s_p) the given state and (v, s) this call's attention,
+ *   lse = ln(e^{s_p} + e^{s}),  out = e^{s_p - lse} v_p + e^{s - lse} v,
+ * exactly mla_merge_states(prefix, mla_decode(...)) up to rounding; an empty
+ * side drops out, two empty sides give out 0 and lse -inf. Unsplit rows merge
+ * in the decode kernel's output stage and split rows in the split-KV merge, so
+ * this call's own (out, lse) never goes through memory.
+ *
+ *   prefix_out_d  [N, H, 512] in out_dtype, contiguous, 16-byte aligned.
+ *   prefix_lse_d  float [N, H] contiguous (natural log).
+ *   out_d, lse_d  as for mla_decode; each either the same memory as the
+ *                 prefix array of its kind (an in-place merge) or disjoint
+ *                 from it.
+ * Other arguments, kv_lens_d included, as for mla_decode. Returns those of
+ * mla_decode.
+ */
+int32_t mla_decode_suffix_merge(const mla_decode_params* params, const void* plan_h,
+                                const void* workspace_d, size_t workspace_bytes,
+                                const void* q_nope_d, int64_t q_nope_stride_n,
+                                int64_t q_nope_stride_h, const void* q_rope_d,
+                                int64_t q_rope_stride_n, int64_t q_rope_stride_h,
+                                const void* kv_cache_d, float kv_scale, const int32_t* kv_indices_d,
+                                const int32_t* kv_lens_d, float sm_scale, const void* prefix_out_d,
+                                const float* prefix_lse_d, void* out_d, float* lse_d, void* stream);
+
+/*
  * mla_merge_states - merge two attention states over disjoint token sets:
  *   s = ln(e^{s_a} + e^{s_b}),  v = e^{s_a - s} v_a + e^{s_b - s} v_b.
  * This is the LSE merge of the prefix and suffix results in the cascade of the

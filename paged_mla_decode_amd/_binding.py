@@ -96,6 +96,9 @@ _lib.mla_decode.argtypes = [_PARAMS, _p, _p, _sz, _p, _i64, _i64, _p, _i64, _i64
 _lib.mla_decode_append.restype = _i32
 _lib.mla_decode_append.argtypes = [_PARAMS, _p, _p, _sz, _p, _i64, _i64, _p, _i64, _i64, _p, _f32,
                                    _p, _p, _i64, _p, _i64, _f32, _p, _p, _p]
+_lib.mla_decode_suffix_merge.restype = _i32
+_lib.mla_decode_suffix_merge.argtypes = [_PARAMS, _p, _p, _sz, _p, _i64, _i64, _p, _i64, _i64, _p,
+                                         _f32, _p, _p, _f32, _p, _p, _p, _p, _p]
 _lib.mla_merge_states.restype = _i32
 _lib.mla_merge_states.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _p]
 _lib.mla_tree_suffix_compact.restype = _i32
@@ -106,7 +109,8 @@ for _fn in (_lib.mla_absorb_query, _lib.mla_project_output):
     _fn.argtypes = [_p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i32, _i32, _i32, _p]
 
 EXPORTED_SYMBOLS = ("mla_status_string", "mla_decode_variant", "mla_decode_workspace_size",
-                    "mla_decode_plan", "mla_decode", "mla_decode_append", "mla_merge_states",
+                    "mla_decode_plan", "mla_decode", "mla_decode_append", "mla_decode_suffix_merge",
+                    "mla_merge_states",
                     "mla_tree_suffix_compact", "mla_absorb_query", "mla_project_output")
 
 
@@ -204,6 +208,18 @@ def mla_decode_append(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_
                                   _ptr(kv_indices_d), _ptr(c_new_d), int(c_new_stride),
                                   _ptr(k_pe_new_d), int(k_pe_new_stride), float(sm_scale),
                                   _ptr(out_d), _ptr(lse_d), _stream(stream))
+
+
+def mla_decode_suffix_merge(params, plan_h, workspace_d, workspace_bytes, q_nope_d,
+                            q_nope_stride_n, q_nope_stride_h, q_rope_d, q_rope_stride_n,
+                            q_rope_stride_h, kv_cache_d, kv_scale, kv_indices_d, kv_lens_d,
+                            sm_scale, prefix_out_d, prefix_lse_d, out_d, lse_d, stream=None):
+    return _lib.mla_decode_suffix_merge(
+        ctypes.byref(params), _ptr(plan_h), _ptr(workspace_d), int(workspace_bytes), _ptr(q_nope_d),
+        int(q_nope_stride_n), int(q_nope_stride_h), _ptr(q_rope_d), int(q_rope_stride_n),
+        int(q_rope_stride_h), _ptr(kv_cache_d), float(kv_scale), _ptr(kv_indices_d), _ptr(kv_lens_d),
+        float(sm_scale), _ptr(prefix_out_d), _ptr(prefix_lse_d), _ptr(out_d), _ptr(lse_d),
+        _stream(stream))
 
 
 def mla_merge_states(v_a_d, s_a_d, v_b_d, s_b_d, v_out_d, s_out_d, num_rows, head_dim, v_dtype,

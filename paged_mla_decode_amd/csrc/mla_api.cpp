@@ -104,6 +104,18 @@ struct AppendIn {
     int64_t k_pe_new_stride;
 };
 
+// The prefix state of mla_decode_suffix_merge.
+struct PrefixIn {
+    const void* out;
+    const float* lse;
+};
+
+// Two byte ranges that are either the same or disjoint.
+bool same_or_disjoint(const void* x, const void* y, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+    return a == b || a + bytes <= b || b + bytes <= a;
+}
+
 // Every request has exactly one query row and a last-chunk item (length >= 1).
 bool append_batch_ok(const mla_plan_header* h, const void* plan_h) {
     if (h->num_rows != h->batch) return false;
@@ -126,7 +138,7 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
                     int64_t q_nope_stride_h, const void* q_rope_d, int64_t q_rope_stride_n,
                     int64_t q_rope_stride_h, const void* kv_cache_d, float kv_scale,
                     const int32_t* kv_indices_d, const int32_t* kv_lens_d, const AppendIn* app,
-                    float sm_scale, void* out_d, float* lse_d, void* stream) {
+                    const PrefixIn* pre, float sm_scale, void* out_d, float* lse_d, void* stream) {
     if (!params || !plan_h || !workspace_d) return MLA_ERR_INVALID_ARG;
     Variant v;
     if (!select_variant(params, &v)) return MLA_ERR_UNSUPPORTED;
@@ -153,6 +165,14 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
             (app->c_new_stride | app->k_pe_new_stride) % 8 != 0)
             return MLA_ERR_INVALID_ARG;
         if (!append_batch_ok(h, plan_h)) return MLA_ERR_INVALID_ARG;
+    }
+    if (pre) {
+        if (!pre->out || !pre->lse || !aligned16(pre->out) || (reinterpret_cast<uintptr_t>(pre->lse) & 3))
+            return MLA_ERR_INVALID_ARG;
+        const size_t elems = (size_t)h->num_rows * (size_t)params->num_heads;
+        const size_t ebytes = params->out_dtype == MLA_DTYPE_FP32 ? 4 : 2;
+        if (!same_or_disjoint(out_d, pre->out, elems * kLatent * ebytes)) return MLA_ERR_INVALID_ARG;
+        if (lse_d && !same_or_disjoint(lse_d, pre->lse, elems * 4)) return MLA_ERR_INVALID_ARG;
     }
 
     const char* ws = static_cast<const char*>(workspace_d);
@@ -188,6 +208,10 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
         a.cache_w = static_cast<uint8_t*>(const_cast<void*>(kv_cache_d));
         a.kv_scale = kv_scale;
     }
+    if (pre) {
+        a.prefix_out = pre->out;
+        a.prefix_lse = pre->lse;
+    }
     int err = launch_decode(v, params->kv_dtype, params->out_dtype, a, h->num_workers, stream);
     if (err != 0) return MLA_ERR_HIP;
     if (h->num_merges > 0) {
@@ -198,6 +222,8 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
         m.out = out_d;
         m.lse = lse_d;
         m.num_heads = params->num_heads;
+        m.prefix_out = a.prefix_out;
+        m.prefix_lse = a.prefix_lse;
         // Merges come most partials first (planner); the leading wide ones.
         const mla_merge_item* hm =
             reinterpret_cast<const mla_merge_item*>(reinterpret_cast<const char*>(plan_h) + h->merges_offset);
@@ -221,7 +247,23 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
                    void* out_d, float* lse_d, void* stream) {
     return decode_impl(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_stride_n,
                        q_nope_stride_h, q_rope_d, q_rope_stride_n, q_rope_stride_h, kv_cache_d,
-                       kv_scale, kv_indices_d, kv_lens_d, nullptr, sm_scale, out_d, lse_d, stream);
+                       kv_scale, kv_indices_d, kv_lens_d, nullptr, nullptr, sm_scale, out_d, lse_d,
+                       stream);
+}
+
+int32_t mla_decode_suffix_merge(const mla_decode_params* params, const void* plan_h,
+                                const void* workspace_d, size_t workspace_bytes,
+                                const void* q_nope_d, int64_t q_nope_stride_n,
+                                int64_t q_nope_stride_h, const void* q_rope_d,
+                                int64_t q_rope_stride_n, int64_t q_rope_stride_h,
+                                const void* kv_cache_d, float kv_scale, const int32_t* kv_indices_d,
+                                const int32_t* kv_lens_d, float sm_scale, const void* prefix_out_d,
+                                const float* prefix_lse_d, void* out_d, float* lse_d, void* stream) {
+    const PrefixIn pre{prefix_out_d, prefix_lse_d};
+    return decode_impl(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_stride_n,
+                       q_nope_stride_h, q_rope_d, q_rope_stride_n, q_rope_stride_h, kv_cache_d,
+                       kv_scale, kv_indices_d, kv_lens_d, nullptr, &pre, sm_scale, out_d, lse_d,
+                       stream);
 }
 
 int32_t mla_decode_append(const mla_decode_params* params, const void* plan_h,
@@ -234,7 +276,8 @@ int32_t mla_decode_append(const mla_decode_params* params, const void* plan_h,
     const AppendIn app{c_new_d, c_new_stride, k_pe_new_d, k_pe_new_stride};
     return decode_impl(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_stride_n,
                        q_nope_stride_h, q_rope_d, q_rope_stride_n, q_rope_stride_h, kv_cache_d,
-                       kv_scale, kv_indices_d, nullptr, &app, sm_scale, out_d, lse_d, stream);
+                       kv_scale, kv_indices_d, nullptr, &app, nullptr, sm_scale, out_d, lse_d,
+                       stream);
 }
 
 int32_t mla_merge_states(const void* v_a_d, const float* s_a_d, const void* v_b_d,

@@ -63,7 +63,7 @@ __device__ __forceinline__ void settle_o(f32x16 (&O)[4][4]) {
                    "+a"(O[3][0]), "+a"(O[3][1]), "+a"(O[3][2]), "+a"(O[3][3]));
 }
 
-template <bool KV8, bool OUT32, bool APPEND>
+template <bool KV8, bool OUT32, int MODE>
 __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
     constexpr int HS = 4;
     using L = H128Layout<KV8>;
@@ -87,6 +87,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) char pbuf[(OUT32 ? 2 : 1) * PBuf::kBytes];
     __shared__ __attribute__((aligned(16))) int idx_ring[kStages][HS][64];
     __shared__ float l_sh[128];
+    __shared__ float wa_sh[128], wb_sh[128];  // fused prefix merge: per-head weights
     __shared__ int rerun_flag[HS];
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         // out behind them, so the latencies of the two overlap.
         prologue_idx();
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the page indices
-        if (APPEND && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
+        if (MODE == kModeAppend && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
             // Fused append: the request's new row goes to the cache before any
             // wave loads a tile that holds it.
             append_row<KV8>(a, it, tid, 256);
@@ -430,19 +431,40 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         const float l = sum_xor32(l_part);
         const int nh = a.num_heads;
         const float lse = l > 0.f ? (m_ref + __log2f(l)) * kLn2 : -INFINITY;
+        // Fused prefix merge of an unsplit row: out = wa * prefix + wb * this,
+        // with the weights of the two states' LSE merge.
+        const bool fuse = MODE == kModeMerge && it.partial < 0;
         if (gq == 0) {
             l_sh[32 * w + hq] = l;
-            if (it.partial >= 0)
+            if (fuse) {
+                const int64_t i = (int64_t)it.row * nh + head;
+                const float la = a.prefix_lse[i];
+                float wa = 0.f, wb = 0.f, s = -INFINITY;
+                if (!(la == -INFINITY && lse == -INFINITY)) {
+                    const float mx = fmaxf(la, lse);
+                    const float ea = __expf(la - mx), eb = __expf(lse - mx);
+                    wa = ea / (ea + eb);
+                    wb = eb / (ea + eb);
+                    s = mx + __logf(ea + eb);
+                }
+                wa_sh[32 * w + hq] = wa;
+                wb_sh[32 * w + hq] = wb;
+                if (a.lse) a.lse[i] = s;
+            } else if (it.partial >= 0) {
                 a.part_lse[(int64_t)it.partial * nh + head] = lse;
-            else if (a.lse)
+            } else if (a.lse) {
                 a.lse[(int64_t)it.row * nh + head] = lse;
+            }
         }
         lds_barrier();
         float inv[4];
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
             const float lh = l_sh[32 * hb + hq];
-            inv[hb] = lh > 0.f ? a.out_scale / lh : 0.f;
+            if (MODE == kModeMerge && fuse)
+                inv[hb] = lh > 0.f ? a.out_scale * wb_sh[32 * hb + hq] / lh : 0.f;
+            else
+                inv[hb] = lh > 0.f ? a.out_scale / lh : 0.f;
         }
         // Output rows of this item: [partial or row][head_begin + h][512].
         const int64_t row0 = (it.partial >= 0 ? (int64_t)it.partial * nh : (int64_t)it.row * nh) + it.head_begin;
@@ -474,8 +496,15 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                 for (int jj = 0; jj < 128 * kUnits / 256; ++jj) {
                     const int u = tid + 256 * jj;
                     const int h = u / kUnits, c8 = u % kUnits;
-                    const bf16x8 v = *(const LDS_AS bf16x8*)(stage + OS::offset(h, 8 * c8));
-                    *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(obase) + (row0 + h) * kLatent + rd * OS::kCols + 8 * c8) = v;
+                    bf16x8 v = *(const LDS_AS bf16x8*)(stage + OS::offset(h, 8 * c8));
+                    const int64_t o = (row0 + h) * kLatent + rd * OS::kCols + 8 * c8;
+                    if (MODE == kModeMerge && fuse) {
+                        const bf16x8 p = *(reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.prefix_out) + o));
+                        const float wa = wa_sh[h];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] + wa * (float)p[e]);
+                    }
+                    *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(obase) + o) = v;
                 }
                 lds_barrier();
             }
@@ -497,8 +526,10 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                 for (int j = 0; j < 16; ++j) {
                     const int u = tid + 256 * j;
                     const int h = u >> 5, c4 = u & 31;
-                    const f32x4 v = *(const LDS_AS f32x4*)(stage + OutStage::offset(h, 4 * c4));
+                    f32x4 v = *(const LDS_AS f32x4*)(stage + OutStage::offset(h, 4 * c4));
                     const int64_t o = (row0 + h) * kLatent + 128 * md + 4 * c4;
+                    if (MODE == kModeMerge && fuse)
+                        v += wa_sh[h] * *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.prefix_out) + o);
                     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(obase) + o) = v;
                 }
                 lds_barrier();
@@ -514,21 +545,28 @@ int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num
     const dim3 grid(num_workers), block(256);
     const bool kv8 = kv_dtype == MLA_DTYPE_FP8_E4M3FN;
     const bool o32 = out_dtype == MLA_DTYPE_FP32;
-    // The fused append is its own instantiation, so the plain decode carries
-    // none of its arguments or branches.
-    const bool app = a.c_new != nullptr;
+    // The fused append and the fused prefix merge are instantiations of their
+    // own, so the plain decode carries none of their arguments or branches.
+    const int mode = a.c_new ? kModeAppend : a.prefix_lse ? kModeMerge : kModePlain;
+    auto go = [&](auto kv8_t, auto o32_t) {
+        constexpr bool K = decltype(kv8_t)::value, O = decltype(o32_t)::value;
+        if (mode == kModeAppend)
+            decode_h128_kernel<K, O, kModeAppend><<<grid, block, 0, s>>>(a);
+        else if (mode == kModeMerge)
+            decode_h128_kernel<K, O, kModeMerge><<<grid, block, 0, s>>>(a);
+        else
+            decode_h128_kernel<K, O, kModePlain><<<grid, block, 0, s>>>(a);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
     if (kv8 && o32)
-        app ? decode_h128_kernel<true, true, true><<<grid, block, 0, s>>>(a)
-            : decode_h128_kernel<true, true, false><<<grid, block, 0, s>>>(a);
+        go(T{}, T{});
     else if (kv8)
-        app ? decode_h128_kernel<true, false, true><<<grid, block, 0, s>>>(a)
-            : decode_h128_kernel<true, false, false><<<grid, block, 0, s>>>(a);
+        go(T{}, F{});
     else if (o32)
-        app ? decode_h128_kernel<false, true, true><<<grid, block, 0, s>>>(a)
-            : decode_h128_kernel<false, true, false><<<grid, block, 0, s>>>(a);
+        go(F{}, T{});
     else
-        app ? decode_h128_kernel<false, false, true><<<grid, block, 0, s>>>(a)
-            : decode_h128_kernel<false, false, false><<<grid, block, 0, s>>>(a);
+        go(F{}, F{});
     return (int)hipGetLastError();
 }
 

@@ -64,7 +64,17 @@ struct DecodeArgs {
     int64_t k_pe_new_sn;
     uint8_t* cache_w;
     float kv_scale;  // fp8 encoding divides by it
+    // Fused prefix merge (null prefix_lse: none): the result is merged by LSE
+    // with the state (prefix_out [N][H][512] in the output's precision,
+    // prefix_lse [N][H]); unsplit rows in the decode kernel, split rows in the
+    // merge kernels. out/lse may be the same memory as prefix_out/prefix_lse.
+    const void* prefix_out;
+    const float* prefix_lse;
 };
+
+// Decode kernel instantiations: the plain decode, the fused append, the fused
+// prefix merge. The extra arguments of the last two never reach the first.
+enum DecodeMode { kModePlain = 0, kModeAppend = 1, kModeMerge = 2 };
 
 struct MergePartialsArgs {
     const mla_merge_item* merges;
@@ -73,6 +83,8 @@ struct MergePartialsArgs {
     void* out;
     float* lse;  // may be null
     int32_t num_heads;
+    const void* prefix_out;  // fused prefix merge, or null
+    const float* prefix_lse;
 };
 
 // Kernel launchers (device code lives in mla_kernels.hip). Return hipError_t as int.

@@ -42,7 +42,7 @@ using namespace dev;
 // ---------------------------------------------------------------------------
 // The decode kernel
 // ---------------------------------------------------------------------------
-template <int HW, int HS, bool KV8, bool OUT32, bool APPEND>
+template <int HW, int HS, bool KV8, bool OUT32, int MODE>
 __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
     using L = TileLayout<KV8>;
     using SA = ScoreAddr<HW, KV8>;
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
             // loop would otherwise also drain the tiles in flight.
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
-        if (APPEND && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
+        if (MODE == kModeAppend && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
             // Fused append: the request's new row goes to the cache before any
             // wave loads a tile that holds it.
             append_row<KV8>(a, it, threadIdx.x, 64 * HS);
@@ -332,9 +332,39 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
         if (HW == 16) l = sum_xor16(l);
         l = sum_xor32(l);
         const bool empty = !(l > 0.f);
-        const float inv = empty ? 0.f : (a.out_scale / l);
-        const float lse = empty ? -INFINITY : (m_run + __log2f(l)) * kLn2;
+        float inv = empty ? 0.f : (a.out_scale / l);
+        float lse = empty ? -INFINITY : (m_run + __log2f(l)) * kLn2;
         const int nh = a.num_heads;
+        // Fused prefix merge of an unsplit row: out = wa * prefix + wb * this,
+        // with the weights of the two states' LSE merge; lse becomes theirs.
+        const bool fuse = MODE == kModeMerge && it.partial < 0;
+        float wa = 0.f;
+        if (MODE == kModeMerge && fuse) {
+            const float la = a.prefix_lse[(int64_t)it.row * nh + head];
+            float wb = 0.f, s = -INFINITY;
+            if (!(la == -INFINITY && lse == -INFINITY)) {
+                const float mx = fmaxf(la, lse);
+                const float ea = __expf(la - mx), eb = __expf(lse - mx);
+                wa = ea / (ea + eb);
+                wb = eb / (ea + eb);
+                s = mx + __logf(ea + eb);
+            }
+            inv *= wb;
+            lse = s;
+        }
+        // Adds the prefix's share to four consecutive output columns.
+        auto with_prefix = [&](f32x4 x, int64_t off) -> f32x4 {
+            if (MODE == kModeMerge && fuse) {
+                if constexpr (OUT32) {
+                    x += wa * *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.prefix_out) + off);
+                } else {
+                    const bf16x4 p = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(a.prefix_out) + off);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] += wa * (float)p[e];
+                }
+            }
+            return x;
+        };
 
         if (it.partial >= 0 && OUT32) {
             float* po = reinterpret_cast<float*>(a.part_out) + ((int64_t)it.partial * nh + head) * kLatent;
@@ -370,12 +400,14 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
                             const int d = 32 * md + 8 * r4 + 4 * gq;
                             f32x4 v = {O32[md][4 * r4] * inv, O32[md][4 * r4 + 1] * inv,
                                        O32[md][4 * r4 + 2] * inv, O32[md][4 * r4 + 3] * inv};
-                            *reinterpret_cast<f32x4*>(o + d) = v;
+                            *reinterpret_cast<f32x4*>(o + d) = with_prefix(v, orow * kLatent + d);
                         }
                 } else {
 #pragma unroll
-                    for (int md = 0; md < kDBlocks; ++md)
-                        *reinterpret_cast<f32x4*>(o + 16 * md + 4 * gq) = O16[md] * inv;
+                    for (int md = 0; md < kDBlocks; ++md) {
+                        const int d = 16 * md + 4 * gq;
+                        *reinterpret_cast<f32x4*>(o + d) = with_prefix(O16[md] * inv, orow * kLatent + d);
+                    }
                 }
             } else {
                 __bf16* o = reinterpret_cast<__bf16*>(obase) + orow * kLatent;
@@ -385,16 +417,19 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
                         for (int r4 = 0; r4 < 4; ++r4) {
                             const int d = 32 * md + 8 * r4 + 4 * gq;
-                            bf16x4 v = {(__bf16)(O32[md][4 * r4] * inv), (__bf16)(O32[md][4 * r4 + 1] * inv),
-                                        (__bf16)(O32[md][4 * r4 + 2] * inv), (__bf16)(O32[md][4 * r4 + 3] * inv)};
+                            f32x4 x = {O32[md][4 * r4] * inv, O32[md][4 * r4 + 1] * inv,
+                                       O32[md][4 * r4 + 2] * inv, O32[md][4 * r4 + 3] * inv};
+                            x = with_prefix(x, orow * kLatent + d);
+                            bf16x4 v = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
                             *reinterpret_cast<bf16x4*>(o + d) = v;
                         }
                 } else {
 #pragma unroll
                     for (int md = 0; md < kDBlocks; ++md) {
-                        const f32x4 x = O16[md] * inv;
+                        const int d = 16 * md + 4 * gq;
+                        const f32x4 x = with_prefix(O16[md] * inv, orow * kLatent + d);
                         bf16x4 v = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-                        *reinterpret_cast<bf16x4*>(o + 16 * md + 4 * gq) = v;
+                        *reinterpret_cast<bf16x4*>(o + d) = v;
                     }
                 }
             }
@@ -462,6 +497,34 @@ __device__ __forceinline__ void merge_batch(const MergePartialsArgs& a, const ml
     }
 }
 
+// Folds the given prefix state of (row, h) into st: the fused prefix merge of
+// a split row. Lane reads its 8 columns before merge_store writes them, so the
+// output may be the prefix's own memory.
+template <bool OUT32>
+__device__ __forceinline__ void merge_prefix(const MergePartialsArgs& a, int row, int h, int lane,
+                                             MergeState& st) {
+    using V = std::conditional_t<OUT32, f32x8, bf16x8>;
+    const int64_t i = (int64_t)row * a.num_heads + h;
+    const float l = a.prefix_lse[i];
+    if (l == -INFINITY) return;
+    const V v = *(reinterpret_cast<const V*>(a.prefix_out) + i * (kLatent / 8) + lane);
+    const float mb = fmaxf(st.m, l);
+    const float r = st.m == -INFINITY ? 0.f : fast_exp2((st.m - mb) * kLog2e);
+    st.acc = st.acc * r;
+    st.wsum *= r;
+    st.m = mb;
+    const float wp = fast_exp2((l - mb) * kLog2e);
+    st.wsum += wp;
+    f32x8 x;
+    if constexpr (OUT32) {
+        x = v;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+    }
+    st.acc += wp * x;
+}
+
 template <bool OUT32>
 __device__ __forceinline__ void merge_store(const MergePartialsArgs& a, const mla_merge_item& mi, int h, int lane,
                                             const MergeState& st) {
@@ -490,6 +553,7 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(const MergePartials
         MergeState st;
         for (int p0 = 0; p0 < mi.num_partials; p0 += kBatch)
             merge_batch<OUT32, kBatch>(a, mi, h, lane, p0, min(kBatch, mi.num_partials - p0), st);
+        if (a.prefix_lse) merge_prefix<OUT32>(a, mi.row, h, lane, st);
         merge_store<OUT32>(a, mi, h, lane, st);
     }
 }
@@ -526,6 +590,7 @@ __global__ __launch_bounds__(1024) void merge_partials_wide_kernel(const MergePa
             t.acc += r * sacc[k][lane];
         }
     }
+    if (a.prefix_lse) merge_prefix<OUT32>(a, mi.row, h, lane, t);
     merge_store<OUT32>(a, mi, h, lane, t);
 }
 
@@ -620,19 +685,27 @@ static int launch_decode_hs(int kv_dtype, int out_dtype, const DecodeArgs& a, in
     const dim3 grid(n), block(64 * HS);
     const bool kv8 = kv_dtype == MLA_DTYPE_FP8_E4M3FN;
     const bool o32 = out_dtype == MLA_DTYPE_FP32;
-    const bool app = a.c_new != nullptr;  // the fused append: its own instantiation
+    // The fused append and prefix merge are instantiations of their own.
+    const int mode = a.c_new ? kModeAppend : a.prefix_lse ? kModeMerge : kModePlain;
+    auto go = [&](auto kv8_t, auto o32_t) {
+        constexpr bool K = decltype(kv8_t)::value, O = decltype(o32_t)::value;
+        if (mode == kModeAppend)
+            decode_kernel<HW, HS, K, O, kModeAppend><<<grid, block, 0, s>>>(a);
+        else if (mode == kModeMerge)
+            decode_kernel<HW, HS, K, O, kModeMerge><<<grid, block, 0, s>>>(a);
+        else
+            decode_kernel<HW, HS, K, O, kModePlain><<<grid, block, 0, s>>>(a);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
     if (kv8 && o32)
-        app ? decode_kernel<HW, HS, true, true, true><<<grid, block, 0, s>>>(a)
-            : decode_kernel<HW, HS, true, true, false><<<grid, block, 0, s>>>(a);
+        go(T{}, T{});
     else if (kv8)
-        app ? decode_kernel<HW, HS, true, false, true><<<grid, block, 0, s>>>(a)
-            : decode_kernel<HW, HS, true, false, false><<<grid, block, 0, s>>>(a);
+        go(T{}, F{});
     else if (o32)
-        app ? decode_kernel<HW, HS, false, true, true><<<grid, block, 0, s>>>(a)
-            : decode_kernel<HW, HS, false, true, false><<<grid, block, 0, s>>>(a);
+        go(F{}, T{});
     else
-        app ? decode_kernel<HW, HS, false, false, true><<<grid, block, 0, s>>>(a)
-            : decode_kernel<HW, HS, false, false, false><<<grid, block, 0, s>>>(a);
+        go(F{}, F{});
     return (int)hipGetLastError();
 }
 

@@ -103,6 +103,29 @@ class PagedMlaDecoder:
         return out, lse
 
 
+    def run_suffix_merge(self, q_nope, q_rope, kv_cache, kv_indices, sm_scale, prefix_out,
+                         prefix_lse, kv_scale=1.0, kv_lens=None, out=None, lse=None, stream=None):
+        """``run`` merged by LSE with the state (prefix_out, prefix_lse) in the same
+        call (mla_decode_suffix_merge). out/lse default to new tensors; passing
+        prefix_out/prefix_lse themselves merges in place."""
+        h = self.header()
+        N, H = h.num_rows, self.num_heads
+        if out is None:
+            out = torch.empty_like(prefix_out)
+        if lse is None:
+            lse = torch.empty((N, H), dtype=torch.float32, device=self.device)
+        assert q_nope.stride(-1) == 1 and q_rope.stride(-1) == 1
+        stream = stream or torch.cuda.current_stream(self.device)
+        st = B.mla_decode_suffix_merge(self.params, self.plan_h, self.workspace, self.workspace.numel(),
+                                       q_nope, q_nope.stride(0), q_nope.stride(1), q_rope,
+                                       q_rope.stride(0), q_rope.stride(1), kv_cache, kv_scale,
+                                       kv_indices, kv_lens, sm_scale, prefix_out, prefix_lse, out,
+                                       lse, stream)
+        if st != B.MLA_OK:
+            raise B.MlaError("mla_decode_suffix_merge", st)
+        return out, lse
+
+
 def merge_states(v_a, s_a, v_b, s_b, out=None, s_out=None, stream=None):
     """LSE merge of two states (bf16 or fp32 v of shape [..., D], fp32 s of shape [...])."""
     assert v_a.dtype == v_b.dtype and v_a.shape == v_b.shape

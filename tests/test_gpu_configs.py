@@ -73,14 +73,16 @@ def test_config_sampled_rows(dev, name, out_dtype, k):
         assert split_rows > 0, "the sample must include a split-KV row"
 
 
-def test_tree_verify_cascade(dev):
+@pytest.mark.parametrize("fused", [False, True], ids=["merge_states", "suffix_merge"])
+def test_tree_verify_cascade(dev, fused):
     from paged_mla_decode_amd.decoder import PagedMlaDecoder, merge_states, tree_suffix_compact
     tv = workloads.tree_verify()
     pre = tv.prefix
     W, D = tv.width, tv.max_tree_depth
     B = pre.batch
     N = pre.num_rows
-    say(f"tree cascade: B={B} W={W} rows={N} prefix={int(pre.seq_lens[0])} depth<={D}")
+    say(f"tree cascade ({'fused' if fused else 'separate'} merge): B={B} W={W} rows={N} "
+        f"prefix={int(pre.seq_lens[0])} depth<={D}")
     qn, qr, cache, idx = batch_to_device(pre, dev)
 
     # 1. stable compaction of the suffix tables (one launch)
@@ -102,10 +104,14 @@ def test_tree_verify_cascade(dev):
     ds = PagedMlaDecoder(pre.num_heads, 1, max_batch=N, max_rows=N, device=dev)
     ds.plan(np.arange(N + 1, dtype=np.int32) * D, np.ones(N, dtype=np.int32))
     suffix_idx = table[:, :D].contiguous().view(-1)
-    out_s, lse_s = ds.run(qn, qr, cache, suffix_idx, pre.sm_scale, kv_lens=seqlens)
-
-    # 4. LSE merge of the two states
-    out, lse = merge_states(out_p, lse_p, out_s, lse_s)
+    if fused:
+        # 3+4. the suffix attention merged with the prefix state in the same call, in place
+        out, lse = ds.run_suffix_merge(qn, qr, cache, suffix_idx, pre.sm_scale, out_p, lse_p,
+                                       kv_lens=seqlens, out=out_p, lse=lse_p)
+    else:
+        out_s, lse_s = ds.run(qn, qr, cache, suffix_idx, pre.sm_scale, kv_lens=seqlens)
+        # 4. LSE merge of the two states
+        out, lse = merge_states(out_p, lse_p, out_s, lse_s)
     torch.cuda.synchronize()
     out = out.float().cpu().numpy().astype(np.float64)
     lse = lse.cpu().numpy().astype(np.float64)
