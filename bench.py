@@ -24,6 +24,11 @@ latent output), cycling over 8 distinct weight and activation sets (about 600
 MB) so that no step is served from the Infinity Cache. value = their
 algorithmic bytes (weights, inputs and outputs, each once) / step time.
 
+With --workload tree_verify it times the tree-verify cascade of the PR 49477
+analysis (16 requests, 2048-token prefix, 64 drafts at depth <= 8, H=128):
+the suffix-table compaction, the prefix attention of all 1024 draft rows, and
+the suffix attention merged into the prefix state (mla_decode_suffix_merge).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
@@ -113,7 +118,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="v3",
-                    choices=["v3", "v2_lite", "skewed_fp8", "projections"])
+                    choices=["v3", "v2_lite", "skewed_fp8", "projections", "tree_verify"])
     ap.add_argument("--append", action="store_true",
                     help="decode workloads: time mla_decode_append (each request's new token "
                          "written into its cache row in the same launch) instead of mla_decode")
@@ -129,6 +134,8 @@ def main():
 
     if args.workload == "projections":
         return bench_projections(args)
+    if args.workload == "tree_verify":
+        return bench_tree_verify(args)
 
     import torch
 
@@ -408,6 +415,169 @@ def bench_projections(args):
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline_projections(p)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_tree(tv, target_s=10.0):
+    """Oracle latent GB/s on the first rows of the cascade (each row's attention
+    over its prefix and its visible drafts), sized to about target_s."""
+    import oracle
+
+    pre, W = tv.prefix, tv.width
+
+    def rows_ref(rows):
+        kv_indptr, kv_indices = [0], []
+        for r in rows:
+            req, plen = r // W, int(tv.prefix_lens[r // W])
+            vis = np.nonzero(tv.tree_mask[r])[0]
+            slots = np.concatenate([tv.req_to_token[req, :plen], tv.req_to_token[req, plen + vis]])
+            kv_indices.append(slots)
+            kv_indptr.append(kv_indptr[-1] + len(slots))
+        t0 = time.perf_counter()
+        oracle.mla_decode(pre.q_nope[rows], pre.q_rope[rows], pre.cache,
+                          np.asarray(kv_indptr, np.int32), np.concatenate(kv_indices).astype(np.int32),
+                          1, pre.sm_scale, kv_last_page_len=np.ones(len(rows), np.int32))
+        return time.perf_counter() - t0, kv_indptr[-1]
+
+    dt, _ = rows_ref(list(range(2)))
+    n = int(min(pre.num_rows, max(2, 2 * target_s / max(dt, 1e-6))))
+    dt, toks = rows_ref(list(range(n)))
+    return {"value": toks * 1152 / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {n} of {pre.num_rows} draft rows (prefix + visible drafts, all 128 heads), "
+                      f"fp64 C oracle, {dt:.1f} s"}
+
+
+def bench_tree_verify(args):
+    import torch
+
+    import workloads
+    from paged_mla_decode_amd.decoder import PagedMlaDecoder, merge_states, tree_suffix_compact
+
+    dev = torch.device("cuda:0")
+    tv = workloads.tree_verify()
+    pre, W, D = tv.prefix, tv.width, tv.max_tree_depth
+    B, N, H = pre.batch, pre.num_rows, pre.num_heads
+
+    def to_dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = {"qn": to_dev_bf16(pre.q_nope), "qr": to_dev_bf16(pre.q_rope), "cache": to_dev_bf16(pre.cache),
+            "idx": torch.from_numpy(pre.kv_indices).to(dev), "mask": torch.from_numpy(tv.tree_mask).to(dev),
+            "r2t": torch.from_numpy(tv.req_to_token).to(dev), "plen": torch.from_numpy(tv.prefix_lens).to(dev)}
+    # Two input sets alternate so that one step's reads are not served from the
+    # previous step's Infinity Cache lines.
+    sets = [base, {k: v.clone() for k, v in base.items()}]
+    dp = PagedMlaDecoder(H, 1, max_batch=B, max_rows=N, device=dev)
+    t0 = time.perf_counter()
+    hp = dp.plan(pre.kv_indptr, pre.kv_last_page_len, pre.qo_indptr)
+    ds = PagedMlaDecoder(H, 1, max_batch=N, max_rows=N, device=dev)
+    hs = ds.plan(np.arange(N + 1, dtype=np.int32) * D, np.ones(N, dtype=np.int32))
+    plan_us = (time.perf_counter() - t0) * 1e6
+    outs = [(torch.empty((N, H, 512), dtype=torch.bfloat16, device=dev),
+             torch.empty((N, H), dtype=torch.float32, device=dev)) for _ in sets]
+    tables = [tree_suffix_compact(s["mask"], s["r2t"], s["plen"], W) for s in sets]
+    stream = torch.cuda.current_stream(dev)
+
+    def compact(i):
+        s = sets[i % 2]
+        return tree_suffix_compact(s["mask"], s["r2t"], s["plen"], W, stream=stream)
+
+    def prefix(i):
+        s, (o, l) = sets[i % 2], outs[i % 2]
+        dp.run(s["qn"], s["qr"], s["cache"], s["idx"], pre.sm_scale, out=o, lse=l, stream=stream)
+
+    def suffix(i, table_seqlens):
+        s, (o, l) = sets[i % 2], outs[i % 2]
+        table, seqlens = table_seqlens
+        ds.run_suffix_merge(s["qn"], s["qr"], s["cache"], table[:, :D].contiguous().view(-1),
+                            pre.sm_scale, o, l, kv_lens=seqlens, out=o, lse=l, stream=stream)
+
+    def suffix_separate(i, table_seqlens):
+        s, (o, l) = sets[i % 2], outs[i % 2]
+        table, seqlens = table_seqlens
+        so, sl = ds.run(s["qn"], s["qr"], s["cache"], table[:, :D].contiguous().view(-1),
+                        pre.sm_scale, kv_lens=seqlens, stream=stream)
+        merge_states(o, l, so, sl, out=o, s_out=l, stream=stream)
+
+    def step(i):
+        ts = compact(i)
+        prefix(i)
+        suffix(i, ts)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    def launch_avg_us(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    compact_us = launch_avg_us(compact)
+    prefix_us = launch_avg_us(prefix)
+    suffix_us = launch_avg_us(lambda i: suffix(i, tables[i % 2]))
+    separate_us = launch_avg_us(lambda i: suffix_separate(i, tables[i % 2]))
+
+    seq = tables[0][1].cpu().numpy()
+    prefix_tokens = int(pre.seq_lens.astype(np.int64).repeat(W).sum())
+    attended = prefix_tokens + int(seq.sum())
+    latent_bytes = costs.mla_decode_latent_bytes(attended, 2)
+    unique_bytes = costs.mla_decode_latent_bytes(int(pre.seq_lens.sum()) + B * W, 2)
+    ms_per_step = elapsed * 1e3 / args.steps
+    gbs = latent_bytes / (ms_per_step * 1e-3) / 1e9
+    prefix_flops = costs.mla_decode_flops(prefix_tokens, H)
+    tflops = prefix_flops / (prefix_us * 1e-6) / 1e12
+    log(f"step {ms_per_step * 1e3:.1f} us: compaction {compact_us:.1f}, prefix {prefix_us:.1f} "
+        f"({tflops:.0f} TFLOP/s), suffix+merge {suffix_us:.1f} (separate suffix then merge: "
+        f"{separate_us:.1f}); prefix plan {hp.num_items} items, suffix plan {hs.num_items} items")
+    res = {
+        "metric": "MLA decode latent-cache GB/s (% of HBM peak) and tokens/s, DeepSeek-V3 shapes",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"tree_verify: B={B} prefix={int(pre.seq_lens[0])} W={W} depth<={D} "
+                               f"H={H} page_size=1 seed={pre.seed}",
+                   "batch": B, "draft_rows": N, "num_heads": H, "kv_tokens_attended": attended,
+                   "unique_kv_tokens": int(pre.seq_lens.sum()) + B * W, "parallelism": "single GPU"},
+        "tokens_per_s": round(N / (ms_per_step * 1e-3), 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "unique_latent_bytes": unique_bytes,
+        "plan_us": round(plan_us, 1),
+        "phases_us": {"compaction": round(compact_us, 2), "prefix": round(prefix_us, 2),
+                      "suffix_merge": round(suffix_us, 2), "suffix_then_merge_states": round(separate_us, 2)},
+        "roofline": {
+            "kernel": "prefix mla_decode launch (1024 draft rows x 2048 prefix tokens, H=128)",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic("mla_decode_tree_verify"),
+            "algorithmic_flops_per_launch": prefix_flops,
+            "launch_avg_us": round(prefix_us, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline_tree(tv)
     print(json.dumps(res), flush=True)
 
 

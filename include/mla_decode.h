@@ -63,7 +63,29 @@ typedef struct {
     int32_t num_cus;          /* compute units to balance over; 0 = ask the device */
     int32_t max_splits;       /* cap on KV chunks per query row; 0 = library default,
                                  1 = never split */
+    int32_t flags;            /* MLA_DECODE_* bits, 0 for none */
+    int32_t max_rows;         /* graph-safe plans: the most query rows any plan will hold
+                                 (>= 1); it fixes where the plan's arrays and the partials
+                                 sit in the workspace. Ignored otherwise. */
 } mla_decode_params;
+
+/*
+ * Graph-safe launches: every grid size and every workspace address of
+ * mla_decode (and of the variants below that take a plan) depends on the
+ * params only, never on the plan: the plan is laid out for params.max_rows
+ * query rows whatever it holds, and the merge kernels read their counts from
+ * the plan's device copy. A hipGraph
+ * captured around one call therefore stays valid for any later plan built
+ * with the same params into the same workspace (by mla_decode_plan on the
+ * stream, before the replay), as the graph-replayed decode of the
+ * attention-backends page requires: buffers sized for the largest batch,
+ * contents changing every step. The decode launch always has all of its
+ * workers (those without work exit at once) and the merge launches run
+ * even when the plan has no split row, which costs a few microseconds
+ * against an ordinary call. Output rows past the plan's query rows are never
+ * written (padding rows keep their contents).
+ */
+#define MLA_DECODE_GRAPH_SAFE 1
 
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(int32_t status);
@@ -73,7 +95,7 @@ const char* mla_status_string(int32_t status);
  * of the device workspace. It is plain data: tests may read it.
  */
 #define MLA_PLAN_MAGIC 0x504C4D41u /* "AMLP" */
-#define MLA_PLAN_VERSION 3
+#define MLA_PLAN_VERSION 4
 
 typedef struct {
     uint32_t magic;
@@ -89,6 +111,8 @@ typedef struct {
     int32_t num_workers;    /* workgroups of the decode launch; worker w processes
                                items [workers[w], workers[w+1]) in order */
     int32_t max_merge_partials; /* most partials any one merged row has (0 without merges) */
+    int32_t num_wide_merges; /* the leading merges, those of at least 16 partials */
+    int32_t flags;          /* the params' flags the plan was built with */
     int64_t num_page_entries; /* kv_indptr[batch]: entries of kv_indices the batch uses */
     int64_t items_offset;   /* byte offset of mla_work_item[num_items] */
     int64_t merges_offset;  /* byte offset of mla_merge_item[num_merges] */

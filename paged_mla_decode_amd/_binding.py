@@ -41,7 +41,8 @@ MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP32 = 1
 MLA_DTYPE_FP8_E4M3FN = 2
 MLA_PLAN_MAGIC = 0x504C4D41
-MLA_PLAN_VERSION = 3
+MLA_PLAN_VERSION = 4
+MLA_DECODE_GRAPH_SAFE = 1
 MLA_ITEM_LAST_CHUNK = 1
 
 
@@ -49,7 +50,8 @@ class mla_decode_params(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("kv_lora_rank", ctypes.c_int32),
                 ("qk_rope_head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("num_cus", ctypes.c_int32), ("max_splits", ctypes.c_int32)]
+                ("num_cus", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("max_rows", ctypes.c_int32)]
 
 
 class mla_plan_header(ctypes.Structure):
@@ -60,6 +62,7 @@ class mla_plan_header(ctypes.Structure):
                 ("num_items", ctypes.c_int32), ("num_merges", ctypes.c_int32),
                 ("num_partials", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
                 ("num_workers", ctypes.c_int32), ("max_merge_partials", ctypes.c_int32),
+                ("num_wide_merges", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("num_page_entries", ctypes.c_int64), ("items_offset", ctypes.c_int64),
                 ("merges_offset", ctypes.c_int64), ("workers_offset", ctypes.c_int64),
                 ("plan_bytes", ctypes.c_int64),
@@ -153,9 +156,10 @@ def _check(fn, status):
 
 
 def make_params(num_heads, page_size, kv_dtype=MLA_DTYPE_BF16, out_dtype=MLA_DTYPE_BF16,
-                num_cus=0, max_splits=0, kv_lora_rank=512, qk_rope_head_dim=64):
+                num_cus=0, max_splits=0, kv_lora_rank=512, qk_rope_head_dim=64, flags=0,
+                max_rows=0):
     return mla_decode_params(num_heads, kv_lora_rank, qk_rope_head_dim, page_size, kv_dtype,
-                             out_dtype, num_cus, max_splits)
+                             out_dtype, num_cus, max_splits, flags, max_rows)
 
 
 # ---- the C-ABI entry points, same names ----

@@ -2,6 +2,7 @@
 // host, then launches on the caller's stream. See include/mla_decode.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -145,10 +146,13 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
     const mla_plan_header* h = static_cast<const mla_plan_header*>(plan_h);
     if (h->magic != MLA_PLAN_MAGIC || h->version != MLA_PLAN_VERSION) return MLA_ERR_INVALID_ARG;
     if (h->num_heads != params->num_heads || h->page_size != params->page_size ||
-        h->kv_dtype != params->kv_dtype || h->out_dtype != params->out_dtype)
+        h->kv_dtype != params->kv_dtype || h->out_dtype != params->out_dtype ||
+        h->flags != params->flags)
         return MLA_ERR_PLAN_MISMATCH;
     if ((size_t)h->workspace_bytes > workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
-    if (h->num_items == 0) return MLA_OK;
+    // A graph-safe call launches whatever this plan holds: a later plan may not be empty.
+    const bool graph = (params->flags & MLA_DECODE_GRAPH_SAFE) != 0;
+    if (h->num_items == 0 && !graph) return MLA_OK;
     if (!q_nope_d || !q_rope_d || !kv_cache_d || !kv_indices_d || !out_d) return MLA_ERR_INVALID_ARG;
     if (!aligned16(q_nope_d) || !aligned16(q_rope_d) || !aligned16(kv_cache_d) || !aligned16(out_d) ||
         !aligned16(workspace_d))
@@ -188,6 +192,7 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
     a.cache = static_cast<const uint8_t*>(kv_cache_d);
     a.kv_indices = kv_indices_d;
     a.num_indices = h->num_page_entries;
+    if (graph) a.plan_d = reinterpret_cast<const mla_plan_header*>(ws);  // replays read the current plan's
     a.kv_lens = kv_lens_d;
     a.out = out_d;
     a.lse = lse_d;
@@ -214,7 +219,7 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
     }
     int err = launch_decode(v, params->kv_dtype, params->out_dtype, a, h->num_workers, stream);
     if (err != 0) return MLA_ERR_HIP;
-    if (h->num_merges > 0) {
+    if (h->num_merges > 0 || graph) {
         MergePartialsArgs m{};
         m.merges = reinterpret_cast<const mla_merge_item*>(ws + h->merges_offset);
         m.part_out = a.part_out;
@@ -224,12 +229,20 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
         m.num_heads = params->num_heads;
         m.prefix_out = a.prefix_out;
         m.prefix_lse = a.prefix_lse;
-        // Merges come most partials first (planner); the leading wide ones.
-        const mla_merge_item* hm =
-            reinterpret_cast<const mla_merge_item*>(reinterpret_cast<const char*>(plan_h) + h->merges_offset);
-        int num_wide = 0;
-        while (num_wide < h->num_merges && hm[num_wide].num_partials >= kWideMergePartials) ++num_wide;
-        err = launch_merge_partials(params->out_dtype, m, h->num_merges, num_wide, stream);
+        // Merges come most partials first (planner); the leading ones are wide.
+        int num_merges = h->num_merges, num_wide = h->num_wide_merges;
+        if (graph) {
+            // Fixed grids that bound any plan of these params: every split row
+            // crosses at least one of the G - 1 worker boundaries, a wide one at
+            // least 15, and no boundary is crossed twice.
+            const mla_plan_header* hd = reinterpret_cast<const mla_plan_header*>(ws);
+            m.dev_num_merges = &hd->num_merges;
+            m.dev_num_wide = &hd->num_wide_merges;
+            const int g = h->num_workers;
+            num_merges = std::max(1, g - 1);
+            num_wide = std::max(1, (g - 1 + kWideMergePartials - 2) / (kWideMergePartials - 1));
+        }
+        err = launch_merge_partials(params->out_dtype, m, num_merges, num_wide, stream);
         if (err != 0) return MLA_ERR_HIP;
     }
     return MLA_OK;

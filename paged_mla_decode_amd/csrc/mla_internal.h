@@ -45,6 +45,8 @@ struct DecodeArgs {
     const uint8_t* cache;
     const int32_t* kv_indices;
     int64_t num_indices;     // entries of kv_indices (range of the scalar loads)
+    const mla_plan_header* plan_d;  // graph-safe calls: the plan's device copy, whose
+                                    // num_page_entries replaces num_indices
     const int32_t* kv_lens;  // may be null
     void* out;
     float* lse;  // may be null
@@ -85,6 +87,11 @@ struct MergePartialsArgs {
     int32_t num_heads;
     const void* prefix_out;  // fused prefix merge, or null
     const float* prefix_lse;
+    // Graph-safe launches: the counts in the plan's device copy (null otherwise).
+    // The narrow kernel then takes merges [*num_wide + blockIdx.x] while below
+    // *num_merges, the wide kernel merges [blockIdx.x] below *num_wide.
+    const int32_t* dev_num_merges;
+    const int32_t* dev_num_wide;
 };
 
 // Kernel launchers (device code lives in mla_kernels.hip). Return hipError_t as int.

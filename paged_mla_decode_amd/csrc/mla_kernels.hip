@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
         // them, and each lane picks its own. Tail tokens are clamped to the last
         // valid token, so no load ever leaves the request's pages.
         using IdxVec = typename std::conditional<L::kTPB == 8, i32x8s, i32x16s>::type;
-        const i32x4s idx_rsrc = make_rsrc(a.kv_indices, a.num_indices);
+        const i32x4s idx_rsrc = make_rsrc(a.kv_indices, a.plan_d ? a.plan_d->num_page_entries : a.num_indices);
         IdxVec sidx[kNTok];
         int p0[kNTok];
         auto fetch_idx = [&](int tile) {  // issue the scalar loads for a tile
@@ -547,7 +547,12 @@ __device__ __forceinline__ void merge_store(const MergePartialsArgs& a, const ml
 template <bool OUT32>
 __global__ __launch_bounds__(256) void merge_partials_kernel(const MergePartialsArgs a) {
     constexpr int kBatch = 8;
-    const mla_merge_item mi = a.merges[blockIdx.x];
+    int m = blockIdx.x;
+    if (a.dev_num_merges) {  // graph-safe launch: a fixed grid, the counts from the plan
+        m += *a.dev_num_wide;
+        if (m >= *a.dev_num_merges) return;
+    }
+    const mla_merge_item mi = a.merges[m];
     const int lane = threadIdx.x & 63;
     for (int h = blockIdx.y * 4 + (threadIdx.x >> 6); h < a.num_heads; h += gridDim.y * 4) {
         MergeState st;
@@ -565,6 +570,7 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(const MergePartials
 template <bool OUT32>
 __global__ __launch_bounds__(1024) void merge_partials_wide_kernel(const MergePartialsArgs a) {
     constexpr int kWaves = 16, kBatch = 8;
+    if (a.dev_num_merges && (int)blockIdx.x >= *a.dev_num_wide) return;  // graph-safe launch
     const mla_merge_item mi = a.merges[blockIdx.x];
     const int h = blockIdx.y;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -722,9 +728,23 @@ int launch_decode(const Variant& v, int kv_dtype, int out_dtype, const DecodeArg
 
 int launch_merge_partials(int out_dtype, const MergePartialsArgs& a, int num_merges, int num_wide,
                           void* stream) {
-    if (num_merges <= 0) return 0;
     hipStream_t s = (hipStream_t)stream;
     const bool o32 = out_dtype == MLA_DTYPE_FP32;
+    if (a.dev_num_merges) {
+        // Graph-safe: num_merges and num_wide bound the plan's counts (which the
+        // kernels read from its device copy); both grids are launched.
+        const dim3 gw(num_wide, a.num_heads), bw(1024);
+        const dim3 gn(num_merges, (a.num_heads + 3) / 4), bn(256);
+        if (o32) {
+            merge_partials_wide_kernel<true><<<gw, bw, 0, s>>>(a);
+            merge_partials_kernel<true><<<gn, bn, 0, s>>>(a);
+        } else {
+            merge_partials_wide_kernel<false><<<gw, bw, 0, s>>>(a);
+            merge_partials_kernel<false><<<gn, bn, 0, s>>>(a);
+        }
+        return (int)hipGetLastError();
+    }
+    if (num_merges <= 0) return 0;
     if (num_wide > 0) {
         const dim3 grid(num_wide, a.num_heads), block(1024);
         if (o32)

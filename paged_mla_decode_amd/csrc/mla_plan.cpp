@@ -41,7 +41,7 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 }  // namespace
 
 bool select_variant(const mla_decode_params* p, Variant* v) {
-    if (!p) return false;
+    if (!p || (p->flags & ~MLA_DECODE_GRAPH_SAFE) != 0) return false;
     if (p->kv_lora_rank != kLatent || p->qk_rope_head_dim != kRope || p->page_size < 1) return false;
     if (p->kv_dtype != MLA_DTYPE_BF16 && p->kv_dtype != MLA_DTYPE_FP8_E4M3FN) return false;
     if (p->out_dtype != MLA_DTYPE_BF16 && p->out_dtype != MLA_DTYPE_FP32) return false;
@@ -100,6 +100,11 @@ int32_t plan_bounds(const mla_decode_params* p, int32_t num_cus, int32_t batch, 
     // Items: one per row plus at most one extra per worker boundary (G - 1);
     // the pieces of split rows are at most 2 (G - 1).
     const int64_t G = (int64_t)num_cus * v.wgs_per_cu;
+    // Graph-safe plans are laid out for params.max_rows rows.
+    if (p->flags & MLA_DECODE_GRAPH_SAFE) {
+        if (p->max_rows < 1) return MLA_ERR_INVALID_ARG;
+        num_rows = std::max(num_rows, p->max_rows);
+    }
     const int64_t items = (int64_t)num_rows + G + 1;
     const int64_t partials = std::min<int64_t>(items, 2 * G + 2);
     mla_plan_header h{};
@@ -243,6 +248,13 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
         it.flags = (r.len > 0 && it.kv_end == r.len) ? MLA_ITEM_LAST_CHUNK : 0u;
         items.push_back(it);
     }
+    // Graph-safe plans list every worker (the launch always has all of them);
+    // the ones past the last with work get empty ranges.
+    if (p->flags & MLA_DECODE_GRAPH_SAFE)
+        while (num_workers < G) {
+            worker_begin.push_back((int32_t)items.size());
+            ++num_workers;
+        }
     worker_begin.push_back((int32_t)items.size());
     const int64_t chunk = hi * kTile;
 
@@ -261,9 +273,22 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
     h.chunk_tokens = (int32_t)std::min<int64_t>(chunk, INT32_MAX);
     h.num_workers = num_workers;
     h.max_merge_partials = 0;
-    for (const mla_merge_item& mi : merges) h.max_merge_partials = std::max(h.max_merge_partials, mi.num_partials);
+    for (const mla_merge_item& mi : merges) {
+        h.max_merge_partials = std::max(h.max_merge_partials, mi.num_partials);
+        if (mi.num_partials >= kWideMergePartials) ++h.num_wide_merges;
+    }
+    h.flags = p->flags;
     h.num_page_entries = kv_indptr[batch];
-    layout(h.num_items, h.num_merges, num_workers, num_partials, p->num_heads, partial_elem_bytes(p), &h);
+    if (p->flags & MLA_DECODE_GRAPH_SAFE) {
+        // The layout of plan_bounds for max_rows rows: the same offsets for every
+        // plan of these params, so that captured launches find each array.
+        if (p->max_rows < 1 || num_rows > p->max_rows) return MLA_ERR_INVALID_ARG;
+        const int64_t cap_items = (int64_t)p->max_rows + G + 1;
+        layout((int32_t)cap_items, p->max_rows, (int32_t)G, (int32_t)std::min<int64_t>(cap_items, 2 * G + 2),
+               p->num_heads, partial_elem_bytes(p), &h);
+    } else {
+        layout(h.num_items, h.num_merges, num_workers, num_partials, p->num_heads, partial_elem_bytes(p), &h);
+    }
     if ((size_t)h.plan_bytes > plan_h_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
     char* dst = static_cast<char*>(plan_h);

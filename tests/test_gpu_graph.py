@@ -1,0 +1,82 @@
+"""Graph-safe decode (MLA_DECODE_GRAPH_SAFE): one call captured in a HIP graph,
+replayed after each new plan is built into the same workspace, must give what
+an eager call on that plan gives, bit for bit. Between replays the test does
+eager work of its own and synchronises, and every replay is checked. Plans
+with fewer query rows leave the output rows past them untouched (padding)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import bf16_to_device, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_graph_replay_follows_the_plan(dev, H):
+    from paged_mla_decode_amd.decoder import PagedMlaDecoder
+    ps, B = 16, 6
+    # One pool holds every batch's tokens: batch k uses its own page list of it.
+    lens_set = [[3000, 40, 1, 700, 64, 2000], [10, 5000, 300, 0, 33, 17], [900, 900, 1]]
+    pool = workloads.random_decode_batch(90 + H, [12000], num_heads=H, page_size=ps)
+    cache = bf16_to_device(pool.cache, dev)
+    rng = np.random.Generator(np.random.PCG64(91))
+    q_all = workloads.f32_to_bf16_bits(rng.standard_normal((B, H, 576), dtype=np.float32) * np.float32(0.5))
+    q = bf16_to_device(q_all, dev)
+    qn, qr = q[:, :, :512], q[:, :, 512:]
+    filled = pool.kv_indices  # the pool pages that hold values (the rest are NaN canaries)
+
+    def csr(lens, seed):
+        r = np.random.Generator(np.random.PCG64(seed))
+        npages = [(L + ps - 1) // ps for L in lens]
+        indptr = np.concatenate([[0], np.cumsum(npages)]).astype(np.int32)
+        indices = filled[r.permutation(len(filled))[:indptr[-1]]].astype(np.int32)
+        last = np.array([L - ps * (n - 1) if L > 0 else 0 for L, n in zip(lens, npages)], np.int32)
+        return indptr, indices, last
+
+    batches = [csr(lens, 100 + k) for k, lens in enumerate(lens_set)]
+    max_idx = max(len(b[1]) for b in batches)
+    idx = torch.zeros(max_idx, dtype=torch.int32, device=dev)  # fixed buffer the graph reads
+    dec = PagedMlaDecoder(H, ps, max_batch=B, num_cus=16, device=dev, graph_safe=True)
+    out = torch.zeros((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros((B, H), dtype=torch.float32, device=dev)
+
+    def load(k):
+        indptr, indices, last = batches[k]
+        idx[:len(indices)].copy_(torch.from_numpy(indices))
+        return dec.plan(indptr, last)
+
+    h0 = load(0)
+    assert h0.num_merges > 0
+    dec.run(qn, qr, cache, idx, pool.sm_scale, out=out, lse=lse)  # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s), torch.cuda.graph(g, stream=s):
+        dec.run(qn, qr, cache, idx, pool.sm_scale, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    for rep, k in enumerate([1, 0, 2, 1, 2, 0]):
+        h = load(k)
+        rows = h.num_rows
+        sentinel_out = out[rows:].clone()
+        sentinel_lse = lse[rows:].clone()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = dec.run(qn, qr, cache, idx, pool.sm_scale)  # eager, same plan
+        torch.cuda.synchronize()
+        say(f"H={H} replay {rep}: batch {k} rows={rows} merges={h.num_merges} wide={h.num_wide_merges}")
+        assert torch.equal(out[:rows], ref_out[:rows]) and torch.equal(lse[:rows], ref_lse[:rows]), \
+            f"replay {rep} (batch {k}) differs from the eager call"
+        assert torch.equal(out[rows:], sentinel_out) and torch.equal(lse[rows:], sentinel_lse), \
+            "padding rows were written"
+        out[:rows].zero_()  # eager work between replays

@@ -139,3 +139,57 @@ def test_empty_requests_get_an_empty_item():
     check_invariants(p, batch, h, items, merges, workers)
     empty = [it for it in items if it.kv_begin == it.kv_end]
     assert sorted(it.row for it in empty) == [0, 2]
+
+
+def test_graph_safe_plans_list_every_worker_and_record_their_counts():
+    """Graph-safe plans: all G workers listed (the launch always has them), the
+    flags recorded, the wide-merge count in the header; the planner rejects
+    unknown flags and the decode call rejects a plan built with other flags."""
+    for H, G in ((128, 64), (16, 2 * 64)):
+        p = m.make_params(H, 64, num_cus=64, flags=m.MLA_DECODE_GRAPH_SAFE, max_rows=8)
+        batch = workloads.random_decode_batch(77, [20000, 300, 5, 2600], num_heads=H, page_size=64)
+        pb, _ = m.mla_decode_workspace_size(p, batch.batch, batch.num_rows)
+        plan = np.zeros(pb, dtype=np.uint8)
+        assert m.mla_decode_plan(p, batch.batch, None, batch.kv_indptr, batch.kv_last_page_len,
+                                 plan, pb) == m.MLA_OK
+        h, items, merges, workers = m.read_plan(plan)
+        assert h.flags == m.MLA_DECODE_GRAPH_SAFE and h.num_workers == G
+        assert len(workers) == G + 1 and workers[-1] == h.num_items
+        assert h.num_wide_merges == sum(1 for mi in merges if mi.num_partials >= 16) >= 1
+        # The fixed merge grids of a graph-safe launch bound the plan's counts.
+        assert h.num_merges <= G - 1 and h.num_wide_merges <= -(-(G - 1) // 15)
+    bad = m.make_params(16, 1, num_cus=8, flags=2)
+    plan = np.zeros(1 << 16, dtype=np.uint8)
+    assert m.mla_decode_plan(bad, 1, None, np.array([0, 3], np.int32), None, plan,
+                             plan.size) == m.MLA_ERR_UNSUPPORTED
+
+
+def test_graph_safe_plans_share_one_layout():
+    """Captured launches keep the workspace addresses of the plan they were
+    captured with, so every graph-safe plan of the same params must put its
+    items, merges, worker table and partials at the same offsets, whatever
+    its batch: those of the bound for max_rows rows."""
+    fields = ("items_offset", "merges_offset", "workers_offset", "plan_bytes", "partial_out_offset",
+              "partial_lse_offset", "workspace_bytes")
+    for H in (16, 128):
+        p = m.make_params(H, 16, num_cus=16, flags=m.MLA_DECODE_GRAPH_SAFE, max_rows=6)
+        pb, wb = m.mla_decode_workspace_size(p, 6, 6)
+        seen = []
+        for k, lens in enumerate([[3000, 40, 1, 700, 64, 2000], [10, 5000, 300, 0, 33, 17], [900, 900, 1], [5]]):
+            batch = workloads.random_decode_batch(50 + k, lens, num_heads=H, page_size=16)
+            plan = np.zeros(pb, dtype=np.uint8)
+            assert m.mla_decode_plan(p, batch.batch, None, batch.kv_indptr, batch.kv_last_page_len,
+                                     plan, pb) == m.MLA_OK
+            h = m.read_plan(plan)[0]
+            seen.append((h.num_items, h.num_merges, tuple(getattr(h, f) for f in fields)))
+        assert len({s[0:2] for s in seen}) > 1, "the batches should differ in items or merges"
+        assert len({s[2] for s in seen}) == 1, seen
+        assert seen[0][2][3] == pb and seen[0][2][6] == wb
+        # More rows than max_rows: rejected; graph-safe without max_rows: rejected.
+        big = workloads.random_decode_batch(60, [5] * 7, num_heads=H, page_size=16)
+        plan = np.zeros(1 << 22, dtype=np.uint8)
+        assert m.mla_decode_plan(p, 7, None, big.kv_indptr, big.kv_last_page_len, plan,
+                                 plan.size) == m.MLA_ERR_INVALID_ARG
+        p0 = m.make_params(H, 16, num_cus=16, flags=m.MLA_DECODE_GRAPH_SAFE)
+        assert m.mla_decode_plan(p0, 1, None, np.array([0, 1], np.int32), None, plan,
+                                 plan.size) == m.MLA_ERR_INVALID_ARG
