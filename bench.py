@@ -27,7 +27,8 @@ algorithmic bytes (weights, inputs and outputs, each once) / step time.
 With --workload tree_verify it times the tree-verify cascade of the PR 49477
 analysis (16 requests, 2048-token prefix, 64 drafts at depth <= 8, H=128):
 the suffix-table compaction, the prefix attention of all 1024 draft rows, and
-the suffix attention merged into the prefix state (mla_decode_suffix_merge).
+the suffix attention merged into the prefix state (a suffix decode and
+mla_merge_states; the fused mla_decode_suffix_merge is timed beside it).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -500,10 +501,13 @@ def bench_tree_verify(args):
                         pre.sm_scale, kv_lens=seqlens, stream=stream)
         merge_states(o, l, so, sl, out=o, s_out=l, stream=stream)
 
+    # The step takes the separate suffix decode + merge: at <= 8 suffix tokens per
+    # row its items are output-bound, and the fused merge's prefix reads, which
+    # sit in the output stage, measured slower. Both are timed below.
     def step(i):
         ts = compact(i)
         prefix(i)
-        suffix(i, ts)
+        suffix_separate(i, ts)
 
     for i in range(args.warmup):
         step(i)
