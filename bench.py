@@ -26,9 +26,10 @@ algorithmic bytes (weights, inputs and outputs, each once) / step time.
 
 With --workload tree_verify it times the tree-verify cascade of the PR 49477
 analysis (16 requests, 2048-token prefix, 64 drafts at depth <= 8, H=128):
-the suffix-table compaction, the prefix attention of all 1024 draft rows, and
-the suffix attention merged into the prefix state (a suffix decode and
-mla_merge_states; the fused mla_decode_suffix_merge is timed beside it).
+the suffix-table compaction, then every draft row's attention over its prefix
+and its visible drafts in one pass (mla_decode_tree_verify). The two-pass
+cascade (prefix decode, suffix decode, LSE merge, separate or fused) is timed
+beside it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -475,6 +476,11 @@ def bench_tree_verify(args):
     ds = PagedMlaDecoder(H, 1, max_batch=N, max_rows=N, device=dev)
     hs = ds.plan(np.arange(N + 1, dtype=np.int32) * D, np.ones(N, dtype=np.int32))
     plan_us = (time.perf_counter() - t0) * 1e6
+    # Single pass: every row over its prefix and then its visible drafts.
+    d1 = PagedMlaDecoder(H, 1, max_batch=B, max_rows=N, device=dev, suffix_tokens=D)
+    t0 = time.perf_counter()
+    h1 = d1.plan(pre.kv_indptr, pre.kv_last_page_len, pre.qo_indptr)
+    plan1_us = (time.perf_counter() - t0) * 1e6
     outs = [(torch.empty((N, H, 512), dtype=torch.bfloat16, device=dev),
              torch.empty((N, H), dtype=torch.float32, device=dev)) for _ in sets]
     tables = [tree_suffix_compact(s["mask"], s["r2t"], s["plen"], W) for s in sets]
@@ -501,13 +507,16 @@ def bench_tree_verify(args):
                         pre.sm_scale, kv_lens=seqlens, stream=stream)
         merge_states(o, l, so, sl, out=o, s_out=l, stream=stream)
 
-    # The step takes the separate suffix decode + merge: at <= 8 suffix tokens per
-    # row its items are output-bound, and the fused merge's prefix reads, which
-    # sit in the output stage, measured slower. Both are timed below.
+    def single(i, table_seqlens):
+        s, (o, l) = sets[i % 2], outs[i % 2]
+        table, seqlens = table_seqlens
+        d1.run_tree_verify(s["qn"], s["qr"], s["cache"], s["idx"], table, seqlens, pre.sm_scale,
+                           out=o, lse=l, stream=stream)
+
+    # The step: compaction, then one pass over prefix and visible drafts. The
+    # two-pass cascade (prefix, suffix, merge; separate or fused) is timed too.
     def step(i):
-        ts = compact(i)
-        prefix(i)
-        suffix_separate(i, ts)
+        single(i, compact(i))
 
     for i in range(args.warmup):
         step(i)
@@ -531,6 +540,7 @@ def bench_tree_verify(args):
     prefix_us = launch_avg_us(prefix)
     suffix_us = launch_avg_us(lambda i: suffix(i, tables[i % 2]))
     separate_us = launch_avg_us(lambda i: suffix_separate(i, tables[i % 2]))
+    single_us = launch_avg_us(lambda i: single(i, tables[i % 2]))
 
     seq = tables[0][1].cpu().numpy()
     prefix_tokens = int(pre.seq_lens.astype(np.int64).repeat(W).sum())
@@ -541,9 +551,12 @@ def bench_tree_verify(args):
     gbs = latent_bytes / (ms_per_step * 1e-3) / 1e9
     prefix_flops = costs.mla_decode_flops(prefix_tokens, H)
     tflops = prefix_flops / (prefix_us * 1e-6) / 1e12
-    log(f"step {ms_per_step * 1e3:.1f} us: compaction {compact_us:.1f}, prefix {prefix_us:.1f} "
-        f"({tflops:.0f} TFLOP/s), suffix+merge {suffix_us:.1f} (separate suffix then merge: "
-        f"{separate_us:.1f}); prefix plan {hp.num_items} items, suffix plan {hs.num_items} items")
+    single_flops = costs.mla_decode_flops(attended, H)
+    single_tflops = single_flops / (single_us * 1e-6) / 1e12
+    log(f"step {ms_per_step * 1e3:.1f} us: compaction {compact_us:.1f}, single pass {single_us:.1f} "
+        f"({single_tflops:.0f} TFLOP/s); two-pass cascade: prefix {prefix_us:.1f} ({tflops:.0f} "
+        f"TFLOP/s), suffix+merge fused {suffix_us:.1f}, separate {separate_us:.1f}; plans: single "
+        f"{h1.num_items} items, prefix {hp.num_items}, suffix {hs.num_items}")
     res = {
         "metric": "MLA decode latent-cache GB/s (% of HBM peak) and tokens/s, DeepSeek-V3 shapes",
         "value": round(gbs, 2),
@@ -564,19 +577,22 @@ def bench_tree_verify(args):
         "tokens_per_s": round(N / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "unique_latent_bytes": unique_bytes,
-        "plan_us": round(plan_us, 1),
-        "phases_us": {"compaction": round(compact_us, 2), "prefix": round(prefix_us, 2),
-                      "suffix_merge": round(suffix_us, 2), "suffix_then_merge_states": round(separate_us, 2)},
+        "plan_us": round(plan1_us, 1),
+        "phases_us": {"compaction": round(compact_us, 2), "single_pass": round(single_us, 2),
+                      "two_pass_prefix": round(prefix_us, 2),
+                      "two_pass_suffix_merge_fused": round(suffix_us, 2),
+                      "two_pass_suffix_then_merge_states": round(separate_us, 2)},
         "roofline": {
-            "kernel": "prefix mla_decode launch (1024 draft rows x 2048 prefix tokens, H=128)",
+            "kernel": "mla_decode_tree_verify launch (1024 draft rows x (2048 prefix + <= 8 draft) "
+                      "tokens, H=128)",
             "bound": "mfma",
-            "achieved": round(tflops, 2),
+            "achieved": round(single_tflops, 2),
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "frac": round(single_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
             "traffic": measured_traffic("mla_decode_tree_verify"),
-            "algorithmic_flops_per_launch": prefix_flops,
-            "launch_avg_us": round(prefix_us, 2),
+            "algorithmic_flops_per_launch": single_flops,
+            "launch_avg_us": round(single_us, 2),
         },
     }
     if not args.no_cpu_baseline:

@@ -67,6 +67,9 @@ typedef struct {
     int32_t max_rows;         /* graph-safe plans: the most query rows any plan will hold
                                  (>= 1); it fixes where the plan's arrays and the partials
                                  sit in the workspace. Ignored otherwise. */
+    int32_t suffix_tokens;    /* mla_decode_tree_verify only: the most suffix slots a row
+                                 adds after its request's tokens, in [1, 256]; 0 for every
+                                 other call */
 } mla_decode_params;
 
 /*
@@ -95,7 +98,7 @@ const char* mla_status_string(int32_t status);
  * of the device workspace. It is plain data: tests may read it.
  */
 #define MLA_PLAN_MAGIC 0x504C4D41u /* "AMLP" */
-#define MLA_PLAN_VERSION 4
+#define MLA_PLAN_VERSION 5
 
 typedef struct {
     uint32_t magic;
@@ -113,6 +116,8 @@ typedef struct {
     int32_t max_merge_partials; /* most partials any one merged row has (0 without merges) */
     int32_t num_wide_merges; /* the leading merges, those of at least 16 partials */
     int32_t flags;          /* the params' flags the plan was built with */
+    int32_t suffix_tokens;  /* the params' suffix_tokens: each row is planned that much longer */
+    int32_t reserved;
     int64_t num_page_entries; /* kv_indptr[batch]: entries of kv_indices the batch uses */
     int64_t items_offset;   /* byte offset of mla_work_item[num_items] */
     int64_t merges_offset;  /* byte offset of mla_merge_item[num_merges] */
@@ -293,6 +298,39 @@ int32_t mla_decode_suffix_merge(const mla_decode_params* params, const void* pla
                                 const void* kv_cache_d, float kv_scale, const int32_t* kv_indices_d,
                                 const int32_t* kv_lens_d, float sm_scale, const void* prefix_out_d,
                                 const float* prefix_lse_d, void* out_d, float* lse_d, void* stream);
+
+/*
+ * mla_decode_tree_verify - the tree-verify attention of the PR 49477 analysis
+ * in one pass: every draft row attends to its request's prefix and, in the same
+ * softmax, to its visible draft slots, instead of a prefix pass, a suffix pass
+ * over the compacted table (section 2) and an LSE merge of the two (section 3).
+ * The result is the cascade's: attention over the union of the two token sets.
+ *
+ * For query row n of request b (rows by qo_indptr, as planned): the request's
+ * L_b planned tokens through kv_indices_d, then the pool rows
+ * suffix_table_d[n*suffix_stride + j] for j < min(suffix_lens_d[n], S), with
+ * S = params.suffix_tokens. These are the page_table and cache_seqlens that
+ * mla_tree_suffix_compact writes (its table_stride as suffix_stride, S the
+ * max_tree_depth of its truncation); rows with suffix_lens_d[n] = 0 attend to
+ * the prefix only.
+ *
+ * Requirements: params.num_heads = 128, params.page_size = 1 (suffix entries
+ * are token slots, that is pool rows), params.suffix_tokens = S in [1, 256],
+ * and a plan built with those params (each row is planned S tokens longer, its
+ * last chunk holding all of them). suffix_stride >= S. Every suffix entry read
+ * is a row of the pool. Other arguments as for mla_decode (no kv_lens_d).
+ * Returns those of mla_decode; MLA_ERR_INVALID_ARG for a missing table or
+ * lengths, or when a plan with suffix_tokens > 0 reaches any other call.
+ */
+int32_t mla_decode_tree_verify(const mla_decode_params* params, const void* plan_h,
+                               const void* workspace_d, size_t workspace_bytes,
+                               const void* q_nope_d, int64_t q_nope_stride_n,
+                               int64_t q_nope_stride_h, const void* q_rope_d,
+                               int64_t q_rope_stride_n, int64_t q_rope_stride_h,
+                               const void* kv_cache_d, float kv_scale, const int32_t* kv_indices_d,
+                               const int32_t* suffix_table_d, int64_t suffix_stride,
+                               const int32_t* suffix_lens_d, float sm_scale, void* out_d,
+                               float* lse_d, void* stream);
 
 /*
  * mla_merge_states - merge two attention states over disjoint token sets:

@@ -17,7 +17,8 @@ _BINDING = (
     "MLA_ERR_WORKSPACE_TOO_SMALL", "MLA_ITEM_LAST_CHUNK", "MLA_DECODE_GRAPH_SAFE", "MLA_OK",
     "MLA_PLAN_VERSION", "MlaError",
     "make_params", "mla_absorb_query", "mla_decode", "mla_decode_append", "mla_decode_plan",
-    "mla_decode_suffix_merge", "mla_decode_variant", "mla_decode_workspace_size",
+    "mla_decode_suffix_merge", "mla_decode_tree_verify", "mla_decode_variant",
+    "mla_decode_workspace_size",
     "mla_merge_states", "mla_project_output", "mla_status_string", "mla_tree_suffix_compact",
     "read_plan")
 # torch-based helpers, so that the host-only ABI can be used without a GPU.

@@ -41,7 +41,7 @@ MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP32 = 1
 MLA_DTYPE_FP8_E4M3FN = 2
 MLA_PLAN_MAGIC = 0x504C4D41
-MLA_PLAN_VERSION = 4
+MLA_PLAN_VERSION = 5
 MLA_DECODE_GRAPH_SAFE = 1
 MLA_ITEM_LAST_CHUNK = 1
 
@@ -51,7 +51,8 @@ class mla_decode_params(ctypes.Structure):
                 ("qk_rope_head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("num_cus", ctypes.c_int32), ("max_splits", ctypes.c_int32),
-                ("flags", ctypes.c_int32), ("max_rows", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("max_rows", ctypes.c_int32),
+                ("suffix_tokens", ctypes.c_int32)]
 
 
 class mla_plan_header(ctypes.Structure):
@@ -63,6 +64,7 @@ class mla_plan_header(ctypes.Structure):
                 ("num_partials", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
                 ("num_workers", ctypes.c_int32), ("max_merge_partials", ctypes.c_int32),
                 ("num_wide_merges", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("suffix_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("num_page_entries", ctypes.c_int64), ("items_offset", ctypes.c_int64),
                 ("merges_offset", ctypes.c_int64), ("workers_offset", ctypes.c_int64),
                 ("plan_bytes", ctypes.c_int64),
@@ -102,6 +104,9 @@ _lib.mla_decode_append.argtypes = [_PARAMS, _p, _p, _sz, _p, _i64, _i64, _p, _i6
 _lib.mla_decode_suffix_merge.restype = _i32
 _lib.mla_decode_suffix_merge.argtypes = [_PARAMS, _p, _p, _sz, _p, _i64, _i64, _p, _i64, _i64, _p,
                                          _f32, _p, _p, _f32, _p, _p, _p, _p, _p]
+_lib.mla_decode_tree_verify.restype = _i32
+_lib.mla_decode_tree_verify.argtypes = [_PARAMS, _p, _p, _sz, _p, _i64, _i64, _p, _i64, _i64, _p,
+                                        _f32, _p, _p, _i64, _p, _f32, _p, _p, _p]
 _lib.mla_merge_states.restype = _i32
 _lib.mla_merge_states.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _p]
 _lib.mla_tree_suffix_compact.restype = _i32
@@ -113,6 +118,7 @@ for _fn in (_lib.mla_absorb_query, _lib.mla_project_output):
 
 EXPORTED_SYMBOLS = ("mla_status_string", "mla_decode_variant", "mla_decode_workspace_size",
                     "mla_decode_plan", "mla_decode", "mla_decode_append", "mla_decode_suffix_merge",
+                    "mla_decode_tree_verify",
                     "mla_merge_states",
                     "mla_tree_suffix_compact", "mla_absorb_query", "mla_project_output")
 
@@ -157,9 +163,9 @@ def _check(fn, status):
 
 def make_params(num_heads, page_size, kv_dtype=MLA_DTYPE_BF16, out_dtype=MLA_DTYPE_BF16,
                 num_cus=0, max_splits=0, kv_lora_rank=512, qk_rope_head_dim=64, flags=0,
-                max_rows=0):
+                max_rows=0, suffix_tokens=0):
     return mla_decode_params(num_heads, kv_lora_rank, qk_rope_head_dim, page_size, kv_dtype,
-                             out_dtype, num_cus, max_splits, flags, max_rows)
+                             out_dtype, num_cus, max_splits, flags, max_rows, suffix_tokens)
 
 
 # ---- the C-ABI entry points, same names ----
@@ -224,6 +230,18 @@ def mla_decode_suffix_merge(params, plan_h, workspace_d, workspace_bytes, q_nope
         int(q_rope_stride_h), _ptr(kv_cache_d), float(kv_scale), _ptr(kv_indices_d), _ptr(kv_lens_d),
         float(sm_scale), _ptr(prefix_out_d), _ptr(prefix_lse_d), _ptr(out_d), _ptr(lse_d),
         _stream(stream))
+
+
+def mla_decode_tree_verify(params, plan_h, workspace_d, workspace_bytes, q_nope_d,
+                           q_nope_stride_n, q_nope_stride_h, q_rope_d, q_rope_stride_n,
+                           q_rope_stride_h, kv_cache_d, kv_scale, kv_indices_d, suffix_table_d,
+                           suffix_stride, suffix_lens_d, sm_scale, out_d, lse_d, stream=None):
+    return _lib.mla_decode_tree_verify(
+        ctypes.byref(params), _ptr(plan_h), _ptr(workspace_d), int(workspace_bytes), _ptr(q_nope_d),
+        int(q_nope_stride_n), int(q_nope_stride_h), _ptr(q_rope_d), int(q_rope_stride_n),
+        int(q_rope_stride_h), _ptr(kv_cache_d), float(kv_scale), _ptr(kv_indices_d),
+        _ptr(suffix_table_d), int(suffix_stride), _ptr(suffix_lens_d), float(sm_scale), _ptr(out_d),
+        _ptr(lse_d), _stream(stream))
 
 
 def mla_merge_states(v_a_d, s_a_d, v_b_d, s_b_d, v_out_d, s_out_d, num_rows, head_dim, v_dtype,

@@ -111,6 +111,13 @@ struct PrefixIn {
     const float* lse;
 };
 
+// The suffix slots of mla_decode_tree_verify.
+struct TreeIn {
+    const int32_t* table;
+    int64_t stride;
+    const int32_t* lens;
+};
+
 // Two byte ranges that are either the same or disjoint.
 bool same_or_disjoint(const void* x, const void* y, size_t bytes) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
@@ -139,7 +146,8 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
                     int64_t q_nope_stride_h, const void* q_rope_d, int64_t q_rope_stride_n,
                     int64_t q_rope_stride_h, const void* kv_cache_d, float kv_scale,
                     const int32_t* kv_indices_d, const int32_t* kv_lens_d, const AppendIn* app,
-                    const PrefixIn* pre, float sm_scale, void* out_d, float* lse_d, void* stream) {
+                    const PrefixIn* pre, const TreeIn* tree, float sm_scale, void* out_d, float* lse_d,
+                    void* stream) {
     if (!params || !plan_h || !workspace_d) return MLA_ERR_INVALID_ARG;
     Variant v;
     if (!select_variant(params, &v)) return MLA_ERR_UNSUPPORTED;
@@ -147,8 +155,12 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
     if (h->magic != MLA_PLAN_MAGIC || h->version != MLA_PLAN_VERSION) return MLA_ERR_INVALID_ARG;
     if (h->num_heads != params->num_heads || h->page_size != params->page_size ||
         h->kv_dtype != params->kv_dtype || h->out_dtype != params->out_dtype ||
-        h->flags != params->flags)
+        h->flags != params->flags || h->suffix_tokens != params->suffix_tokens)
         return MLA_ERR_PLAN_MISMATCH;
+    // suffix_tokens plans are for the tree-verify call, and it needs one.
+    if ((params->suffix_tokens > 0) != (tree != nullptr)) return MLA_ERR_INVALID_ARG;
+    if (tree && (!tree->table || !tree->lens || tree->stride < params->suffix_tokens))
+        return MLA_ERR_INVALID_ARG;
     if ((size_t)h->workspace_bytes > workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
     // A graph-safe call launches whatever this plan holds: a later plan may not be empty.
     const bool graph = (params->flags & MLA_DECODE_GRAPH_SAFE) != 0;
@@ -217,6 +229,12 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
         a.prefix_out = pre->out;
         a.prefix_lse = pre->lse;
     }
+    if (tree) {
+        a.sfx_table = tree->table;
+        a.sfx_stride = tree->stride;
+        a.sfx_lens = tree->lens;
+        a.sfx_max = params->suffix_tokens;
+    }
     int err = launch_decode(v, params->kv_dtype, params->out_dtype, a, h->num_workers, stream);
     if (err != 0) return MLA_ERR_HIP;
     if (h->num_merges > 0 || graph) {
@@ -260,8 +278,24 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
                    void* out_d, float* lse_d, void* stream) {
     return decode_impl(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_stride_n,
                        q_nope_stride_h, q_rope_d, q_rope_stride_n, q_rope_stride_h, kv_cache_d,
-                       kv_scale, kv_indices_d, kv_lens_d, nullptr, nullptr, sm_scale, out_d, lse_d,
-                       stream);
+                       kv_scale, kv_indices_d, kv_lens_d, nullptr, nullptr, nullptr, sm_scale, out_d,
+                       lse_d, stream);
+}
+
+int32_t mla_decode_tree_verify(const mla_decode_params* params, const void* plan_h,
+                               const void* workspace_d, size_t workspace_bytes,
+                               const void* q_nope_d, int64_t q_nope_stride_n,
+                               int64_t q_nope_stride_h, const void* q_rope_d,
+                               int64_t q_rope_stride_n, int64_t q_rope_stride_h,
+                               const void* kv_cache_d, float kv_scale, const int32_t* kv_indices_d,
+                               const int32_t* suffix_table_d, int64_t suffix_stride,
+                               const int32_t* suffix_lens_d, float sm_scale, void* out_d,
+                               float* lse_d, void* stream) {
+    const TreeIn tree{suffix_table_d, suffix_stride, suffix_lens_d};
+    return decode_impl(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_stride_n,
+                       q_nope_stride_h, q_rope_d, q_rope_stride_n, q_rope_stride_h, kv_cache_d,
+                       kv_scale, kv_indices_d, nullptr, nullptr, nullptr, &tree, sm_scale, out_d,
+                       lse_d, stream);
 }
 
 int32_t mla_decode_suffix_merge(const mla_decode_params* params, const void* plan_h,
@@ -275,8 +309,8 @@ int32_t mla_decode_suffix_merge(const mla_decode_params* params, const void* pla
     const PrefixIn pre{prefix_out_d, prefix_lse_d};
     return decode_impl(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_stride_n,
                        q_nope_stride_h, q_rope_d, q_rope_stride_n, q_rope_stride_h, kv_cache_d,
-                       kv_scale, kv_indices_d, kv_lens_d, nullptr, &pre, sm_scale, out_d, lse_d,
-                       stream);
+                       kv_scale, kv_indices_d, kv_lens_d, nullptr, &pre, nullptr, sm_scale, out_d,
+                       lse_d, stream);
 }
 
 int32_t mla_decode_append(const mla_decode_params* params, const void* plan_h,
@@ -289,8 +323,8 @@ int32_t mla_decode_append(const mla_decode_params* params, const void* plan_h,
     const AppendIn app{c_new_d, c_new_stride, k_pe_new_d, k_pe_new_stride};
     return decode_impl(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_stride_n,
                        q_nope_stride_h, q_rope_d, q_rope_stride_n, q_rope_stride_h, kv_cache_d,
-                       kv_scale, kv_indices_d, nullptr, &app, nullptr, sm_scale, out_d, lse_d,
-                       stream);
+                       kv_scale, kv_indices_d, nullptr, &app, nullptr, nullptr, sm_scale, out_d,
+                       lse_d, stream);
 }
 
 int32_t mla_merge_states(const void* v_a_d, const float* s_a_d, const void* v_b_d,

@@ -106,6 +106,17 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         const int kv_begin = it.kv_begin;
         int kv_end = it.kv_end;
         if (a.kv_lens) kv_end = min(kv_end, a.kv_lens[it.request]);
+        // Single-pass tree verify: the row's last chunk ends with its suffix
+        // slots, tokens [lb, lb + visible) read from its row of the table.
+        int lb = kv_end;
+        const int32_t* sfx_row = nullptr;
+        if (MODE == kModeTree && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
+            // Wave-uniform values, kept in scalar registers.
+            const int row = __builtin_amdgcn_readfirstlane(it.row);
+            lb = __builtin_amdgcn_readfirstlane(it.kv_end) - a.sfx_max;
+            kv_end = lb + min(max(a.sfx_lens[row], 0), a.sfx_max);
+            sfx_row = a.sfx_table + (int64_t)row * a.sfx_stride;
+        }
         const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + kTile - 1) / kTile : 0;
         const int hq = lane & 31, gq = lane >> 5;
         const int head = it.head_begin + 32 * w + hq;  // this lane's head in the score phase
@@ -120,7 +131,9 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         auto page_of = [&](int tok) { return a.page_shift >= 0 ? tok >> a.page_shift : tok / ps; };
         auto issue_idx = [&](int tile, int slot) {
             const int tok = min(kv_begin + tile * kTile + tb * L::kTPB + min(lane, L::kTPB - 1), kv_end - 1);
-            dma4(page_table + page_of(tok), (LDS_AS int*)&idx_ring[slot][w][0]);
+            const int32_t* src = page_table + page_of(tok);
+            if (MODE == kModeTree && tok >= lb) src = sfx_row + (tok - lb);
+            dma4(src, (LDS_AS int*)&idx_ring[slot][w][0]);
         };
         auto issue_tile = [&](int tile, int slot) {
             const int tau = min(kv_begin + tile * kTile + L::block_token(tb, lane), kv_end - 1);
@@ -547,11 +560,13 @@ int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num
     const bool o32 = out_dtype == MLA_DTYPE_FP32;
     // The fused append and the fused prefix merge are instantiations of their
     // own, so the plain decode carries none of their arguments or branches.
-    const int mode = a.c_new ? kModeAppend : a.prefix_lse ? kModeMerge : kModePlain;
+    const int mode = a.c_new ? kModeAppend : a.prefix_lse ? kModeMerge : a.sfx_table ? kModeTree : kModePlain;
     auto go = [&](auto kv8_t, auto o32_t) {
         constexpr bool K = decltype(kv8_t)::value, O = decltype(o32_t)::value;
         if (mode == kModeAppend)
             decode_h128_kernel<K, O, kModeAppend><<<grid, block, 0, s>>>(a);
+        else if (mode == kModeTree)
+            decode_h128_kernel<K, O, kModeTree><<<grid, block, 0, s>>>(a);
         else if (mode == kModeMerge)
             decode_h128_kernel<K, O, kModeMerge><<<grid, block, 0, s>>>(a);
         else

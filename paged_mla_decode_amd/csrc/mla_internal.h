@@ -72,11 +72,22 @@ struct DecodeArgs {
     // merge kernels. out/lse may be the same memory as prefix_out/prefix_lse.
     const void* prefix_out;
     const float* prefix_lse;
+    // Single-pass tree verify (null sfx_table: none). A row's last chunk (planned
+    // sfx_max tokens longer than its request) takes tokens [L, L + sfx_lens[row])
+    // from the pool rows sfx_table[row * sfx_stride + j] instead of the page table.
+    const int32_t* sfx_table;
+    int64_t sfx_stride;
+    const int32_t* sfx_lens;
+    int32_t sfx_max;
 };
 
 // Decode kernel instantiations: the plain decode, the fused append, the fused
-// prefix merge. The extra arguments of the last two never reach the first.
-enum DecodeMode { kModePlain = 0, kModeAppend = 1, kModeMerge = 2 };
+// prefix merge, the single-pass tree verify (128-head kernel only). The extra
+// arguments of the last three never reach the first.
+enum DecodeMode { kModePlain = 0, kModeAppend = 1, kModeMerge = 2, kModeTree = 3 };
+
+// Single-pass tree verify: at most this many suffix slots per row.
+constexpr int kMaxSuffixTokens = 256;
 
 struct MergePartialsArgs {
     const mla_merge_item* merges;

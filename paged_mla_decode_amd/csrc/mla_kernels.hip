@@ -691,7 +691,9 @@ static int launch_decode_hs(int kv_dtype, int out_dtype, const DecodeArgs& a, in
     const dim3 grid(n), block(64 * HS);
     const bool kv8 = kv_dtype == MLA_DTYPE_FP8_E4M3FN;
     const bool o32 = out_dtype == MLA_DTYPE_FP32;
-    // The fused append and prefix merge are instantiations of their own.
+    // The fused append and prefix merge are instantiations of their own. The
+    // single-pass tree verify exists for the 128-head kernel only.
+    if (a.sfx_table) return (int)hipErrorInvalidValue;
     const int mode = a.c_new ? kModeAppend : a.prefix_lse ? kModeMerge : kModePlain;
     auto go = [&](auto kv8_t, auto o32_t) {
         constexpr bool K = decltype(kv8_t)::value, O = decltype(o32_t)::value;

@@ -42,6 +42,9 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 bool select_variant(const mla_decode_params* p, Variant* v) {
     if (!p || (p->flags & ~MLA_DECODE_GRAPH_SAFE) != 0) return false;
+    // Single-pass tree verify: the 128-head kernel over token slots (page size 1).
+    if (p->suffix_tokens < 0 || p->suffix_tokens > kMaxSuffixTokens) return false;
+    if (p->suffix_tokens > 0 && (p->num_heads != 128 || p->page_size != 1)) return false;
     if (p->kv_lora_rank != kLatent || p->qk_rope_head_dim != kRope || p->page_size < 1) return false;
     if (p->kv_dtype != MLA_DTYPE_BF16 && p->kv_dtype != MLA_DTYPE_FP8_E4M3FN) return false;
     if (p->out_dtype != MLA_DTYPE_BF16 && p->out_dtype != MLA_DTYPE_FP32) return false;
@@ -136,6 +139,7 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
             if (last < 1 || last > ps) return MLA_ERR_INVALID_ARG;
             L = (np - 1) * ps + last;
         }
+        L += p->suffix_tokens;  // tree verify: room for each row's suffix slots
         if (L > INT32_MAX - kTile) return MLA_ERR_UNSUPPORTED;
         len[b] = L;
         const int64_t rows = qo_indptr ? (int64_t)qo_indptr[b + 1] - qo_indptr[b] : 1;
@@ -149,6 +153,7 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
     const int64_t max_splits = p->max_splits > 0 ? p->max_splits : kDefaultMaxSplits;
     const int64_t item_cost = v.item_cost;
     const int64_t min_piece = item_cost;  // a piece is at least as long as its fixed cost
+    const int64_t sfx = p->suffix_tokens;
 
     struct Row {
         int32_t row, request;
@@ -186,6 +191,12 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
                 // where the row allows it.
                 if (take < rem && rem - take < min_piece) take = rem >= 2 * min_piece ? rem - min_piece : rem;
                 if (take < rem && take < min_piece) take = std::min(rem, min_piece);
+                // Tree verify: no cut inside a row's last suffix_tokens tokens, so
+                // that its last chunk holds every suffix slot.
+                if (sfx > 0 && take < rem && (t + take) * kTile > rows[i].len - sfx) {
+                    const int64_t cut = (rows[i].len - sfx) / kTile;
+                    take = cut > t ? cut - t : rem;
+                }
                 if (out) out->push_back(Piece{(int32_t)i, (int32_t)w, t, t + take});
                 t += take;
                 rem -= take;
@@ -278,6 +289,7 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
         if (mi.num_partials >= kWideMergePartials) ++h.num_wide_merges;
     }
     h.flags = p->flags;
+    h.suffix_tokens = p->suffix_tokens;
     h.num_page_entries = kv_indptr[batch];
     if (p->flags & MLA_DECODE_GRAPH_SAFE) {
         // The layout of plan_bounds for max_rows rows: the same offsets for every

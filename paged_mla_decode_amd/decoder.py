@@ -18,14 +18,16 @@ class PagedMlaDecoder:
 
     def __init__(self, num_heads: int, page_size: int, max_batch: int, max_rows: int | None = None,
                  kv_dtype: str = "bf16", out_dtype: str = "bf16", num_cus: int = 0,
-                 max_splits: int = 0, device="cuda", graph_safe: bool = False):
+                 max_splits: int = 0, device="cuda", graph_safe: bool = False,
+                 suffix_tokens: int = 0):
         self.device = torch.device(device)
         max_rows = max_batch if max_rows is None else max_rows
         # Graph-safe: launches and workspace addresses fixed for up to max_rows rows.
         self.params = B.make_params(num_heads, page_size, _DTYPES[kv_dtype], _DTYPES[out_dtype],
                                     num_cus, max_splits,
                                     flags=B.MLA_DECODE_GRAPH_SAFE if graph_safe else 0,
-                                    max_rows=max_rows if graph_safe else 0)
+                                    max_rows=max_rows if graph_safe else 0,
+                                    suffix_tokens=suffix_tokens)
         self.kv_dtype = kv_dtype
         self.out_dtype = out_dtype
         self.num_heads = num_heads
@@ -127,6 +129,30 @@ class PagedMlaDecoder:
                                        lse, stream)
         if st != B.MLA_OK:
             raise B.MlaError("mla_decode_suffix_merge", st)
+        return out, lse
+
+
+    def run_tree_verify(self, q_nope, q_rope, kv_cache, kv_indices, suffix_table, suffix_lens,
+                        sm_scale, kv_scale=1.0, out=None, lse=None, stream=None):
+        """Each planned row over its request's tokens and then its visible suffix
+        slots (suffix_table [rows, stride] int32 pool rows, suffix_lens [rows]),
+        in one pass (mla_decode_tree_verify). Needs suffix_tokens > 0."""
+        h = self.header()
+        N, H = h.num_rows, self.num_heads
+        if out is None:
+            dt = torch.float32 if self.out_dtype == "fp32" else torch.bfloat16
+            out = torch.empty((N, H, 512), dtype=dt, device=self.device)
+        if lse is None:
+            lse = torch.empty((N, H), dtype=torch.float32, device=self.device)
+        assert q_nope.stride(-1) == 1 and q_rope.stride(-1) == 1 and suffix_table.stride(-1) == 1
+        stream = stream or torch.cuda.current_stream(self.device)
+        st = B.mla_decode_tree_verify(self.params, self.plan_h, self.workspace, self.workspace.numel(),
+                                      q_nope, q_nope.stride(0), q_nope.stride(1), q_rope,
+                                      q_rope.stride(0), q_rope.stride(1), kv_cache, kv_scale,
+                                      kv_indices, suffix_table, suffix_table.stride(0), suffix_lens,
+                                      sm_scale, out, lse, stream)
+        if st != B.MLA_OK:
+            raise B.MlaError("mla_decode_tree_verify", st)
         return out, lse
 
 

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     lib = ctypes.CDLL(m.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -184,6 +184,23 @@ def test_decode_append_validates_before_launch():
     assert m.mla_decode_plan(p, 2, np.array([0, 2, 3], np.int32), np.array([0, 3, 8], np.int32),
                              None, plan2, pb) == m.MLA_OK
     assert call(plan2) == m.MLA_ERR_INVALID_ARG
+
+
+def test_tree_verify_plans_only_reach_the_tree_call():
+    p = m.make_params(128, 1, num_cus=16, suffix_tokens=8)
+    st, plan = _plan(p, [0, 40, 90])
+    assert st == m.MLA_OK
+    h = m.read_plan(plan)[0]
+    common = dict(params=p, plan_h=plan, workspace_d=FAKE, workspace_bytes=h.workspace_bytes,
+                  q_nope_d=FAKE, q_nope_stride_n=128 * 512, q_nope_stride_h=512, q_rope_d=FAKE,
+                  q_rope_stride_n=128 * 64, q_rope_stride_h=64, kv_cache_d=FAKE, kv_scale=1.0,
+                  kv_indices_d=FAKE, sm_scale=0.1, out_d=FAKE, lse_d=None, stream=0)
+    assert m.mla_decode(kv_lens_d=None, **common) == m.MLA_ERR_INVALID_ARG
+    tree = dict(suffix_table_d=FAKE, suffix_stride=64, suffix_lens_d=FAKE)
+    assert m.mla_decode_tree_verify(**{**common, **tree, "suffix_table_d": None}) == m.MLA_ERR_INVALID_ARG
+    assert m.mla_decode_tree_verify(**{**common, **tree, "suffix_stride": 4}) == m.MLA_ERR_INVALID_ARG
+    plain = m.make_params(128, 1, num_cus=16)
+    assert m.mla_decode_tree_verify(**{**common, **tree, "params": plain}) == m.MLA_ERR_PLAN_MISMATCH
 
 
 def test_merge_and_compact_validate():

@@ -73,15 +73,15 @@ def test_config_sampled_rows(dev, name, out_dtype, k):
         assert split_rows > 0, "the sample must include a split-KV row"
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["merge_states", "suffix_merge"])
-def test_tree_verify_cascade(dev, fused):
+@pytest.mark.parametrize("mode", ["merge_states", "suffix_merge", "single_pass"])
+def test_tree_verify_cascade(dev, mode):
     from paged_mla_decode_amd.decoder import PagedMlaDecoder, merge_states, tree_suffix_compact
     tv = workloads.tree_verify()
     pre = tv.prefix
     W, D = tv.width, tv.max_tree_depth
     B = pre.batch
     N = pre.num_rows
-    say(f"tree cascade ({'fused' if fused else 'separate'} merge): B={B} W={W} rows={N} "
+    say(f"tree cascade ({mode}): B={B} W={W} rows={N} "
         f"prefix={int(pre.seq_lens[0])} depth<={D}")
     qn, qr, cache, idx = batch_to_device(pre, dev)
 
@@ -94,6 +94,11 @@ def test_tree_verify_cascade(dev, fused):
     assert np.array_equal(seq_h, tv.tree_mask.sum(axis=1)), "seqlens = visible drafts per row"
     assert seq_h.max() <= D, "depth bound: truncation to max_tree_depth drops nothing"
 
+    if mode == "single_pass":
+        # 2-4. one pass: each row over its prefix and then its visible drafts
+        d1 = PagedMlaDecoder(pre.num_heads, 1, max_batch=B, max_rows=N, device=dev, suffix_tokens=D)
+        d1.plan(pre.kv_indptr, pre.kv_last_page_len, pre.qo_indptr)
+        out, lse = d1.run_tree_verify(qn, qr, cache, idx, table, seqlens, pre.sm_scale)
     # 2. prefix: every draft row attends to its request's prefix
     dp = PagedMlaDecoder(pre.num_heads, 1, max_batch=B, max_rows=N, device=dev)
     dp.plan(pre.kv_indptr, pre.kv_last_page_len, pre.qo_indptr)
@@ -104,7 +109,17 @@ def test_tree_verify_cascade(dev, fused):
     ds = PagedMlaDecoder(pre.num_heads, 1, max_batch=N, max_rows=N, device=dev)
     ds.plan(np.arange(N + 1, dtype=np.int32) * D, np.ones(N, dtype=np.int32))
     suffix_idx = table[:, :D].contiguous().view(-1)
-    if fused:
+    if mode == "single_pass":
+        # The two-pass cascade on the same rows must agree with the single pass
+        # to bf16 rounding (checked below against the oracle as well).
+        out_s, lse_s = ds.run(qn, qr, cache, suffix_idx, pre.sm_scale, kv_lens=seqlens)
+        out2, lse2 = merge_states(out_p, lse_p, out_s, lse_s)
+        torch.cuda.synchronize()
+        d2 = (out.float() - out2.float()).abs().max().item()
+        dl = (lse - lse2).abs().max().item()
+        say(f"  single pass vs two-pass cascade: max_abs={d2:.3e} lse={dl:.3e}")
+        assert d2 <= 2e-2 and dl <= 1e-3
+    elif mode == "suffix_merge":
         # 3+4. the suffix attention merged with the prefix state in the same call, in place
         out, lse = ds.run_suffix_merge(qn, qr, cache, suffix_idx, pre.sm_scale, out_p, lse_p,
                                        kv_lens=seqlens, out=out_p, lse=lse_p)

@@ -193,3 +193,30 @@ def test_graph_safe_plans_share_one_layout():
         p0 = m.make_params(H, 16, num_cus=16, flags=m.MLA_DECODE_GRAPH_SAFE)
         assert m.mla_decode_plan(p0, 1, None, np.array([0, 1], np.int32), None, plan,
                                  plan.size) == m.MLA_ERR_INVALID_ARG
+
+
+def test_tree_verify_plans_keep_every_suffix_slot_in_the_last_chunk():
+    """suffix_tokens S: each row is planned S tokens longer, no chunk boundary
+    falls inside its last S tokens (so only its last chunk, flagged, reads the
+    suffix table), and the planner takes S only for H = 128 at page size 1."""
+    S = 8
+    p = m.make_params(128, 1, num_cus=16, suffix_tokens=S)
+    lens = [2048, 2048, 1, 0, 5000, 300, 31, 33]
+    batch = workloads.random_decode_batch(70, lens, num_heads=128, page_size=1, rows_per_request=3)
+    pb, _ = m.mla_decode_workspace_size(p, batch.batch, batch.num_rows)
+    plan = np.zeros(pb, dtype=np.uint8)
+    assert m.mla_decode_plan(p, batch.batch, batch.qo_indptr, batch.kv_indptr, batch.kv_last_page_len,
+                             plan, pb) == m.MLA_OK
+    h, items, merges, _ = m.read_plan(plan)
+    assert h.suffix_tokens == S and h.num_merges > 0
+    row_len = np.repeat(np.asarray(lens), 3)
+    for it in items:
+        Lp = int(row_len[it.row])
+        if it.flags & m.MLA_ITEM_LAST_CHUNK:
+            assert it.kv_end == Lp + S and it.kv_begin <= Lp
+        else:
+            assert it.kv_end <= Lp
+    for bad in (m.make_params(16, 1, suffix_tokens=S), m.make_params(128, 16, suffix_tokens=S),
+                m.make_params(128, 1, suffix_tokens=257)):
+        assert m.mla_decode_plan(bad, 1, None, np.array([0, 4], np.int32), None, plan,
+                                 plan.size) == m.MLA_ERR_UNSUPPORTED
