@@ -28,8 +28,7 @@ With --workload tree_verify it times the tree-verify cascade of the PR 49477
 analysis (16 requests, 2048-token prefix, 64 drafts at depth <= 8, H=128):
 the suffix-table compaction, then every draft row's attention over its prefix
 and its visible drafts in one pass (mla_decode_tree_verify). The two-pass
-cascade (prefix decode, suffix decode, LSE merge, separate or fused) is timed
-beside it.
+cascade (prefix decode, suffix decode, LSE merge) is timed beside it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -494,12 +493,6 @@ def bench_tree_verify(args):
         s, (o, l) = sets[i % 2], outs[i % 2]
         dp.run(s["qn"], s["qr"], s["cache"], s["idx"], pre.sm_scale, out=o, lse=l, stream=stream)
 
-    def suffix(i, table_seqlens):
-        s, (o, l) = sets[i % 2], outs[i % 2]
-        table, seqlens = table_seqlens
-        ds.run_suffix_merge(s["qn"], s["qr"], s["cache"], table[:, :D].contiguous().view(-1),
-                            pre.sm_scale, o, l, kv_lens=seqlens, out=o, lse=l, stream=stream)
-
     def suffix_separate(i, table_seqlens):
         s, (o, l) = sets[i % 2], outs[i % 2]
         table, seqlens = table_seqlens
@@ -514,10 +507,16 @@ def bench_tree_verify(args):
                            out=o, lse=l, stream=stream)
 
     # The step: compaction, then one pass over prefix and visible drafts. The
-    # two-pass cascade (prefix, suffix, merge; separate or fused) is timed too.
+    # two-pass cascade (prefix, then suffix and merge) is timed too.
     def step(i):
         single(i, compact(i))
 
+    if args.copy_mb:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -538,7 +537,6 @@ def bench_tree_verify(args):
 
     compact_us = launch_avg_us(compact)
     prefix_us = launch_avg_us(prefix)
-    suffix_us = launch_avg_us(lambda i: suffix(i, tables[i % 2]))
     separate_us = launch_avg_us(lambda i: suffix_separate(i, tables[i % 2]))
     single_us = launch_avg_us(lambda i: single(i, tables[i % 2]))
 
@@ -555,7 +553,7 @@ def bench_tree_verify(args):
     single_tflops = single_flops / (single_us * 1e-6) / 1e12
     log(f"step {ms_per_step * 1e3:.1f} us: compaction {compact_us:.1f}, single pass {single_us:.1f} "
         f"({single_tflops:.0f} TFLOP/s); two-pass cascade: prefix {prefix_us:.1f} ({tflops:.0f} "
-        f"TFLOP/s), suffix+merge fused {suffix_us:.1f}, separate {separate_us:.1f}; plans: single "
+        f"TFLOP/s), suffix + merge_states {separate_us:.1f}; plans: single "
         f"{h1.num_items} items, prefix {hp.num_items}, suffix {hs.num_items}")
     res = {
         "metric": "MLA decode latent-cache GB/s (% of HBM peak) and tokens/s, DeepSeek-V3 shapes",
@@ -580,7 +578,6 @@ def bench_tree_verify(args):
         "plan_us": round(plan1_us, 1),
         "phases_us": {"compaction": round(compact_us, 2), "single_pass": round(single_us, 2),
                       "two_pass_prefix": round(prefix_us, 2),
-                      "two_pass_suffix_merge_fused": round(suffix_us, 2),
                       "two_pass_suffix_then_merge_states": round(separate_us, 2)},
         "roofline": {
             "kernel": "mla_decode_tree_verify launch (1024 draft rows x (2048 prefix + <= 8 draft) "

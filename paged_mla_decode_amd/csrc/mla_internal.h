@@ -86,6 +86,9 @@ struct DecodeArgs {
 // arguments of the last three never reach the first.
 enum DecodeMode { kModePlain = 0, kModeAppend = 1, kModeMerge = 2, kModeTree = 3 };
 
+// XCDs of an MI355X: workgroups go to them round robin.
+constexpr int kXcds = 8;
+
 // Single-pass tree verify: at most this many suffix slots per row.
 constexpr int kMaxSuffixTokens = 256;
 

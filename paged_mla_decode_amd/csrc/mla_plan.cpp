@@ -238,16 +238,12 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
     std::stable_sort(merges.begin(), merges.end(),
                      [](const mla_merge_item& x, const mla_merge_item& y) { return x.num_partials > y.num_partials; });
     std::vector<int32_t> next_slot(first_slot);
-    std::vector<mla_work_item> items;
-    items.reserve(pieces.size());
-    int32_t num_workers = 0;
-    std::vector<int32_t> worker_begin;
+    // Items per worker in pour order (pieces of a row get their partial slots in
+    // token order).
+    std::vector<std::vector<mla_work_item>> per_worker;
     for (const Piece& pc : pieces) {
         const Row& r = rows[pc.row_index];
-        while (num_workers <= pc.worker) {
-            worker_begin.push_back((int32_t)items.size());
-            ++num_workers;
-        }
+        if ((size_t)pc.worker >= per_worker.size()) per_worker.resize((size_t)pc.worker + 1);
         mla_work_item it{};
         it.row = r.row;
         it.request = r.request;
@@ -257,15 +253,28 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
         it.partial = npieces[pc.row_index] > 1 ? next_slot[pc.row_index]++ : -1;
         it.head_begin = 0;
         it.flags = (r.len > 0 && it.kv_end == r.len) ? MLA_ITEM_LAST_CHUNK : 0u;
-        items.push_back(it);
+        per_worker[(size_t)pc.worker].push_back(it);
     }
-    // Graph-safe plans list every worker (the launch always has all of them);
-    // the ones past the last with work get empty ranges.
-    if (p->flags & MLA_DECODE_GRAPH_SAFE)
-        while (num_workers < G) {
-            worker_begin.push_back((int32_t)items.size());
-            ++num_workers;
-        }
+    // Worker order. The device hands workgroups to its XCDs round robin
+    // (workgroup p to XCD p % 8), each XCD with its own L2. The pour fills
+    // workers with consecutive rows, and the rows of one request (several query
+    // rows, a long row's pieces) are consecutive, so consecutive pour workers go
+    // to one XCD: pour worker v runs as workgroup p with
+    // v = (p % 8) * (G / 8) + p / 8. Tiles that several of them read then meet
+    // in one L2. The launch then has all G workers, as graph-safe plans do
+    // anyway; those without work exit at once.
+    const int64_t used = (int64_t)per_worker.size();
+    const bool by_xcd = G % kXcds == 0;
+    const int64_t nw = (by_xcd || (p->flags & MLA_DECODE_GRAPH_SAFE)) ? G : used;
+    std::vector<mla_work_item> items;
+    items.reserve(pieces.size());
+    std::vector<int32_t> worker_begin;
+    for (int64_t w = 0; w < nw; ++w) {
+        const int64_t v = by_xcd ? (w % kXcds) * (G / kXcds) + w / kXcds : w;
+        worker_begin.push_back((int32_t)items.size());
+        if (v < used) items.insert(items.end(), per_worker[(size_t)v].begin(), per_worker[(size_t)v].end());
+    }
+    const int32_t num_workers = (int32_t)nw;
     worker_begin.push_back((int32_t)items.size());
     const int64_t chunk = hi * kTile;
 

@@ -76,8 +76,18 @@ def check_invariants(p, batch, h, items, merges, workers):
     assert all(a.num_partials >= b.num_partials for a, b in zip(merges, merges[1:])), "most partials first"
     # the worker table partitions the items, at most one worker per resident workgroup
     assert len(workers) == h.num_workers + 1 and workers[0] == 0 and workers[-1] == len(items)
-    assert all(a < b for a, b in zip(workers, workers[1:])), "every worker has an item"
-    assert h.num_workers <= max(1, p.num_cus) * 2
+    assert all(a <= b for a, b in zip(workers, workers[1:]))
+    G = max(1, p.num_cus) * (2 if p.num_heads == 16 else 1)
+    busy = [w for w in range(h.num_workers) if workers[w + 1] > workers[w]]
+    if G % 8 == 0:
+        # XCD order: pour worker v runs as workgroup w with v = (w % 8) * (G / 8) + w / 8,
+        # so the busy workgroups are the first pour workers, a request's rows on one XCD.
+        assert h.num_workers == G
+        pour = sorted((w % 8) * (G // 8) + w // 8 for w in busy)
+        assert pour == list(range(len(busy))), "busy workers are a prefix of the pour"
+    else:
+        assert busy == list(range(h.num_workers)), "every worker has an item"
+    assert h.num_workers <= G
     # no worker above the plan's capacity by more than a minimum piece, unless
     # a single item (or an unsplittable row) forces it
     cap = h.chunk_tokens // TILE
