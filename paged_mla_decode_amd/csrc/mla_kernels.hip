@@ -78,10 +78,14 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
         const int hq = HW == 32 ? (lane & 31) : (lane & 15);
         const int gq = HW == 32 ? (lane >> 5) : (lane >> 4);
         const int head = it.head_begin + w * HW + hq;
+        // A wave whose heads lie past num_heads only loads tiles: with 16 heads the
+        // second wave halves the first one's loads per tile, which lets the vmcnt
+        // budget cover twice the stages.
+        const bool active = w * HW < a.num_heads;
 
         // ---- absorbed query -> registers (B operand of the score MFMA) ----
         bf16x8 q[kSteps];
-        {
+        if (active) {
             const uint16_t* qn = a.q_nope + (int64_t)it.row * a.qn_sn + (int64_t)head * a.qn_sh;
             const uint16_t* qr = a.q_rope + (int64_t)it.row * a.qr_sn + (int64_t)head * a.qr_sh;
 #pragma unroll
@@ -197,6 +201,7 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
                 wait_tiles_barrier<kStages - 1, kLoadsMin>(min(kStages - 1, ntiles - 1 - i));
 
                 const int nvalid = min(kTile, kv_end - tstart);
+                if (active) {
 
                 // ---- score: S^T = C . Q^T ----
                 float sv[NV];
@@ -300,6 +305,7 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
                         if (OUT32) O16[md] = mfma16(A, Plo[kk], O16[md]);
                     }
                 });
+                }  // active
                 lds_barrier();  // everyone is done with this buffer before it is refilled
             };
             // Tile t lives in buffer t % kStages. Step i computes tile i and fills
@@ -325,6 +331,8 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
         if (!any) break;
         m_ref = m_true;  // second pass: every probability is at most 1
         }
+
+        if (!active) continue;  // a load-only wave has no heads to write
 
         // ---- finalize: l across the lanes of a head, normalise, write ----
         const float m_run = m_ref;

@@ -55,7 +55,9 @@ bool select_variant(const mla_decode_params* p, Variant* v) {
         case 128: *v = Variant{32, 4, 1, 8}; return true;
         case 64: *v = Variant{16, 4, 1, 4}; return true;
         case 32: *v = Variant{16, 2, 1, 4}; return true;
-        case 16: *v = Variant{16, 1, 2, 4}; return true;
+        // 16 heads: a second, load-only wave halves each wave's loads per tile,
+        // so that four stages fit the vmcnt budget (one workgroup per CU).
+        case 16: *v = Variant{16, 2, 1, 4}; return true;
         default: return false;
     }
 }

@@ -57,7 +57,7 @@ def test_status_strings():
     assert m.mla_status_string(99) == "MLA_ERR_UNKNOWN"
 
 
-@pytest.mark.parametrize("H,variant", [(16, "hw16,hs1"), (32, "hw16,hs2"), (64, "hw16,hs4"),
+@pytest.mark.parametrize("H,variant", [(16, "hw16,hs2"), (32, "hw16,hs2"), (64, "hw16,hs4"),
                                        (128, "hw32,hs4")])
 def test_variant_names(H, variant):
     p = m.make_params(H, 1, num_cus=256)

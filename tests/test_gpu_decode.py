@@ -22,7 +22,7 @@ def test_tiny(dev, out_dtype):
     batch = workloads.tiny()
     say(f"tiny out={out_dtype}")
     out, lse, dec = run_decode(batch, dev, out_dtype)
-    assert dec.variant == f"mla_decode<hw16,hs1,kv_bf16,out_{out_dtype}>"
+    assert dec.variant == f"mla_decode<hw16,hs2,kv_bf16,out_{out_dtype}>"
     ref_out, ref_lse = oracle.decode_batch(batch)
     compare(out, lse, ref_out, ref_lse, out_dtype == "fp32", "tiny")
 
