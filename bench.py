@@ -66,6 +66,25 @@ def kernel_source_sha256():
     return h.hexdigest()
 
 
+def copy_bandwidth_gbs(torch, dev, mib=1024, reps=5):
+    """Device-to-device copy rate of this machine (bytes read + written per second,
+    median of `reps`): the second reference the measured rate is stated against."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    return 2.0 * (mib << 20) / float(np.median(times)) / 1e9
+
+
 def measured_traffic(summary, key="traffic_bytes_per_launch"):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     profiles/<summary>_counters.md, or None when there is none or the kernels
@@ -81,7 +100,10 @@ def measured_traffic(summary, key="traffic_bytes_per_launch"):
                 fields[k] = v.strip()
     if fields.get("kernel_source_sha256") != kernel_source_sha256():
         return None
-    return int(fields[key]) if key in fields else None
+    if key not in fields:
+        return None
+    v = float(fields[key])
+    return int(v) if v.is_integer() else v
 
 
 def cpu_baseline(batch, target_s=12.0):
@@ -271,6 +293,12 @@ def main():
             "mfma_frac": round(flops / (launch_avg_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
         },
     }
+    copy_gbs = copy_bandwidth_gbs(torch, dev)
+    res["copy_gbs"] = round(copy_gbs, 1)
+    res["frac_of_copy_bandwidth"] = round(achieved / copy_gbs, 4)
+    res["launch_us_p10_p50_p90"] = [round(float(np.percentile(launch_ms, q)) * 1e3, 2) for q in (10, 50, 90)]
+    mfma = measured_traffic(f"mla_decode_{args.workload}", "mfma_util_percent_decode")
+    res["roofline"]["mfma_busy_counter_percent"] = None if mfma is None else mfma / 100.0
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(batch)
