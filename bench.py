@@ -298,7 +298,7 @@ def main():
     res["frac_of_copy_bandwidth"] = round(achieved / copy_gbs, 4)
     res["launch_us_p10_p50_p90"] = [round(float(np.percentile(launch_ms, q)) * 1e3, 2) for q in (10, 50, 90)]
     mfma = measured_traffic(f"mla_decode_{args.workload}", "mfma_util_percent_decode")
-    res["roofline"]["mfma_busy_counter_percent"] = None if mfma is None else mfma / 100.0
+    res["roofline"]["mfma_busy_counter"] = None if mfma is None else round(mfma / 100.0, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(batch)
