@@ -80,3 +80,70 @@ def test_graph_replay_follows_the_plan(dev, H):
         assert torch.equal(out[rows:], sentinel_out) and torch.equal(lse[rows:], sentinel_lse), \
             "padding rows were written"
         out[:rows].zero_()  # eager work between replays
+
+
+def test_tree_verify_step_replays_from_one_graph(dev):
+    """Configuration 4's step (compaction, then the single pass) captured once
+    and replayed for new draft trees and new prefix lengths: buffers sized for
+    the largest batch, padding rows past the live ones, plans rebuilt between
+    replays. Every replay must equal the eager step on the same inputs."""
+    from paged_mla_decode_amd.decoder import PagedMlaDecoder, tree_suffix_compact
+    B, W, D, H = 4, 64, 8, 128
+    trees = [workloads.tree_verify(seed=40 + k, batch=B, prefix_len=300 + 37 * k, width=W, max_depth=D,
+                                   pool_slots=8192) for k in range(3)]
+    N = B * W
+    rows_pad = N + 16  # graph padding rows: the compaction zeroes them, the decode never plans them
+    base = trees[0].prefix
+    cache = bf16_to_device(base.cache, dev)  # one pool; every tree's slots hold values in it
+    for t in trees[1:]:
+        used = np.unique(t.req_to_token)
+        cache.view(-1, 576)[torch.from_numpy(used.astype(np.int64)).to(dev)] = \
+            bf16_to_device(t.prefix.cache.reshape(-1, 576)[used], dev)
+    qn = torch.zeros((rows_pad, H, 512), dtype=torch.bfloat16, device=dev)
+    qr = torch.zeros((rows_pad, H, 64), dtype=torch.bfloat16, device=dev)
+    mask = torch.zeros((N, W), dtype=torch.uint8, device=dev)
+    r2t = torch.zeros(trees[0].req_to_token.shape[0], 2048, dtype=torch.int32, device=dev)
+    plen = torch.zeros(B, dtype=torch.int32, device=dev)
+    idx = torch.zeros(B * 2048, dtype=torch.int32, device=dev)
+    dec = PagedMlaDecoder(H, 1, max_batch=B, max_rows=N, device=dev, graph_safe=True, suffix_tokens=D)
+    out = torch.zeros((N, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros((N, H), dtype=torch.float32, device=dev)
+
+    def load(t):
+        p = t.prefix
+        qn[:N].copy_(bf16_to_device(p.q_nope, dev))
+        qr[:N].copy_(bf16_to_device(p.q_rope, dev))
+        mask.copy_(torch.from_numpy(t.tree_mask))
+        r2t.zero_()
+        r2t[:, :t.req_to_token.shape[1]].copy_(torch.from_numpy(t.req_to_token))
+        plen.copy_(torch.from_numpy(t.prefix_lens))
+        idx.zero_()
+        idx[:len(p.kv_indices)].copy_(torch.from_numpy(p.kv_indices))
+        dec.plan(p.kv_indptr, p.kv_last_page_len, p.qo_indptr)
+
+    def step(o, l):
+        table, seqlens = tree_suffix_compact(mask, r2t, plen, W, num_rows=rows_pad, num_actual_rows=N)
+        dec.run_tree_verify(qn, qr, cache, idx, table, seqlens, base.sm_scale, out=o, lse=l)
+
+    load(trees[0])
+    step(out, lse)  # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s), torch.cuda.graph(g, stream=s):
+        step(out, lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep, k in enumerate([1, 2, 0, 2]):
+        load(trees[k])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_o = torch.empty_like(out)
+        ref_l = torch.empty_like(lse)
+        step(ref_o, ref_l)
+        torch.cuda.synchronize()
+        say(f"tree replay {rep}: tree {k}, prefix {int(trees[k].prefix_lens[0])}")
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {rep} differs"
+        out.zero_()
