@@ -151,7 +151,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share: --gpus {args.gpus} is not supported "
-              "(this build runs on a single MI355X; sharding is described, not built).",
+              "(the library runs on a single MI355X; sharding is described, not built).",
               file=sys.stderr)
         sys.exit(2)
 

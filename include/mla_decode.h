@@ -39,7 +39,7 @@ extern "C" {
 typedef enum {
     MLA_OK = 0,
     MLA_ERR_INVALID_ARG = 1,         /* NULL pointer, bad size, malformed CSR arrays */
-    MLA_ERR_UNSUPPORTED = 2,         /* a shape or dtype this build does not implement */
+    MLA_ERR_UNSUPPORTED = 2,         /* a shape or dtype the library does not implement */
     MLA_ERR_WORKSPACE_TOO_SMALL = 3, /* a caller buffer is smaller than required */
     MLA_ERR_HIP = 4,                 /* the HIP runtime reported an error */
     MLA_ERR_PLAN_MISMATCH = 5        /* the plan was built for other parameters */

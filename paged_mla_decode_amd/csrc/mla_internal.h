@@ -24,7 +24,7 @@ struct Variant {
 };
 
 // Selects the kernel instantiation for these parameters. Returns false when the
-// parameters are outside what this build implements.
+// parameters are outside what the library implements.
 bool select_variant(const mla_decode_params* p, Variant* v);
 const char* variant_name(const mla_decode_params* p);
 
