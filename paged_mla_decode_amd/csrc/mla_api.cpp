@@ -203,8 +203,6 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
     a.qr_sh = q_rope_stride_h;
     a.cache = static_cast<const uint8_t*>(kv_cache_d);
     a.kv_indices = kv_indices_d;
-    a.num_indices = h->num_page_entries;
-    if (graph) a.plan_d = reinterpret_cast<const mla_plan_header*>(ws);  // replays read the current plan's
     a.kv_lens = kv_lens_d;
     a.out = out_d;
     a.lse = lse_d;

@@ -117,35 +117,6 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned lo, unsigned hi) {
     return r;
 }
 
-typedef int i32x4s __attribute__((ext_vector_type(4)));
-typedef int i32x8s __attribute__((ext_vector_type(8)));
-typedef int i32x16s __attribute__((ext_vector_type(16)));
-// Scalar buffer loads (SMEM, tracked by lgkmcnt, range-checked by the buffer
-// descriptor: dwords past num_records read as 0).
-__device__ i32x8s sbuffer_load_x8(i32x4s rsrc, int byte_off, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v8i32");
-__device__ i32x16s sbuffer_load_x16(i32x4s rsrc, int byte_off, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v16i32");
-
-// Raw buffer descriptor for a dword array of n entries (gfx9 family dword 3).
-__device__ __forceinline__ i32x4s make_rsrc(const void* base, int64_t n_dwords) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    const uint64_t bytes = (uint64_t)n_dwords * 4u;
-    i32x4s r;
-    r[0] = (int)(uint32_t)a;
-    r[1] = (int)(uint32_t)((a >> 32) & 0xFFFFu);  // stride 0
-    r[2] = (int)(uint32_t)(bytes > 0xFFFFFFFFull ? 0xFFFFFFFFull : bytes);
-    r[3] = 0x00020000;
-    return r;
-}
-
-// v[off] for a per-lane off in [0, N), from a wave-uniform (SGPR) vector.
-template <int N, class V>
-__device__ __forceinline__ int select_lane(const V& v, int off) {
-    int x = v[0];
-#pragma unroll
-    for (int j = 1; j < N; ++j) x = off == j ? v[j] : x;
-    return x;
-}
-
 // Software pipeline over N unrolled steps: the LDS operand of step i + D is
 // requested right after step i's MFMA is issued, so D reads are in flight
 // while the matrix core works. With one wave per SIMD there is no other wave

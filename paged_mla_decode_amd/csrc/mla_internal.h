@@ -44,9 +44,6 @@ struct DecodeArgs {
     int64_t qr_sn, qr_sh;
     const uint8_t* cache;
     const int32_t* kv_indices;
-    int64_t num_indices;     // entries of kv_indices (range of the scalar loads)
-    const mla_plan_header* plan_d;  // graph-safe calls: the plan's device copy, whose
-                                    // num_page_entries replaces num_indices
     const int32_t* kv_lens;  // may be null
     void* out;
     float* lse;  // may be null

@@ -42,6 +42,32 @@ using namespace dev;
 // ---------------------------------------------------------------------------
 // The decode kernel
 // ---------------------------------------------------------------------------
+
+// Loads a wave issues after tile i's data when r = ntiles-1-i tiles follow it:
+// the data of tiles i+1 .. i+stages-1 (kLoads each) and the page-table loads
+// of the steps after the one that issued tile i's data, which fetch the
+// entries of tiles i+stages+1 .. i+2 stages-1 (one each).
+__host__ __device__ constexpr int wait_count(int r, int stages, int loads) {
+    const int data = r < stages - 1 ? r : stages - 1;
+    const int idx = r - stages < 0 ? 0 : (r - stages > stages - 1 ? stages - 1 : r - stages);
+    return data * loads + idx;
+}
+// Waits until tile i's data (and every older load) has landed, then a
+// workgroup barrier. r is wave-uniform and >= 0; wait_count is nondecreasing
+// in r and constant from r = kR on.
+template <int kR, int kStages, int kLoads>
+__device__ __forceinline__ void wait_tile_and_idx(int r) {
+    if constexpr (kR > 0) {
+        if (r >= kR) {
+            wait_vmcnt_barrier<wait_count(kR, kStages, kLoads)>();
+            return;
+        }
+        wait_tile_and_idx<kR - 1, kStages, kLoads>(r);
+    } else {
+        wait_vmcnt_barrier<0>();
+    }
+}
+
 template <int HW, int HS, bool KV8, bool OUT32, int MODE>
 __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
     using L = TileLayout<KV8>;
@@ -53,14 +79,19 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
     constexpr int kNTok = HS >= L::kNTB ? 1 : L::kNTB / HS;      // distinct tokens a lane loads
     constexpr int kSteps = SA::kSteps;
     constexpr int kDBlocks = PA::kDBlocks;
-    static_assert(kLoadsMax + kNTok < 64, "vmcnt budget");
+    static_assert(kNTok * L::kTPB <= 64, "one entry per lane");
     // LDS operand reads kept in flight ahead of the MFMAs.
     constexpr int kPipe = HW == 32 ? ((KV8 && OUT32) ? 2 : 4) : 3;
     // Ring of kStages tile buffers: tiles i+1 .. i+kStages-1 are in flight
     // while tile i is computed. Bounded by LDS and by the 6-bit vmcnt.
     constexpr int kStages = Stages<HW, HS, KV8, OUT32>::value;
-    static_assert((kStages - 1) * kLoadsMax < 64, "vmcnt budget");
+    static_assert(wait_count(2 * kStages - 1, kStages, kLoadsMin) < 64, "vmcnt budget");
+    // Page-table entries of tile t: issued kIdxLead steps before its data, in
+    // slot t % kIdxSlots. A slot is rewritten two steps after its last read.
+    constexpr int kIdxLead = kStages;
+    constexpr int kIdxSlots = kIdxLead + 2;
     __shared__ __attribute__((aligned(1024))) char smem[kStages * L::kTileBytes];
+    __shared__ __attribute__((aligned(16))) int idx_ring[kIdxSlots][HS][64];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -115,38 +146,34 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
         // Global byte offset of the chunk this lane loads, within its row (chunk group 0).
         const int dma_lane_off = L::block_chunk(0, lane) * 16;
 
-        // ---- page-table lookups for the tokens this lane loads ----
-        // A wave's lanes load TPB consecutive tokens per token block, which span at
-        // most TPB consecutive page-table entries: one scalar buffer load fetches
-        // them, and each lane picks its own. Tail tokens are clamped to the last
-        // valid token, so no load ever leaves the request's pages.
-        using IdxVec = typename std::conditional<L::kTPB == 8, i32x8s, i32x16s>::type;
-        const i32x4s idx_rsrc = make_rsrc(a.kv_indices, a.plan_d ? a.plan_d->num_page_entries : a.num_indices);
-        IdxVec sidx[kNTok];
-        int p0[kNTok];
-        auto fetch_idx = [&](int tile) {  // issue the scalar loads for a tile
-            const int tstart = kv_begin + tile * kTile;
-#pragma unroll
-            for (int k = 0; k < kNTok; ++k) {
-                const int tb = HS >= L::kNTB ? (w % L::kNTB) : (w + HS * k);
-                const int first = min(tstart + tb * L::kTPB, kv_end - 1);
-                p0[k] = first / ps;
-                const int off = (it.page_base + p0[k]) * 4;
-                if constexpr (L::kTPB == 8)
-                    sidx[k] = sbuffer_load_x8(idx_rsrc, off, 0);
-                else
-                    sidx[k] = sbuffer_load_x16(idx_rsrc, off, 0);
-            }
+        // ---- page-table entries, through a small LDS ring ----
+        // One direct-to-LDS dword load per wave and tile brings the entries of
+        // the tokens the wave loads: lane kTPB k + j holds token j of its k-th
+        // token block (tail tokens are clamped to the last valid token, so no
+        // load leaves the request's pages). These loads are issued kIdxLead
+        // steps ahead of the tile's data and are counted by the same vmcnt
+        // waits. A scalar load of the entries would make the compiler wait
+        // lgkmcnt(0), i.e. a full memory round trip, before the first LDS read
+        // of every tile.
+        const int32_t* page_table = a.kv_indices + it.page_base;
+        auto page_of = [&](int tok) { return a.page_shift >= 0 ? tok >> a.page_shift : tok / ps; };
+        auto issue_idx = [&](int tile) {
+            const int k = min(lane / L::kTPB, kNTok - 1);
+            const int tb = HS >= L::kNTB ? (w % L::kNTB) : (w + HS * k);
+            const int j = min(lane - k * L::kTPB, L::kTPB - 1);
+            const int tok = min(kv_begin + tile * kTile + tb * L::kTPB + j, kv_end - 1);
+            dma4(page_table + page_of(tok), (LDS_AS int*)&idx_ring[tile % kIdxSlots][w][0]);
         };
         auto resolve_rows = [&](int tile, const uint8_t** rowp) {  // lane row pointers of a tile
             const int tstart = kv_begin + tile * kTile;
+            const int slot = tile % kIdxSlots;
 #pragma unroll
             for (int k = 0; k < kNTok; ++k) {
                 const int tb = HS >= L::kNTB ? (w % L::kNTB) : (w + HS * k);
                 const int tau = min(tstart + L::block_token(tb, lane), kv_end - 1);
-                const int pi = tau / ps;
-                const int page = select_lane<L::kTPB>(sidx[k], pi - p0[k]);
-                rowp[k] = a.cache + ((int64_t)page * ps + (tau - pi * ps)) * L::kRowBytes + dma_lane_off;
+                const int page = idx_ring[slot][w][k * L::kTPB + lane / L::kCG];
+                const int row = a.page_shift >= 0 ? (tau & (ps - 1)) : tau % ps;
+                rowp[k] = a.cache + ((int64_t)page * ps + row) * L::kRowBytes + dma_lane_off;
             }
         };
         auto issue_tile = [&](LDS_AS char* base, const uint8_t* const* rowp) {
@@ -180,25 +207,28 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
         l_part = 0.f;
 
         if (ntiles > 0) {
+            // The entries of tiles 0 .. kIdxLead-1, which steps read before the
+            // loop's first wait; later ones come with the steps.
+            for (int t = 0; t < kIdxLead && t < ntiles; ++t) issue_idx(t);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             // One tile step. T is the buffer computed, N the one being filled;
             // distinct restrict-qualified parameters tell the compiler the two
             // never alias, so it adds no waits of its own for the direct-to-LDS
-            // loads: the explicit vmcnt waits order them. Step i = -1 only starts
-            // the pipeline (loads of tile 0). Every vector memory load in flight
-            // here is a tile load: the page table is read through the scalar path.
-            fetch_idx(0);
+            // loads: the explicit vmcnt waits order them. Steps i < 0 only fill
+            // the pipeline. Every vector memory load in flight here is a tile or
+            // page-table load of this loop.
             auto tile_step = [&](const LDS_AS char* __restrict__ T, LDS_AS char* __restrict__ N, int i) {
                 const int tstart = kv_begin + i * kTile;
                 const int ahead = i + kStages - 1;  // the tile whose loads this step issues
                 if (ahead < ntiles) {
                     const uint8_t* rowp[kNTok];
                     resolve_rows(ahead, rowp);
-                    if (ahead + 1 < ntiles) fetch_idx(ahead + 1);
+                    if (ahead + kIdxLead < ntiles) issue_idx(ahead + kIdxLead);
                     issue_tile(N, rowp);
                 }
                 if (i < 0) return;  // pipeline fill
-                // Tiles issued after tile i and still outstanding: min(kStages-1, ntiles-1-i).
-                wait_tiles_barrier<kStages - 1, kLoadsMin>(min(kStages - 1, ntiles - 1 - i));
+                // Tile i has landed, and with it the entries that step i+1 reads.
+                wait_tile_and_idx<2 * kStages - 1, kStages, kLoadsMin>(ntiles - 1 - i);
 
                 const int nvalid = min(kTile, kv_end - tstart);
                 if (active) {
