@@ -11,6 +11,10 @@ Python binding never import it, and it imports neither of them.
 * ``e4m3fn_encode`` / ``append_then_decode``: the fused KV-cache update, written
   as what it must equal: store the new token's row (bf16, or e4m3fn codes
   chosen as the nearest code to value / scale), then decode.
+* ``quantize_query_e4m3fn``: the query of the optional fp8 score, as its
+  definition: per (row, head) a power-of-two scale and the nearest e4m3fn code
+  of every scaled value. The decode with that score is ``mla_decode`` on the
+  dequantized query, since the query enters only the score.
 * ``tree_suffix_compact``: the pre-PR definition of the suffix page table from
   section 1 of the SGLang PR 49477 analysis: sort the keys "column if visible,
   column + W if not" with a stable sort, gather the draft slots in that order,
@@ -161,6 +165,41 @@ def e4m3fn_encode(x) -> np.ndarray:
     pick = np.where(a == vals[hi], hi, pick)
     sign = np.signbit(x).ravel().astype(np.uint8) << 7
     return (pick.astype(np.uint8) | sign).reshape(x.shape)
+
+
+def quantize_query_e4m3fn(q_nope, q_rope):
+    """Query of the optional fp8 score (an fp8 matrix-core product of the
+    query with an e4m3fn cache; the pages leave the query's quantisation open).
+
+    Per query row n and head h, over the head's 576 values (the 512 absorbed
+    no-rope values, then the 64 rope values): amax is the largest magnitude
+    and e the smallest integer with amax * 2^-e <= 448 (e = 0 for a head of
+    zeros). Every value is scaled by 2^-e, which is exact, and encoded as its
+    nearest e4m3fn code (``e4m3fn_encode``). The score then multiplies the
+    dequantized query q_hat = code value * 2^e.
+
+    ``q_nope`` [N,H,512] and ``q_rope`` [N,H,64] are bf16 bit patterns (uint16)
+    or float64. Returns (codes_nope uint8, codes_rope uint8, e int32 [N,H],
+    q_hat_nope float64, q_hat_rope float64)."""
+    qn = np.asarray(q_nope)
+    qr = np.asarray(q_rope)
+    qn = bf16_to_double(qn) if qn.dtype == np.uint16 else np.asarray(qn, np.float64)
+    qr = bf16_to_double(qr) if qr.dtype == np.uint16 else np.asarray(qr, np.float64)
+    q = np.concatenate([qn, qr], axis=-1)
+    amax = np.abs(q).max(axis=-1)
+    e = np.zeros(amax.shape, dtype=np.int64)
+    for idx in zip(*np.nonzero(amax > 0)):
+        a = float(amax[idx])
+        k = int(np.floor(np.log2(a))) - 9  # a first guess; the two loops make it exact
+        while np.ldexp(a, -k) > 448.0:
+            k += 1
+        while np.ldexp(a, -(k - 1)) <= 448.0:
+            k -= 1
+        e[idx] = k
+    codes = e4m3fn_encode(np.ldexp(q, -e[..., None]))
+    q_hat = np.ldexp(e4m3fn_to_double(codes), e[..., None])
+    return (codes[..., :LATENT], codes[..., LATENT:], e.astype(np.int32),
+            q_hat[..., :LATENT], q_hat[..., LATENT:])
 
 
 def append_then_decode(q_nope, q_rope, cache, kv_indptr, kv_indices, kv_last_page_len, page_size,

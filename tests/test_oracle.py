@@ -429,3 +429,77 @@ def test_append_single_token_requests_return_the_new_row(cache_dtype):
         np.testing.assert_allclose(lse[b], score, rtol=1e-12, atol=1e-12)
     changed = np.nonzero((cache != batch.cache).any(axis=-1).ravel())[0]
     assert set(changed) <= {int(batch.kv_indices[batch.kv_indptr[b]]) * 4 for b in range(3)}
+
+
+# ---------------------------------------------------------------------------
+# Query quantisation of the optional fp8 score. Pinned against the definition's
+# properties (minimal power-of-two exponent), torch's float8_e4m3fn cast of the
+# scaled values, worked values and the e4m3fn error bound.
+# ---------------------------------------------------------------------------
+
+def _bf16(x):
+    return workloads.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def _quant_inputs(seed, N=6, H=5):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    # Heads of very different magnitudes, one head of zeros, one exactly on a boundary.
+    mag = np.exp2(rng.uniform(-20, 20, size=(N, H, 1)))
+    q = rng.standard_normal((N, H, 576)) * mag
+    q[0, 0] = 0.0
+    q[1, 1] = 0.0
+    q[1, 1, 7] = 448.0 * 2.0 ** 5           # amax exactly 448 * 2^5
+    q[2, 2] = rng.standard_normal(576)
+    q[2, 2, 3] = -448.0 * 2.0 ** -3 * (1 + 2.0 ** -7)  # just above 448 * 2^-3 (a bf16 value)
+    bits = _bf16(q)
+    return bits[..., :512], bits[..., 512:]
+
+
+def test_query_quant_exponent_is_the_smallest_that_fits():
+    qn, qr = _quant_inputs(41)
+    _, _, e, _, _ = oracle.quantize_query_e4m3fn(qn, qr)
+    q = np.concatenate([oracle.bf16_to_double(qn), oracle.bf16_to_double(qr)], axis=-1)
+    amax = np.abs(q).max(axis=-1)
+    nz = amax > 0
+    assert (np.ldexp(amax[nz], -e[nz]) <= 448.0).all()
+    assert (np.ldexp(amax[nz], -(e[nz] - 1)) > 448.0).all()
+    assert e[0, 0] == 0 and e[1, 1] == 5 and e[2, 2] == -2
+
+
+def test_query_quant_codes_match_torch_cast_of_scaled_values():
+    qn, qr = _quant_inputs(42)
+    cn, cr, e, hn, hr = oracle.quantize_query_e4m3fn(qn, qr)
+    q = np.concatenate([oracle.bf16_to_double(qn), oracle.bf16_to_double(qr)], axis=-1)
+    scaled = np.ldexp(q, -e[..., None].astype(np.int64))
+    # Scaled bf16 values have 8 significant bits: exact in float32.
+    assert np.array_equal(scaled.astype(np.float32).astype(np.float64), scaled)
+    ref = _torch_e4m3fn(scaled.astype(np.float32))
+    assert np.array_equal(np.concatenate([cn, cr], axis=-1), ref)
+    back = torch.from_numpy(ref).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.concatenate([hn, hr], axis=-1), np.ldexp(back, e[..., None]))
+
+
+def test_query_quant_worked_values():
+    q = np.zeros((1, 3, 576))
+    q[0, 0, :4] = [448.0, -1.0, 0.30078125, 0.0]  # 0.30078125: the bf16 value nearest 0.3
+    q[0, 1, 0] = 1000.0                            # e = 2: 1000/4 = 250 fits, 1000/2 = 500 does not
+    bits = _bf16(q)
+    cn, _, e, hn, _ = oracle.quantize_query_e4m3fn(bits[..., :512], bits[..., 512:])
+    assert list(e[0]) == [0, 2, 0]
+    # 448 = 1.75 * 2^8: code 0x7E; -1: 0xB8; 0.30078125 lies between 0.28125 (0x29)
+    # and 0.3125 (0x2A), nearer the latter.
+    assert list(cn[0, 0, :4]) == [0x7E, 0xB8, 0x2A, 0x00]
+    # 250 lies between 240 (0x77) and 256 (0x78), nearer 256: q_hat = 256 * 4.
+    assert cn[0, 1, 0] == 0x78 and hn[0, 1, 0] == 1024.0
+    assert (cn[0, 2] == 0).all() and (hn[0, 2] == 0).all()
+
+
+def test_query_quant_error_within_half_a_step():
+    qn, qr = _quant_inputs(43, N=16, H=8)
+    _, _, e, hn, hr = oracle.quantize_query_e4m3fn(qn, qr)
+    q = np.concatenate([oracle.bf16_to_double(qn), oracle.bf16_to_double(qr)], axis=-1)
+    q_hat = np.concatenate([hn, hr], axis=-1)
+    # e4m3fn has 3 fraction bits: half a step is 2^-4 of a normal value, and
+    # half the subnormal step 2^-9 below 2^-6; both scale by 2^e.
+    bound = np.maximum(2.0 ** -4 * np.abs(q), np.ldexp(2.0 ** -10, e[..., None]))
+    assert (np.abs(q_hat - q) <= bound).all()
