@@ -90,6 +90,25 @@ typedef struct {
  */
 #define MLA_DECODE_GRAPH_SAFE 1
 
+/*
+ * fp8 score (e4m3fn cache, 128 heads, bf16 output, mla_decode only): the
+ * score's contraction runs on the fp8 matrix core, twice the bf16 rate, with
+ * the query quantised to e4m3fn. The fp8 cache itself is the FP8 KV cache of
+ * the DeepSeek-V3/R1 optimisations page; quantising the query too is this
+ * library's reading (the pages leave it open): per query row and head, the
+ * 576 query values (absorbed no-rope part, then rope part) are scaled by
+ * 2^-e, e the smallest integer with amax * 2^-e <= 448 (amax their largest
+ * magnitude; e = 0 for a head of zeros), which is exact, and rounded to the
+ * nearest e4m3fn code, ties to even. The score is then computed from these
+ * codes times 2^e. mla_decode quantises the query into its workspace with a
+ * kernel of its own before the decode launch; the rest of the path (softmax,
+ * the P . latent product in bf16, merges) is unchanged. The results differ
+ * from the bf16 score by the query's rounding (at most 2^-4 of each value)
+ * and by the fp8 matrix core's internal sums (measured within 2^-12 of the
+ * sum of the products' magnitudes).
+ */
+#define MLA_DECODE_FP8_SCORE 2
+
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(int32_t status);
 
@@ -98,7 +117,7 @@ const char* mla_status_string(int32_t status);
  * of the device workspace. It is plain data: tests may read it.
  */
 #define MLA_PLAN_MAGIC 0x504C4D41u /* "AMLP" */
-#define MLA_PLAN_VERSION 5
+#define MLA_PLAN_VERSION 6
 
 typedef struct {
     uint32_t magic;
@@ -127,6 +146,10 @@ typedef struct {
                                    bf16 (fp32 when out_dtype is MLA_DTYPE_FP32) */
     int64_t partial_lse_offset; /* workspace offset of float[num_partials][H] */
     int64_t workspace_bytes;    /* workspace bytes this plan needs */
+    int64_t query_codes_offset; /* MLA_DECODE_FP8_SCORE: workspace offset of the quantised
+                                   query, uint8 e4m3fn codes [rows][H][576]; else 0 */
+    int64_t query_exp_offset;   /* MLA_DECODE_FP8_SCORE: workspace offset of int32 [rows][H],
+                                   the exponent e of each row and head; else 0 */
 } mla_plan_header;
 
 typedef struct {

@@ -41,8 +41,9 @@ MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP32 = 1
 MLA_DTYPE_FP8_E4M3FN = 2
 MLA_PLAN_MAGIC = 0x504C4D41
-MLA_PLAN_VERSION = 5
+MLA_PLAN_VERSION = 6
 MLA_DECODE_GRAPH_SAFE = 1
+MLA_DECODE_FP8_SCORE = 2
 MLA_ITEM_LAST_CHUNK = 1
 
 
@@ -69,7 +70,8 @@ class mla_plan_header(ctypes.Structure):
                 ("merges_offset", ctypes.c_int64), ("workers_offset", ctypes.c_int64),
                 ("plan_bytes", ctypes.c_int64),
                 ("partial_out_offset", ctypes.c_int64), ("partial_lse_offset", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_int64)]
+                ("workspace_bytes", ctypes.c_int64),
+                ("query_codes_offset", ctypes.c_int64), ("query_exp_offset", ctypes.c_int64)]
 
 
 class mla_work_item(ctypes.Structure):

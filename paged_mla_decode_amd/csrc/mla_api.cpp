@@ -175,6 +175,9 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
     if (!std::isfinite(sm_scale) || sm_scale <= 0.f || !std::isfinite(kv_scale) || kv_scale <= 0.f)
         return MLA_ERR_INVALID_ARG;
     if (params->kv_dtype == MLA_DTYPE_BF16 && kv_scale != 1.f) return MLA_ERR_INVALID_ARG;
+    // The fp8 score is a variant of the plain decode only.
+    const bool qf8 = (params->flags & MLA_DECODE_FP8_SCORE) != 0;
+    if (qf8 && (app || pre || tree)) return MLA_ERR_UNSUPPORTED;
     if (app) {
         if (!app->c_new || !app->k_pe_new || !aligned16(app->c_new) || !aligned16(app->k_pe_new) ||
             app->c_new_stride < 0 || app->k_pe_new_stride < 0 ||
@@ -232,6 +235,24 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
         a.sfx_stride = tree->stride;
         a.sfx_lens = tree->lens;
         a.sfx_max = params->suffix_tokens;
+    }
+    if (qf8) {
+        QuantQueryArgs q{};
+        q.q_nope = a.q_nope;
+        q.qn_sn = q_nope_stride_n;
+        q.qn_sh = q_nope_stride_h;
+        q.q_rope = a.q_rope;
+        q.qr_sn = q_rope_stride_n;
+        q.qr_sh = q_rope_stride_h;
+        q.num_heads = params->num_heads;
+        q.dev_num_rows = &reinterpret_cast<const mla_plan_header*>(ws)->num_rows;
+        q.codes = reinterpret_cast<uint8_t*>(const_cast<char*>(ws) + h->query_codes_offset);
+        q.exps = reinterpret_cast<int32_t*>(const_cast<char*>(ws) + h->query_exp_offset);
+        // Graph-safe: a grid for max_rows rows, whatever this plan holds.
+        const int rows = graph ? params->max_rows : h->num_rows;
+        if (rows > 0 && launch_quantize_query(q, rows, stream) != 0) return MLA_ERR_HIP;
+        a.q8 = q.codes;
+        a.q8_exp = q.exps;
     }
     int err = launch_decode(v, params->kv_dtype, params->out_dtype, a, h->num_workers, stream);
     if (err != 0) return MLA_ERR_HIP;

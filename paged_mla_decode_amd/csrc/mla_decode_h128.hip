@@ -63,8 +63,13 @@ __device__ __forceinline__ void settle_o(f32x16 (&O)[4][4]) {
                    "+a"(O[3][0]), "+a"(O[3][1]), "+a"(O[3][2]), "+a"(O[3][3]));
 }
 
-template <bool KV8, bool OUT32, int MODE>
+// QF8: the fp8 score (e4m3fn cache, bf16 output, plain decode). The query
+// comes as e4m3fn codes and a per-head exponent (quantize_query_kernel); the
+// score runs on the 32x32x64 fp8 MFMA, whose operands are the tile's fp8 bytes
+// as read, with no widening.
+template <bool KV8, bool OUT32, int MODE, bool QF8 = false>
 __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
+    static_assert(!QF8 || (KV8 && !OUT32 && MODE == kModePlain), "fp8 score: fp8 cache, bf16 output, plain decode");
     constexpr int HS = 4;
     using L = H128Layout<KV8>;
     constexpr int kLoadsMax = (L::kNB + HS - 1) / HS;
@@ -187,8 +192,24 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         if (ntiles > 0) start_tiles();
 
         // ---- absorbed query -> registers ----
-        bf16x8 q[kSteps];
-        {
+        // bf16: 36 k-slices of 8 features. fp8 score: 9 steps of 32 codes, the
+        // features 64 v + 16 gq + [0, 16) and 64 v + 32 + 16 gq + [0, 16), which
+        // are the bytes the step's two tile reads give this lane.
+        bf16x8 q[QF8 ? 1 : kSteps];
+        u32x8 q8[QF8 ? 9 : 1];
+        float sl2 = a.scale_log2;  // score scale (log2 units), times 2^e for the fp8 score
+        if constexpr (QF8) {
+            const int64_t qrow = (int64_t)it.row * a.num_heads + head;
+            const uint8_t* src = a.q8 + qrow * kRow + 16 * gq;
+#pragma unroll
+            for (int v = 0; v < 9; ++v) {
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(src + 64 * v);
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 64 * v + 32);
+                q8[v] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            sl2 = ldexpf(a.scale_log2, a.q8_exp[qrow]);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), as below
+        } else {
             const uint16_t* qn = a.q_nope + (int64_t)it.row * a.qn_sn + (int64_t)head * a.qn_sh;
             const uint16_t* qr = a.q_rope + (int64_t)it.row * a.qr_sn + (int64_t)head * a.qr_sh;
 #pragma unroll
@@ -293,17 +314,29 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                     // are spread evenly between the score MFMAs, so the score's LDS
                     // reads (each wave reads the whole tile) proceed under product
                     // MFMAs; the last kTail products carry the softmax of tile j.
-                    constexpr int kSM = 36;
+                    constexpr int kSM = QF8 ? 9 : 36;
                     constexpr int kPM = OUT32 ? 64 : 32;
                     constexpr int kTail = OUT32 ? 16 : 8;
                     constexpr int kMix = kPM - kTail;
                     constexpr int kSR = L::kScoreReads;  // 36 | 18 reads
-                    constexpr int kMPR = kSM / kSR;      // MFMAs per score read
+                    constexpr int kMPR = QF8 ? 1 : kSM / kSR;  // MFMAs per score read (fp8 score: 2 reads per MFMA)
+                    constexpr int kPipe8 = kPipe / 2;        // fp8 score operands in flight
                     constexpr int kPPS = OUT32 ? 8 : 4;  // product MFMAs per A step
 
-                    SOp sb[kPipe];
+                    SOp sb[QF8 ? 1 : kPipe];
+                    u32x8 sb8[QF8 ? kPipe8 : 1];
+                    // fp8 score step v: tile reads 2 v and 2 v + 1 (64 features of one token).
+                    auto sload8 = [&](int v) {
+                        const u32x4 lo = sload(2 * v), hi = sload(2 * v + 1);
+                        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    };
+                    if constexpr (QF8) {
 #pragma unroll
-                    for (int i = 0; i < kPipe; ++i) sb[i] = sload(i);
+                        for (int i = 0; i < kPipe8; ++i) sb8[i] = sload8(i);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < kPipe; ++i) sb[i] = sload(i);
+                    }
                     ARaw ab[2] = {aload(0), aload(1)};
                     bf16x8 Bp[4], Bl[4];
 #pragma unroll
@@ -315,13 +348,19 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                     bf16x8 Acur;
 
                     auto score_mfma = [&](int si) {
-                        const int s = si / kMPR, h = si % kMPR;
-                        bf16x8 A;
-                        if constexpr (KV8) A = fp8x8_to_bf16(sb[s % kPipe][2 * h], sb[s % kPipe][2 * h + 1]);
-                        else A = sb[s % kPipe];
-                        if (si == 0) mfma32_first_v(S, A, q[si]);
-                        else mfma32_acc_v(S, A, q[si]);
-                        if (h == kMPR - 1 && s + kPipe < kSR) sb[s % kPipe] = sload(s + kPipe);
+                        if constexpr (QF8) {
+                            if (si == 0) mfma32_f8_first_v(S, sb8[0], q8[0]);
+                            else mfma32_f8_acc_v(S, sb8[si % kPipe8], q8[si]);
+                            if (si + kPipe8 < kSM) sb8[si % kPipe8] = sload8(si + kPipe8);
+                        } else {
+                            const int s = si / kMPR, h = si % kMPR;
+                            bf16x8 A;
+                            if constexpr (KV8) A = fp8x8_to_bf16(sb[s % kPipe][2 * h], sb[s % kPipe][2 * h + 1]);
+                            else A = sb[s % kPipe];
+                            if (si == 0) mfma32_first_v(S, A, q[si]);
+                            else mfma32_acc_v(S, A, q[si]);
+                            if (h == kMPR - 1 && s + kPipe < kSR) sb[s % kPipe] = sload(s + kPipe);
+                        }
                     };
                     auto product_mfma = [&](int pi) {
                         const int a = pi / kPPS, hb = (pi % kPPS) / (OUT32 ? 2 : 1), lo = OUT32 ? pi % 2 : 0;
@@ -381,7 +420,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                             for (int r = 8; r < 16; ++r) tmax = fmaxf(tmax, S[r]);
                             asm volatile("" : "+v"(tmax));
                         } else if (piece == 3) {
-                            tmax = max_xor32(tmax) * a.scale_log2;
+                            tmax = max_xor32(tmax) * sl2;
                             if (j == 0 && pass == 0) m_ref = tmax;
                             m_true = fmaxf(m_true, tmax);
                             asm volatile("" : "+v"(m_ref), "+v"(m_true));
@@ -389,7 +428,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                             const int kk = (piece - 4) >> 1, e0 = 4 * ((piece - 4) & 1);
 #pragma unroll
                             for (int e = e0; e < e0 + 4; ++e) {
-                                const float pv = fast_exp2(fmaf(S[8 * kk + e], a.scale_log2, -m_ref));
+                                const float pv = fast_exp2(fmaf(S[8 * kk + e], sl2, -m_ref));
                                 if (e & 1)
                                     ls1 += pv;
                                 else
@@ -561,6 +600,11 @@ int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num
     // The fused append and the fused prefix merge are instantiations of their
     // own, so the plain decode carries none of their arguments or branches.
     const int mode = a.c_new ? kModeAppend : a.prefix_lse ? kModeMerge : a.sfx_table ? kModeTree : kModePlain;
+    if (a.q8) {
+        if (!kv8 || o32 || mode != kModePlain) return (int)hipErrorInvalidValue;
+        decode_h128_kernel<true, false, kModePlain, true><<<grid, block, 0, s>>>(a);
+        return (int)hipGetLastError();
+    }
     auto go = [&](auto kv8_t, auto o32_t) {
         constexpr bool K = decltype(kv8_t)::value, O = decltype(o32_t)::value;
         if (mode == kModeAppend)

@@ -20,6 +20,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(unsigned)))) unsigned u32x8;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -172,6 +173,15 @@ __device__ __forceinline__ void mfma32_zero_a(f32x16& c, bf16x8 z) {
 __device__ __forceinline__ void mfma32_acc_a(f32x16& c, bf16x8 a, bf16x8 b) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
+// The fp8 score: 32x32x64 e4m3fn x e4m3fn (16 passes), 32 bytes of k per lane.
+__device__ __forceinline__ void mfma32_f8_first_v(f32x16& c, u32x8 a, u32x8 b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_f8_acc_v(f32x16& c, u32x8 a, u32x8 b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+// 24 wait states after the last MFMA that writes c, before any VALU access to
+// it (a 16-pass XDL write needs 19, an 8-pass one 11).
 __device__ __forceinline__ void settle_v(f32x16& c) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
 }

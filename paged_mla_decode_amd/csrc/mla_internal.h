@@ -76,7 +76,27 @@ struct DecodeArgs {
     int64_t sfx_stride;
     const int32_t* sfx_lens;
     int32_t sfx_max;
+    // fp8 score (null q8: none): the query as e4m3fn codes, [rows][H][576]
+    // (no-rope then rope features), and the exponent e of each row and head,
+    // [rows][H]: query value = code * 2^e. The 128-head fp8 kernel only.
+    const uint8_t* q8;
+    const int32_t* q8_exp;
 };
+
+// Quantisation of the query for the fp8 score (one workgroup per query row).
+// Rows at or past *dev_num_rows (the plan's device copy) are skipped, so that a
+// graph-safe launch can cover max_rows rows.
+struct QuantQueryArgs {
+    const uint16_t* q_nope;
+    int64_t qn_sn, qn_sh;
+    const uint16_t* q_rope;
+    int64_t qr_sn, qr_sh;
+    int32_t num_heads;
+    const int32_t* dev_num_rows;
+    uint8_t* codes;
+    int32_t* exps;
+};
+int launch_quantize_query(const QuantQueryArgs& q, int rows, void* stream);
 
 // Decode kernel instantiations: the plain decode, the fused append, the fused
 // prefix merge, the single-pass tree verify (128-head kernel only). The extra

@@ -719,11 +719,59 @@ __global__ __launch_bounds__(256) void tree_compact_kernel(
     if (lane == 0) seqlens[row] = count;
 }
 
+// ---------------------------------------------------------------------------
+// Query quantisation for the fp8 score. Workgroup = one query row; wave w
+// takes heads w, w + 4, ... Per head, lane l holds the eight values of 16-byte
+// chunk l of the 576 (no-rope chunks 0..63) and, for l < 8, rope chunk l as
+// well. amax over the head's values fixes e, the smallest integer with
+// amax * 2^-e <= 448 (0 for a head of zeros); each value is scaled by 2^-e
+// (exact) and rounded to its nearest e4m3fn code.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_at(const bf16x8& v, int i) { return (float)v[i]; }
+
+__global__ __launch_bounds__(256) void quantize_query_kernel(const QuantQueryArgs q) {
+    const int row = blockIdx.x;
+    if (row >= *q.dev_num_rows) return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int h = w; h < q.num_heads; h += 4) {
+        const bf16x8 vn = load_bf16x8(q.q_nope + (int64_t)row * q.qn_sn + (int64_t)h * q.qn_sh + 8 * lane);
+        bf16x8 vr = {};
+        if (lane < kRope / 8) vr = load_bf16x8(q.q_rope + (int64_t)row * q.qr_sn + (int64_t)h * q.qr_sh + 8 * lane);
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_at(vn, i)), fabsf(bf16_at(vr, i))));
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+        // amax = m * 2^k with m in [0.5, 1); 448 = 0.875 * 2^9.
+        int k = 0;
+        const float m = frexpf(amax, &k);
+        const int e = amax > 0.f ? (m <= 0.875f ? k - 9 : k - 8) : 0;
+        auto pack = [&](const bf16x8& v) {
+            uint2 r;
+            uint32_t c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = e4m3fn_rne(ldexpf(bf16_at(v, i), -e));
+            r.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+            r.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+            return r;
+        };
+        uint8_t* dst = q.codes + ((int64_t)row * q.num_heads + h) * kRow;
+        *reinterpret_cast<uint2*>(dst + 8 * lane) = pack(vn);
+        if (lane < kRope / 8) *reinterpret_cast<uint2*>(dst + kLatent + 8 * lane) = pack(vr);
+        if (lane == 0) q.exps[(int64_t)row * q.num_heads + h] = e;
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+int launch_quantize_query(const QuantQueryArgs& q, int rows, void* stream) {
+    quantize_query_kernel<<<dim3(rows), dim3(256), 0, (hipStream_t)stream>>>(q);
+    return (int)hipGetLastError();
+}
+
 template <int HW, int HS>
 static int launch_decode_hs(int kv_dtype, int out_dtype, const DecodeArgs& a, int n, hipStream_t s) {
     const dim3 grid(n), block(64 * HS);

@@ -41,7 +41,12 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 }  // namespace
 
 bool select_variant(const mla_decode_params* p, Variant* v) {
-    if (!p || (p->flags & ~MLA_DECODE_GRAPH_SAFE) != 0) return false;
+    if (!p || (p->flags & ~(MLA_DECODE_GRAPH_SAFE | MLA_DECODE_FP8_SCORE)) != 0) return false;
+    // The fp8 score: the 128-head kernel over an e4m3fn cache, bf16 output, plain decode.
+    if ((p->flags & MLA_DECODE_FP8_SCORE) &&
+        (p->num_heads != 128 || p->kv_dtype != MLA_DTYPE_FP8_E4M3FN || p->out_dtype != MLA_DTYPE_BF16 ||
+         p->suffix_tokens != 0))
+        return false;
     // Single-pass tree verify: the 128-head kernel over token slots (page size 1).
     if (p->suffix_tokens < 0 || p->suffix_tokens > kMaxSuffixTokens) return false;
     if (p->suffix_tokens > 0 && (p->num_heads != 128 || p->page_size != 1)) return false;
@@ -65,6 +70,7 @@ bool select_variant(const mla_decode_params* p, Variant* v) {
 const char* variant_name(const mla_decode_params* p) {
     Variant v;
     if (!select_variant(p, &v)) return nullptr;
+    if (p->flags & MLA_DECODE_FP8_SCORE) return "mla_decode<hw32,hs4,kv_fp8,out_bf16,score_fp8>";
     const bool kv8 = p->kv_dtype == MLA_DTYPE_FP8_E4M3FN;
     const bool o32 = p->out_dtype == MLA_DTYPE_FP32;
     static const char* names[2][3][2][2] = {
@@ -85,8 +91,9 @@ const char* variant_name(const mla_decode_params* p) {
 // Partials are stored in the output's precision: bf16, or fp32 in the fp32 mode.
 static int64_t partial_elem_bytes(const mla_decode_params* p) { return p->out_dtype == MLA_DTYPE_FP32 ? 4 : 2; }
 
+// q_rows: rows of the quantised query (fp8 score), 0 without it.
 static void layout(int32_t num_items, int32_t num_merges, int32_t num_workers, int32_t num_partials,
-                   int32_t num_heads, int64_t elem_bytes, mla_plan_header* h) {
+                   int32_t num_heads, int64_t elem_bytes, int32_t q_rows, mla_plan_header* h) {
     h->items_offset = align_up(sizeof(mla_plan_header), 64);
     h->merges_offset = align_up(h->items_offset + (int64_t)num_items * sizeof(mla_work_item), 64);
     h->workers_offset = align_up(h->merges_offset + (int64_t)num_merges * sizeof(mla_merge_item), 64);
@@ -95,6 +102,15 @@ static void layout(int32_t num_items, int32_t num_merges, int32_t num_workers, i
     h->partial_lse_offset =
         align_up(h->partial_out_offset + (int64_t)num_partials * num_heads * kLatent * elem_bytes, 256);
     h->workspace_bytes = align_up(h->partial_lse_offset + (int64_t)num_partials * num_heads * 4, 256);
+    h->query_codes_offset = h->query_exp_offset = 0;
+    if (q_rows > 0) {
+        h->query_codes_offset = h->workspace_bytes;
+        h->query_exp_offset = align_up(h->query_codes_offset + (int64_t)q_rows * num_heads * (kLatent + kRope), 256);
+        h->workspace_bytes = align_up(h->query_exp_offset + (int64_t)q_rows * num_heads * 4, 256);
+    }
+}
+static int32_t query_rows(const mla_decode_params* p, int32_t rows) {
+    return (p->flags & MLA_DECODE_FP8_SCORE) ? rows : 0;
 }
 
 int32_t plan_bounds(const mla_decode_params* p, int32_t num_cus, int32_t batch, int32_t num_rows,
@@ -113,7 +129,8 @@ int32_t plan_bounds(const mla_decode_params* p, int32_t num_cus, int32_t batch, 
     const int64_t items = (int64_t)num_rows + G + 1;
     const int64_t partials = std::min<int64_t>(items, 2 * G + 2);
     mla_plan_header h{};
-    layout((int32_t)items, num_rows, (int32_t)G, (int32_t)partials, p->num_heads, partial_elem_bytes(p), &h);
+    layout((int32_t)items, num_rows, (int32_t)G, (int32_t)partials, p->num_heads, partial_elem_bytes(p),
+           query_rows(p, num_rows), &h);
     if (plan_bytes) *plan_bytes = (size_t)h.plan_bytes;
     if (workspace_bytes) *workspace_bytes = (size_t)h.workspace_bytes;
     return MLA_OK;
@@ -308,9 +325,10 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
         if (p->max_rows < 1 || num_rows > p->max_rows) return MLA_ERR_INVALID_ARG;
         const int64_t cap_items = (int64_t)p->max_rows + G + 1;
         layout((int32_t)cap_items, p->max_rows, (int32_t)G, (int32_t)std::min<int64_t>(cap_items, 2 * G + 2),
-               p->num_heads, partial_elem_bytes(p), &h);
+               p->num_heads, partial_elem_bytes(p), query_rows(p, p->max_rows), &h);
     } else {
-        layout(h.num_items, h.num_merges, num_workers, num_partials, p->num_heads, partial_elem_bytes(p), &h);
+        layout(h.num_items, h.num_merges, num_workers, num_partials, p->num_heads, partial_elem_bytes(p),
+               query_rows(p, h.num_rows), &h);
     }
     if ((size_t)h.plan_bytes > plan_h_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
 

@@ -247,3 +247,65 @@ def test_projections_validate(fn):
     for i in (1, 2, 4, 5, 7, 8):
         assert call(**{f"a{i}": 12}) == m.MLA_ERR_INVALID_ARG
         assert call(**{f"a{i}": -8}) == m.MLA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# The fp8 score flag (MLA_DECODE_FP8_SCORE)
+# ---------------------------------------------------------------------------
+
+def _qf8_params(**over):
+    kw = dict(num_heads=128, page_size=64, kv_dtype=m.MLA_DTYPE_FP8_E4M3FN, num_cus=256,
+              flags=m.MLA_DECODE_FP8_SCORE)
+    kw.update(over)
+    return m.make_params(**kw)
+
+
+def test_fp8_score_only_for_the_128_head_fp8_bf16_plain_decode():
+    assert m.mla_decode_variant(_qf8_params()).endswith("score_fp8>")
+    for bad in (dict(num_heads=16), dict(num_heads=64), dict(kv_dtype=m.MLA_DTYPE_BF16),
+                dict(out_dtype=m.MLA_DTYPE_FP32), dict(page_size=1, suffix_tokens=8)):
+        assert m.mla_decode_variant(_qf8_params(**bad)) is None, bad
+    assert m.mla_decode_variant(_qf8_params(flags=4)) is None  # an unknown flag
+
+
+@pytest.mark.parametrize("graph", [False, True])
+def test_fp8_score_workspace_holds_the_quantised_query(graph):
+    flags = m.MLA_DECODE_FP8_SCORE | (m.MLA_DECODE_GRAPH_SAFE if graph else 0)
+    p = _qf8_params(flags=flags, max_rows=40 if graph else 0)
+    plain = m.make_params(128, 64, kv_dtype=m.MLA_DTYPE_FP8_E4M3FN, num_cus=256,
+                          flags=m.MLA_DECODE_GRAPH_SAFE if graph else 0, max_rows=40 if graph else 0)
+    indptr = [0, 3, 50, 51]
+    pb, wb = m.mla_decode_workspace_size(p, 3, 3)
+    st, plan = _plan(p, indptr, size=pb)
+    assert st == m.MLA_OK
+    h = m.read_plan(plan)[0]
+    rows = 40 if graph else 3
+    assert h.query_codes_offset >= h.partial_lse_offset + h.num_partials * 128 * 4 or h.num_partials == 0
+    assert h.query_codes_offset % 256 == 0 and h.query_exp_offset % 256 == 0
+    assert h.query_exp_offset >= h.query_codes_offset + rows * 128 * 576
+    assert h.workspace_bytes >= h.query_exp_offset + rows * 128 * 4
+    assert h.workspace_bytes <= wb
+    # Without the flag the regions are absent and everything else sits where it did.
+    st, plan0 = _plan(plain, indptr)
+    h0 = m.read_plan(plan0)[0]
+    assert h0.query_codes_offset == 0 and h0.query_exp_offset == 0
+    assert (h0.partial_out_offset, h0.partial_lse_offset) == (h.partial_out_offset, h.partial_lse_offset)
+    assert h0.workspace_bytes == h.query_codes_offset
+
+
+def test_fp8_score_rejected_by_the_fused_variants():
+    p = _qf8_params()
+    st, plan = _plan(p, [0, 3, 8])
+    assert st == m.MLA_OK
+    h = m.read_plan(plan)[0]
+    common = dict(params=p, plan_h=plan, workspace_d=FAKE, workspace_bytes=h.workspace_bytes,
+                  q_nope_d=FAKE, q_nope_stride_n=128 * 512, q_nope_stride_h=512, q_rope_d=FAKE,
+                  q_rope_stride_n=128 * 64, q_rope_stride_h=64, kv_cache_d=FAKE, kv_scale=0.5,
+                  kv_indices_d=FAKE, sm_scale=0.1, out_d=FAKE, lse_d=None, stream=0)
+    assert m.mla_decode_append(**common, c_new_d=FAKE, c_new_stride=576, k_pe_new_d=FAKE + 1024,
+                               k_pe_new_stride=576) == m.MLA_ERR_UNSUPPORTED
+    assert m.mla_decode_suffix_merge(**common, kv_lens_d=None, prefix_out_d=FAKE,
+                                     prefix_lse_d=FAKE) == m.MLA_ERR_UNSUPPORTED
+    # A plan built without the flag does not serve a call with it, nor the reverse.
+    plain = m.make_params(128, 64, kv_dtype=m.MLA_DTYPE_FP8_E4M3FN, num_cus=256)
+    assert m.mla_decode(**{**common, "params": plain}, kv_lens_d=None) == m.MLA_ERR_PLAN_MISMATCH
