@@ -145,6 +145,9 @@ def main():
     ap.add_argument("--append", action="store_true",
                     help="decode workloads: time mla_decode_append (each request's new token "
                          "written into its cache row in the same launch) instead of mla_decode")
+    ap.add_argument("--fp8-score", action="store_true",
+                    help="skewed_fp8: the score on the fp8 matrix core with an e4m3fn-quantised "
+                         "query (MLA_DECODE_FP8_SCORE)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -155,6 +158,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.fp8_score and (args.workload != "skewed_fp8" or args.append):
+        print("--fp8-score applies to the skewed_fp8 workload's mla_decode only", file=sys.stderr)
+        sys.exit(2)
     if args.workload == "projections":
         return bench_projections(args)
     if args.workload == "tree_verify":
@@ -186,7 +192,7 @@ def main():
 
     dec = PagedMlaDecoder(batch.num_heads, batch.page_size, max_batch=batch.batch,
                           max_rows=batch.num_rows, kv_dtype=batch.cache_dtype, out_dtype="bf16",
-                          device=dev)
+                          device=dev, fp8_score=args.fp8_score)
     t0 = time.perf_counter()
     h = dec.plan(batch.kv_indptr, batch.kv_last_page_len)
     plan_us = (time.perf_counter() - t0) * 1e6
@@ -237,6 +243,7 @@ def main():
     elapsed = time.perf_counter() - t0
     launch_ms = np.array([a.elapsed_time(b) for a, b in events])
 
+    profile_key = f"mla_decode_{args.workload}" + ("_fp8_score" if args.fp8_score else "")
     tokens = int(batch.seq_lens.sum())
     latent_bytes = costs.mla_decode_latent_bytes(tokens, 1 if batch.cache_dtype != "bf16" else 2)
     assert latent_bytes == tokens * batch.cache_bytes_per_token
@@ -263,7 +270,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if batch.cache_dtype == "bf16" else "fp8_e4m3fn cache, bf16 mfma",
+        "dtype": "bf16" if batch.cache_dtype == "bf16" else
+                 ("fp8_e4m3fn cache, fp8 score mfma, bf16 product mfma" if args.fp8_score
+                  else "fp8_e4m3fn cache, bf16 mfma"),
         "data": "synthetic",
         "config": {
             "workload": f"{batch.name}: B={batch.batch} H={batch.num_heads} latent 512+64 "
@@ -271,7 +280,7 @@ def main():
             "batch": batch.batch, "num_heads": batch.num_heads, "kv_lora_rank": 512,
             "qk_rope_head_dim": 64, "page_size": batch.page_size, "kv_tokens": tokens,
             "query_rows": batch.num_rows, "parallelism": "single GPU",
-            "fused_append": bool(args.append),
+            "fused_append": bool(args.append), "fp8_score": bool(args.fp8_score),
         },
         "tokens_per_s": round(batch.num_rows / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -280,13 +289,14 @@ def main():
                  "partials": h.num_partials, "capacity_tokens": h.chunk_tokens},
         "roofline": {
             "kernel": ("mla_decode_append" if args.append else "mla_decode") +
-                      " launch (decode kernel + split-KV merge kernel)",
+                      (" launch (query quantisation + decode kernel + split-KV merge kernel)"
+                       if args.fp8_score else " launch (decode kernel + split-KV merge kernel)"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if args.append else measured_traffic(f"mla_decode_{args.workload}"),
+            "traffic": None if args.append else measured_traffic(profile_key),
             "algorithmic_bytes_per_launch": latent_bytes,
             "launch_avg_us": round(launch_avg_ms * 1e3, 2),
             "mfma_tflops": round(flops / (launch_avg_ms * 1e-3) / 1e12, 1),
@@ -297,7 +307,7 @@ def main():
     res["copy_gbs"] = round(copy_gbs, 1)
     res["frac_of_copy_bandwidth"] = round(achieved / copy_gbs, 4)
     res["launch_us_p10_p50_p90"] = [round(float(np.percentile(launch_ms, q)) * 1e3, 2) for q in (10, 50, 90)]
-    mfma = measured_traffic(f"mla_decode_{args.workload}", "mfma_util_percent_decode")
+    mfma = None if args.append else measured_traffic(profile_key, "mfma_util_percent_decode")
     res["roofline"]["mfma_busy_counter"] = None if mfma is None else round(mfma / 100.0, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

@@ -83,7 +83,7 @@ struct DecodeArgs {
     const int32_t* q8_exp;
 };
 
-// Quantisation of the query for the fp8 score (one workgroup per query row).
+// Quantisation of the query for the fp8 score (one wave per query row and head).
 // Rows at or past *dev_num_rows (the plan's device copy) are skipped, so that a
 // graph-safe launch can cover max_rows rows.
 struct QuantQueryArgs {

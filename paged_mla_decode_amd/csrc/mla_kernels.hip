@@ -720,8 +720,8 @@ __global__ __launch_bounds__(256) void tree_compact_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Query quantisation for the fp8 score. Workgroup = one query row; wave w
-// takes heads w, w + 4, ... Per head, lane l holds the eight values of 16-byte
+// Query quantisation for the fp8 score. One wave per (row, head): workgroup
+// (row, g) takes heads 4 g .. 4 g + 3. Per head, lane l holds the eight values of 16-byte
 // chunk l of the 576 (no-rope chunks 0..63) and, for l < 8, rope chunk l as
 // well. amax over the head's values fixes e, the smallest integer with
 // amax * 2^-e <= 448 (0 for a head of zeros); each value is scaled by 2^-e
@@ -732,8 +732,9 @@ __device__ __forceinline__ float bf16_at(const bf16x8& v, int i) { return (float
 __global__ __launch_bounds__(256) void quantize_query_kernel(const QuantQueryArgs q) {
     const int row = blockIdx.x;
     if (row >= *q.dev_num_rows) return;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    for (int h = w; h < q.num_heads; h += 4) {
+    const int lane = threadIdx.x & 63;
+    const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
+    if (h < q.num_heads) {
         const bf16x8 vn = load_bf16x8(q.q_nope + (int64_t)row * q.qn_sn + (int64_t)h * q.qn_sh + 8 * lane);
         bf16x8 vr = {};
         if (lane < kRope / 8) vr = load_bf16x8(q.q_rope + (int64_t)row * q.qr_sn + (int64_t)h * q.qr_sh + 8 * lane);
@@ -768,7 +769,7 @@ __global__ __launch_bounds__(256) void quantize_query_kernel(const QuantQueryArg
 // Launchers
 // ---------------------------------------------------------------------------
 int launch_quantize_query(const QuantQueryArgs& q, int rows, void* stream) {
-    quantize_query_kernel<<<dim3(rows), dim3(256), 0, (hipStream_t)stream>>>(q);
+    quantize_query_kernel<<<dim3(rows, (q.num_heads + 3) / 4), dim3(256), 0, (hipStream_t)stream>>>(q);
     return (int)hipGetLastError();
 }
 
