@@ -18,14 +18,17 @@ def dev():
     return require_gpu()
 
 
-@pytest.mark.parametrize("H", [16, 128])
-def test_graph_replay_follows_the_plan(dev, H):
+@pytest.mark.parametrize("H,fp8_score", [(16, False), (128, False), (128, True)])
+def test_graph_replay_follows_the_plan(dev, H, fp8_score):
+    """fp8_score: an e4m3fn pool and MLA_DECODE_FP8_SCORE, whose query
+    quantisation launch is captured with the decode and merges."""
     from paged_mla_decode_amd.decoder import PagedMlaDecoder
     ps, B = 16, 6
     # One pool holds every batch's tokens: batch k uses its own page list of it.
     lens_set = [[3000, 40, 1, 700, 64, 2000], [10, 5000, 300, 0, 33, 17], [900, 900, 1]]
-    pool = workloads.random_decode_batch(90 + H, [12000], num_heads=H, page_size=ps)
-    cache = bf16_to_device(pool.cache, dev)
+    kv = "fp8_e4m3fn" if fp8_score else "bf16"
+    pool = workloads.random_decode_batch(90 + H, [12000], num_heads=H, page_size=ps, cache_dtype=kv)
+    cache = torch.from_numpy(pool.cache).to(dev) if fp8_score else bf16_to_device(pool.cache, dev)
     rng = np.random.Generator(np.random.PCG64(91))
     q_all = workloads.f32_to_bf16_bits(rng.standard_normal((B, H, 576), dtype=np.float32) * np.float32(0.5))
     q = bf16_to_device(q_all, dev)
@@ -43,7 +46,8 @@ def test_graph_replay_follows_the_plan(dev, H):
     batches = [csr(lens, 100 + k) for k, lens in enumerate(lens_set)]
     max_idx = max(len(b[1]) for b in batches)
     idx = torch.zeros(max_idx, dtype=torch.int32, device=dev)  # fixed buffer the graph reads
-    dec = PagedMlaDecoder(H, ps, max_batch=B, num_cus=16, device=dev, graph_safe=True)
+    dec = PagedMlaDecoder(H, ps, max_batch=B, num_cus=16, device=dev, graph_safe=True, kv_dtype=kv,
+                          fp8_score=fp8_score)
     out = torch.zeros((B, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.zeros((B, H), dtype=torch.float32, device=dev)
 
@@ -54,13 +58,13 @@ def test_graph_replay_follows_the_plan(dev, H):
 
     h0 = load(0)
     assert h0.num_merges > 0
-    dec.run(qn, qr, cache, idx, pool.sm_scale, out=out, lse=lse)  # warm up outside the capture
+    dec.run(qn, qr, cache, idx, pool.sm_scale, pool.kv_scale, out=out, lse=lse)  # warm up outside the capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s), torch.cuda.graph(g, stream=s):
-        dec.run(qn, qr, cache, idx, pool.sm_scale, out=out, lse=lse)
+        dec.run(qn, qr, cache, idx, pool.sm_scale, pool.kv_scale, out=out, lse=lse)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
 
@@ -72,9 +76,9 @@ def test_graph_replay_follows_the_plan(dev, H):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        ref_out, ref_lse = dec.run(qn, qr, cache, idx, pool.sm_scale)  # eager, same plan
+        ref_out, ref_lse = dec.run(qn, qr, cache, idx, pool.sm_scale, pool.kv_scale)  # eager, same plan
         torch.cuda.synchronize()
-        say(f"H={H} replay {rep}: batch {k} rows={rows} merges={h.num_merges} wide={h.num_wide_merges}")
+        say(f"H={H} fp8_score={fp8_score} replay {rep}: batch {k} rows={rows} merges={h.num_merges} wide={h.num_wide_merges}")
         assert torch.equal(out[:rows], ref_out[:rows]) and torch.equal(lse[:rows], ref_lse[:rows]), \
             f"replay {rep} (batch {k}) differs from the eager call"
         assert torch.equal(out[rows:], sentinel_out) and torch.equal(lse[rows:], sentinel_lse), \
