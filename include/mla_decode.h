@@ -100,7 +100,7 @@ typedef struct {
  * 2^-e, e the smallest integer with amax * 2^-e <= 448 (amax their largest
  * magnitude; e = 0 for a head of zeros), which is exact, and rounded to the
  * nearest e4m3fn code, ties to even. The score is then computed from these
- * codes times 2^e. mla_decode quantises the query into its workspace with a
+ * codes times 2^e. Query values must be finite. mla_decode quantises the query into its workspace with a
  * kernel of its own before the decode launch; the rest of the path (softmax,
  * the P . latent product in bf16, merges) is unchanged. The results differ
  * from the bf16 score by the query's rounding (at most 2^-4 of each value)
