@@ -171,7 +171,9 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
     const int64_t G = std::max<int64_t>(1, (int64_t)num_cus * v.wgs_per_cu);
     const int64_t max_splits = p->max_splits > 0 ? p->max_splits : kDefaultMaxSplits;
     const int64_t item_cost = v.item_cost;
-    const int64_t min_piece = item_cost;  // a piece is at least as long as its fixed cost
+    // Shortest piece: the item cost (a piece at least as long as its fixed
+    // cost), or two tiles where that lowers the capacity (below).
+    int64_t min_piece = item_cost;
     const int64_t sfx = p->suffix_tokens;
 
     struct Row {
@@ -228,15 +230,35 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
         }
         return true;
     };
-    int64_t hi = item_cost;
-    for (const Row& r : rows) hi += r.tiles + item_cost;
-    int64_t lo = 0;  // infeasible (no capacity)
-    while (hi - lo > 1) {
-        const int64_t mid = lo + (hi - lo) / 2;
-        if (fill(mid, nullptr))
-            hi = mid;
+    // The least capacity with which the pour fits G workers.
+    auto search = [&]() {
+        int64_t hi = item_cost;
+        for (const Row& r : rows) hi += r.tiles + item_cost;
+        int64_t lo = 0;  // infeasible (no capacity)
+        while (hi - lo > 1) {
+            const int64_t mid = lo + (hi - lo) / 2;
+            if (fill(mid, nullptr))
+                hi = mid;
+            else
+                lo = mid;
+        }
+        return hi;
+    };
+    int64_t hi = search();
+    // With the item cost as the shortest piece a worker moves on while up to
+    // twice that much capacity is left, so the search can settle a tile or more
+    // above the average load and leave workers idle (12 of 256 on a 64-row,
+    // 16-head batch). Two-tile pieces fill those gaps; they are kept only where
+    // they lower the capacity, since otherwise they only add items (each loads
+    // the query and writes an output): measured on three workloads, a
+    // 2-4% gain where the capacity fell and a 2% loss where it did not.
+    if (item_cost > 2) {
+        min_piece = 2;
+        const int64_t hi2 = search();
+        if (hi2 < hi)
+            hi = hi2;
         else
-            lo = mid;
+            min_piece = item_cost;
     }
     std::vector<Piece> pieces;
     if (!fill(hi, &pieces)) return MLA_ERR_UNSUPPORTED;  // unreachable: hi is feasible

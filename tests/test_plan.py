@@ -142,6 +142,22 @@ def test_workers_are_balanced(name):
     assert max(loads) <= mean + cost + 8, (max(loads), mean)
 
 
+@pytest.mark.parametrize("name,max_idle", [("v2_lite", 1), ("skewed_fp8", 3), ("v3", 1)])
+def test_capacity_leaves_few_workers_idle(name, max_idle):
+    """No worker's load exceeds the plan's capacity, and the capacity sits
+    close enough to the mean load that at most a few workers get no item
+    (two-tile pieces are taken where they lower the capacity; with whole
+    item-cost pieces the 16-head batch left 12 workers idle)."""
+    batch = getattr(workloads, name)()
+    kv = m.MLA_DTYPE_FP8_E4M3FN if batch.cache_dtype != "bf16" else m.MLA_DTYPE_BF16
+    p = m.make_params(batch.num_heads, batch.page_size, kv_dtype=kv, num_cus=256)
+    h, items, merges, workers = build(p, batch)
+    loads = worker_loads(items, workers, item_cost(batch.num_heads))
+    assert max(loads) * TILE <= h.chunk_tokens
+    idle = sum(1 for w in range(h.num_workers) if workers[w + 1] == workers[w])
+    assert idle <= max_idle, idle
+
+
 def test_empty_requests_get_an_empty_item():
     batch = workloads.random_decode_batch(3, [0, 5, 0], 16, 4)
     p = m.make_params(16, 4, num_cus=256)
