@@ -42,7 +42,8 @@ def run_qf8(batch, dev, num_cus=0, graph_max_rows=None):
                           max_rows=graph_max_rows if graph else batch.num_rows,
                           kv_dtype=batch.cache_dtype, num_cus=num_cus, device=dev,
                           graph_safe=graph, fp8_score=True)
-    h = dec.plan(batch.kv_indptr, batch.kv_last_page_len)
+    qo = None if batch.num_rows == batch.batch else batch.qo_indptr
+    h = dec.plan(batch.kv_indptr, batch.kv_last_page_len, qo)
     out, lse = dec.run(qn, qr, cache, idx, batch.sm_scale, batch.kv_scale)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), dec, h
@@ -50,7 +51,7 @@ def run_qf8(batch, dev, num_cus=0, graph_max_rows=None):
 
 def score_bounds(batch, q_hat):
     """D [N, H] and M [N, 512] of the tolerance, from the dequantised operands
-    (one query row per request)."""
+    (query rows qo_indptr[b] .. qo_indptr[b+1] attend to request b)."""
     flat = batch.cache.reshape(-1, 576)
     q_abs = np.abs(q_hat)
     D = np.zeros(q_hat.shape[:2])
@@ -63,8 +64,9 @@ def score_bounds(batch, q_hat):
         rows = batch.kv_indices[batch.kv_indptr[b] + t // batch.page_size].astype(np.int64) * \
             batch.page_size + t % batch.page_size
         c = np.abs(oracle.e4m3fn_to_double(flat[rows])) * batch.kv_scale
-        D[b] = (c @ q_abs[b].T).max(axis=0)
-        M[b] = c[:, :512].max(axis=0)
+        for n in range(int(batch.qo_indptr[b]), int(batch.qo_indptr[b + 1])):
+            D[n] = (c @ q_abs[n].T).max(axis=0)
+            M[n] = c[:, :512].max(axis=0)
     return MFMA_SUM_ERR * batch.sm_scale * D, M
 
 
@@ -91,7 +93,7 @@ def reference(batch):
     ref_out, ref_lse = oracle.mla_decode(hn, hr, batch.cache, batch.kv_indptr, batch.kv_indices,
                                          batch.page_size, batch.sm_scale,
                                          kv_last_page_len=batch.kv_last_page_len,
-                                         kv_scale=batch.kv_scale)
+                                         qo_indptr=batch.qo_indptr, kv_scale=batch.kv_scale)
     D, M = score_bounds(batch, np.concatenate([hn, hr], axis=-1))
     return ref_out, ref_lse, D, M
 
@@ -135,6 +137,18 @@ def test_fp8_score_parity(dev, ps, num_cus):
         assert h.num_merges > 0  # the long rows are split
     ref_out, ref_lse, D, M = reference(batch)
     check(out, lse, ref_out, ref_lse, D, M, f"fp8 score ps={ps} num_cus={num_cus}")
+
+
+def test_fp8_score_several_rows_per_request(dev):
+    """Three query rows per request (qo_indptr): each row has its own quantised
+    query and exponents, and the rows of a request read the same tokens."""
+    batch = workloads.random_decode_batch(975, [40, 1500, 1, 333], num_heads=128, page_size=16,
+                                          cache_dtype="fp8_e4m3fn", rows_per_request=3)
+    say(f"fp8 score, {batch.num_rows} rows over {batch.batch} requests")
+    out, lse, _, h = run_qf8(batch, dev, num_cus=8)
+    assert h.num_rows == 12
+    ref_out, ref_lse, D, M = reference(batch)
+    check(out, lse, ref_out, ref_lse, D, M, "fp8 score qo_indptr")
 
 
 def test_fp8_score_graph_safe_plan_with_fewer_rows(dev):
