@@ -93,19 +93,20 @@ typedef struct {
 /*
  * fp8 score (e4m3fn cache, 128 heads, bf16 output, mla_decode only): the
  * score's contraction runs on the fp8 matrix core, twice the bf16 rate, with
- * the query quantised to e4m3fn. The fp8 cache itself is the FP8 KV cache of
- * the DeepSeek-V3/R1 optimisations page; quantising the query too is this
- * library's reading (the pages leave it open): per query row and head, the
- * 576 query values (absorbed no-rope part, then rope part) are scaled by
- * 2^-e, e the smallest integer with amax * 2^-e <= 448 (amax their largest
- * magnitude; e = 0 for a head of zeros), which is exact, and rounded to the
- * nearest e4m3fn code, ties to even. The score is then computed from these
- * codes times 2^e. Query values must be finite. mla_decode quantises the query into its workspace with a
- * kernel of its own before the decode launch; the rest of the path (softmax,
- * the P . latent product in bf16, merges) is unchanged. The results differ
- * from the bf16 score by the query's rounding (at most 2^-4 of each value)
- * and by the fp8 matrix core's internal sums (measured within 2^-12 of the
- * sum of the products' magnitudes).
+ * the query quantised to e4m3fn. The fp8 cache itself is the FP8 KV cache the
+ * SGLang v0.3 MLA page counts among its four decode optimisations; quantising
+ * the query too is this library's reading (the pages leave it open): per
+ * query row and head, the 576 query values (absorbed no-rope part, then rope
+ * part) are scaled by 2^-e, e the smallest integer with amax * 2^-e <= 448
+ * (amax their largest magnitude; e = 0 for a head of zeros), which is exact,
+ * and rounded to the nearest e4m3fn code, ties to even. The score is then
+ * computed from these codes times 2^e. Query values must be finite.
+ * mla_decode quantises the query into its workspace with a kernel of its own
+ * before the decode launch; the rest of the path (softmax, the P . latent
+ * product in bf16, merges) is unchanged. The results differ from the bf16
+ * score by the query's rounding (at most 2^-4 of each value) and by the fp8
+ * matrix core's internal sums (measured within 2^-12 of the sum of the
+ * products' magnitudes).
  */
 #define MLA_DECODE_FP8_SCORE 2
 
