@@ -151,6 +151,18 @@ def test_fp8_score_several_rows_per_request(dev):
     check(out, lse, ref_out, ref_lse, D, M, "fp8 score qo_indptr")
 
 
+def test_fp8_score_empty_requests(dev):
+    """Requests without tokens: lse -inf and a zero output, beside ordinary rows."""
+    batch = workloads.random_decode_batch(977, [0, 5, 0, 700, 0], num_heads=128, page_size=64,
+                                          cache_dtype="fp8_e4m3fn")
+    say("fp8 score with empty requests")
+    out, lse, _, _ = run_qf8(batch, dev, num_cus=8)
+    ref_out, ref_lse, D, M = reference(batch)
+    empty = batch.seq_lens == 0
+    assert np.isneginf(lse[empty]).all() and (out[empty] == 0).all()
+    check(out, lse, ref_out, ref_lse, D, M, "fp8 score empty requests")
+
+
 def test_fp8_score_graph_safe_plan_with_fewer_rows(dev):
     batch = workloads.random_decode_batch(971, [5, 700, 64], num_heads=128, page_size=64,
                                           cache_dtype="fp8_e4m3fn")
