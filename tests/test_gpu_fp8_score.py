@@ -74,7 +74,7 @@ def check(out, lse, ref_out, ref_lse, D, M, what):
     assert np.isfinite(out).all(), f"{what}: non-finite output"
     fin = ~np.isneginf(ref_lse)
     assert np.array_equal(np.isneginf(lse), ~fin), f"{what}: -inf lse pattern differs"
-    lse_err = np.abs(lse - ref_lse)[fin]
+    lse_err = np.abs(lse[fin] - ref_lse[fin])
     lse_tol = (TOL_LSE_MAX_ABS + D)[fin]
     slack = np.expm1(2 * D)[..., None] * M[:, None, :]
     err = np.abs(out - ref_out)
