@@ -115,8 +115,9 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
         const bool active = w * HW < a.num_heads;
 
         // ---- absorbed query -> registers (B operand of the score MFMA) ----
+        // Loaded with the first page-table entries (below), under one wait.
         bf16x8 q[kSteps];
-        if (active) {
+        auto load_query = [&] {
             const uint16_t* qn = a.q_nope + (int64_t)it.row * a.qn_sn + (int64_t)head * a.qn_sh;
             const uint16_t* qr = a.q_rope + (int64_t)it.row * a.qr_sn + (int64_t)head * a.qr_sh;
 #pragma unroll
@@ -124,11 +125,7 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
                 const int k0 = (HW == 32 ? 16 : 32) * s + 8 * gq;
                 q[s] = (s < kSteps * 8 / 9) ? load_bf16x8(qn + k0) : load_bf16x8(qr + (k0 - kLatent));
             }
-            // Let the query land before any tile load is issued: the compiler does not
-            // see the tile loads, so its own waits for these registers inside the
-            // loop would otherwise also drain the tiles in flight.
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        }
+        };
         if (MODE == kModeAppend && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
             // Fused append: the request's new row goes to the cache before any
             // wave loads a tile that holds it.
@@ -210,6 +207,12 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
             // The entries of tiles 0 .. kIdxLead-1, which steps read before the
             // loop's first wait; later ones come with the steps.
             for (int t = 0; t < kIdxLead && t < ntiles; ++t) issue_idx(t);
+            // The query goes out beside them and one wait covers both (an item
+            // without tiles needs no query). It must land before any tile load is
+            // issued: the compiler does not see the tile loads, so its own waits
+            // for these registers inside the loop would also drain the tiles in
+            // flight.
+            if (pass == 0 && active) load_query();
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             // One tile step. T is the buffer computed, N the one being filled;
             // distinct restrict-qualified parameters tell the compiler the two
