@@ -178,26 +178,21 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                 if (t < ntiles) issue_tile(t, t);
             }
         };
-        // Page indices of the first tiles, then their data; the query loads go
-        // out behind them, so the latencies of the two overlap.
-        prologue_idx();
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the page indices
-        if (MODE == kModeAppend && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
-            // Fused append: the request's new row goes to the cache before any
-            // wave loads a tile that holds it.
-            append_row<KV8>(a, it, tid, 256);
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the row's stores are done
-            __syncthreads();
-        }
-        if (ntiles > 0) start_tiles();
-
-        // ---- absorbed query -> registers ----
+        // ---- page indices of the first tiles, the absorbed query, the first tiles ----
+        // The query loads go out right behind the page indices, and the first wait
+        // leaves them in flight (loads retire in issue order, so vmcnt <= kQLoads
+        // means the indices have landed): the query's transfer overlaps the
+        // indices' round trip. The first tiles follow, and one wait covers them
+        // and the query.
         // bf16: 36 k-slices of 8 features. fp8 score: 9 steps of 32 codes, the
         // features 64 v + 16 gq + [0, 16) and 64 v + 32 + 16 gq + [0, 16), which
-        // are the bytes the step's two tile reads give this lane.
+        // are the bytes the step's two tile reads give this lane, and the head's
+        // exponent (19 loads).
+        constexpr int kQLoads = QF8 ? 19 : kSteps;
+        prologue_idx();
         bf16x8 q[QF8 ? 1 : kSteps];
         u32x8 q8[QF8 ? 9 : 1];
-        float sl2 = a.scale_log2;  // score scale (log2 units), times 2^e for the fp8 score
+        int q8e = 0;
         if constexpr (QF8) {
             const int64_t qrow = (int64_t)it.row * a.num_heads + head;
             const uint8_t* src = a.q8 + qrow * kRow + 16 * gq;
@@ -207,8 +202,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                 const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 64 * v + 32);
                 q8[v] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            sl2 = ldexpf(a.scale_log2, a.q8_exp[qrow]);
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), as below
+            q8e = a.q8_exp[qrow];
         } else {
             const uint16_t* qn = a.q_nope + (int64_t)it.row * a.qn_sn + (int64_t)head * a.qn_sh;
             const uint16_t* qr = a.q_rope + (int64_t)it.row * a.qr_sn + (int64_t)head * a.qr_sh;
@@ -217,12 +211,22 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                 const int f = L::q_feature(u, gq);
                 q[u] = u < 32 ? load_bf16x8(qn + f) : load_bf16x8(qr + (f - kLatent));
             }
-            // vmcnt(0), as a builtin the compiler accounts for: the query (the
-            // youngest loads) has landed, and with it the first tiles, so the
-            // compiler places no waits of its own in the loop, where they would
-            // also drain the tiles in flight.
-            __builtin_amdgcn_s_waitcnt(0x0F70);
         }
+        wait_vmcnt<kQLoads>();  // the page indices
+        if (MODE == kModeAppend && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
+            // Fused append: the request's new row goes to the cache before any
+            // wave loads a tile that holds it.
+            append_row<KV8>(a, it, tid, 256);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the row's stores are done
+            __syncthreads();
+        }
+        if (ntiles > 0) start_tiles();
+        // vmcnt(0), as a builtin the compiler accounts for: the query and the first
+        // tiles have landed, so the compiler places no waits of its own in the
+        // loop, where they would also drain the tiles in flight.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        // Score scale (log2 units), times 2^e for the fp8 score.
+        const float sl2 = QF8 ? ldexpf(a.scale_log2, q8e) : a.scale_log2;
 
         int sbase[L::kScoreBases], pbase[L::kPvBases];
 #pragma unroll

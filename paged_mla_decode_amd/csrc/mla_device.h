@@ -36,6 +36,12 @@ constexpr float kOverflowSlack = 64.0f;  // log2 units: probabilities stay below
 // own. Direct-to-LDS loads complete in issue order with the other vector
 // memory loads, so "vmcnt <= N" means everything but the N most recent loads
 // has landed in LDS.
+// The same wait for this wave alone, without the barrier.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
