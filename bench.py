@@ -106,32 +106,109 @@ def measured_traffic(summary, key="traffic_bytes_per_launch"):
     return int(v) if v.is_integer() else v
 
 
-def cpu_baseline(batch, target_s=12.0):
-    """Oracle GB/s on a prefix of the batch sized to about target_s seconds."""
+def warm_until_steady(torch, stream, step, min_steps, min_s=1.5, max_s=5.0, batch=25):
+    """Warm the GPU to steady clocks before a timed region, whatever --warmup
+    asks: run `min_steps` steps, then batches of `batch` steps until at least
+    `min_s` seconds have passed and two consecutive batches agree within 1%
+    (at most `max_s` seconds). Returns (seconds, steps run)."""
+    t0 = time.perf_counter()
+    done = 0
+    for _ in range(min_steps):
+        step(done)
+        done += 1
+    torch.cuda.synchronize()
+    prev = None
+    while True:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(batch):
+            step(done)
+            done += 1
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cur = e0.elapsed_time(e1)
+        el = time.perf_counter() - t0
+        steady = prev is not None and abs(cur - prev) <= 0.01 * prev
+        if el >= max_s or (el >= min_s and steady):
+            return el, done
+        prev = cur
+
+
+def median_plan_us(plan, reps=21):
+    """Host plan time: the median of `reps` calls after a warm one (the plan is
+    built once per batch and reused by every layer)."""
+    plan()
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        plan()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)) * 1e6
+
+
+def _timed_runs(fn, runs=3):
+    """One untimed warm-up call, then `runs` timed calls; the median seconds."""
+    fn()
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times))
+
+
+def _sized_subset(batch, seconds):
+    """The first requests of `batch` whose oracle run takes about `seconds`
+    with the oracle's current thread count (calibrated on two requests)."""
     import oracle
 
-    cal = batch.subset(range(2))
+    cal = batch.subset(range(min(2, batch.batch)))
     t0 = time.perf_counter()
     oracle.decode_batch(cal)
     dt = time.perf_counter() - t0
     rate = float(cal.seq_lens.sum()) / max(dt, 1e-9)  # tokens/s
-    want = rate * target_s
     cum = np.cumsum(batch.seq_lens.astype(np.int64))
-    n = int(min(batch.batch, max(1, np.searchsorted(cum, want) + 1)))
-    sub = batch.subset(range(n))
-    t0 = time.perf_counter()
-    oracle.decode_batch(sub)
-    dt = time.perf_counter() - t0
+    n = int(min(batch.batch, max(1, np.searchsorted(cum, rate * seconds) + 1)))
+    return batch.subset(range(n)), n
+
+
+def cpu_baseline(batch, run_s=3.0, one_core_s=2.0):
+    """The oracle's GB/s on a bounded prefix of the batch, on every host core:
+    one warm-up and three timed runs of the same prefix, the median reported.
+    The same protocol on one core for the tiny and the V2-Lite configurations."""
+    import oracle
+    import workloads
+
+    oracle.set_num_threads(0)
+    sub, n = _sized_subset(batch, run_s)
+    dt = _timed_runs(lambda: oracle.decode_batch(sub))
     toks = int(sub.seq_lens.sum())
-    return {
+    res = {
         "value": toks * batch.cache_bytes_per_token / dt / 1e9,
         "unit": "GB/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": f"first {n} of {batch.batch} requests ({toks} KV tokens, all {batch.num_heads} heads), "
-                  f"fp64 C oracle, {dt:.1f} s",
+                  f"fp64 C oracle, median of 3 runs after 1 warm-up, {dt:.2f} s per run",
         "tokens_per_s": sub.num_rows / dt,
     }
+    one = {}
+    oracle.set_num_threads(1)
+    try:
+        for name, make in (("tiny", workloads.tiny), ("v2_lite", workloads.v2_lite)):
+            b = make()
+            s1, n1 = _sized_subset(b, one_core_s)
+            d1 = _timed_runs(lambda: oracle.decode_batch(s1))
+            t1 = int(s1.seq_lens.sum())
+            one[name] = {"value": t1 * b.cache_bytes_per_token / d1 / 1e9, "unit": "GB/s", "cores": 1,
+                         "tokens_per_s": s1.num_rows / d1,
+                         "sample": f"first {n1} of {b.batch} requests ({t1} KV tokens, all "
+                                   f"{b.num_heads} heads), median of 3 runs after 1 warm-up, "
+                                   f"{d1:.3f} s per run"}
+    finally:
+        oracle.set_num_threads(0)
+    res["one_core"] = one
+    return res
 
 
 def main():
@@ -193,9 +270,8 @@ def main():
     dec = PagedMlaDecoder(batch.num_heads, batch.page_size, max_batch=batch.batch,
                           max_rows=batch.num_rows, kv_dtype=batch.cache_dtype, out_dtype="bf16",
                           device=dev, fp8_score=args.fp8_score)
-    t0 = time.perf_counter()
     h = dec.plan(batch.kv_indptr, batch.kv_last_page_len)
-    plan_us = (time.perf_counter() - t0) * 1e6
+    plan_us = median_plan_us(lambda: dec.plan(batch.kv_indptr, batch.kv_last_page_len))
     torch.cuda.synchronize()
     outs = [torch.empty((batch.num_rows, batch.num_heads, 512), dtype=torch.bfloat16, device=dev)
             for _ in sets]
@@ -230,9 +306,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_s, warm_steps = warm_until_steady(torch, stream, step, args.warmup)
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -284,7 +358,11 @@ def main():
         },
         "tokens_per_s": round(batch.num_rows / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "warmup_run": {"steps": warm_steps, "seconds": round(warm_s, 2),
+                       "rule": "at least --warmup steps, then until two 25-step batches agree "
+                               "within 1% after >= 1.5 s (at most 5 s)"},
         "plan_us": round(plan_us, 1),
+        "plan_us_note": "host plan + its copy to the device, median of 21 calls after a warm call",
         "plan": {"workers": h.num_workers, "items": h.num_items, "merges": h.num_merges,
                  "partials": h.num_partials, "capacity_tokens": h.chunk_tokens},
         "roofline": {
@@ -315,8 +393,9 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline_projections(p, target_s=10.0):
-    """Oracle absorb + project GB/s, repeated on the full shape for about target_s."""
+def cpu_baseline_projections(p, run_s=3.0):
+    """Oracle absorb + project GB/s: one warm-up and three timed runs, each
+    repeating the full shape for about run_s, the median reported."""
     import oracle
     import threadpoolctl
     import workloads
@@ -325,18 +404,24 @@ def cpu_baseline_projections(p, target_s=10.0):
     q, w_uk, w_uv, x = (f(a).astype(np.float64) for a in (p.q, p.w_uk, p.w_uv, p.x))
     N, H, D = q.shape
     nbytes = costs.absorb_bytes(N, H, D) + costs.project_bytes(N, H, D)
-    reps, t0 = 0, time.perf_counter()
-    while True:
+
+    def once():
         oracle.absorb_query(q, w_uk)
         oracle.project_output(x, w_uv)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= target_s:
-            break
+
+    t0 = time.perf_counter()
+    once()
+    reps = max(1, int(run_s / max(time.perf_counter() - t0, 1e-6)))
+
+    def run():
+        for _ in range(reps):
+            once()
+
+    dt = _timed_runs(run)
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
     return {"value": reps * nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} repetitions of the full shape (N={N}, H={H}), fp64 numpy per-head "
-                      f"products, {dt:.1f} s"}
+            "sample": f"{reps} repetitions of the full shape (N={N}, H={H}) per run, fp64 numpy "
+                      f"per-head products, median of 3 runs after 1 warm-up, {dt:.2f} s per run"}
 
 
 def bench_projections(args):
@@ -381,9 +466,7 @@ def bench_projections(args):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_s, warm_steps = warm_until_steady(torch, stream, step, args.warmup)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
@@ -438,6 +521,7 @@ def bench_projections(args):
                    "query_rows": N, "num_heads": H, "head_dim": D, "kv_lora_rank": A,
                    "parallelism": "single GPU"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "warmup_run": {"steps": warm_steps, "seconds": round(warm_s, 2)},
         "kernels_us": {"absorb": round(absorb_us, 2), "project": round(project_us, 2)},
         "roofline": {
             "kernel": kname,
@@ -457,14 +541,15 @@ def bench_projections(args):
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline_tree(tv, target_s=10.0):
+def cpu_baseline_tree(tv, run_s=4.0):
     """Oracle latent GB/s on the first rows of the cascade (each row's attention
-    over its prefix and its visible drafts), sized to about target_s."""
+    over its prefix and its visible drafts): one warm-up and three timed runs
+    of a prefix of rows sized to about run_s each, the median reported."""
     import oracle
 
     pre, W = tv.prefix, tv.width
 
-    def rows_ref(rows):
+    def rows_args(rows):
         kv_indptr, kv_indices = [0], []
         for r in rows:
             req, plen = r // W, int(tv.prefix_lens[r // W])
@@ -472,19 +557,27 @@ def cpu_baseline_tree(tv, target_s=10.0):
             slots = np.concatenate([tv.req_to_token[req, :plen], tv.req_to_token[req, plen + vis]])
             kv_indices.append(slots)
             kv_indptr.append(kv_indptr[-1] + len(slots))
-        t0 = time.perf_counter()
-        oracle.mla_decode(pre.q_nope[rows], pre.q_rope[rows], pre.cache,
-                          np.asarray(kv_indptr, np.int32), np.concatenate(kv_indices).astype(np.int32),
-                          1, pre.sm_scale, kv_last_page_len=np.ones(len(rows), np.int32))
-        return time.perf_counter() - t0, kv_indptr[-1]
+        return (np.asarray(kv_indptr, np.int32), np.concatenate(kv_indices).astype(np.int32))
 
-    dt, _ = rows_ref(list(range(2)))
-    n = int(min(pre.num_rows, max(2, 2 * target_s / max(dt, 1e-6))))
-    dt, toks = rows_ref(list(range(n)))
+    def run(rows, indptr, indices):
+        oracle.mla_decode(pre.q_nope[rows], pre.q_rope[rows], pre.cache, indptr, indices, 1,
+                          pre.sm_scale, kv_last_page_len=np.ones(len(rows), np.int32))
+
+    oracle.set_num_threads(0)
+    cal = list(range(2))
+    a = rows_args(cal)
+    t0 = time.perf_counter()
+    run(cal, *a)
+    dt = time.perf_counter() - t0
+    n = int(min(pre.num_rows, max(2, 2 * run_s / max(dt, 1e-6))))
+    rows = list(range(n))
+    a = rows_args(rows)
+    dt = _timed_runs(lambda: run(rows, *a))
+    toks = int(a[0][-1])
     return {"value": toks * 1152 / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"first {n} of {pre.num_rows} draft rows (prefix + visible drafts, all 128 heads), "
-                      f"fp64 C oracle, {dt:.1f} s"}
+                      f"fp64 C oracle, median of 3 runs after 1 warm-up, {dt:.2f} s per run"}
 
 
 def bench_tree_verify(args):
@@ -515,9 +608,8 @@ def bench_tree_verify(args):
     plan_us = (time.perf_counter() - t0) * 1e6
     # Single pass: every row over its prefix and then its visible drafts.
     d1 = PagedMlaDecoder(H, 1, max_batch=B, max_rows=N, device=dev, suffix_tokens=D)
-    t0 = time.perf_counter()
     h1 = d1.plan(pre.kv_indptr, pre.kv_last_page_len, pre.qo_indptr)
-    plan1_us = (time.perf_counter() - t0) * 1e6
+    plan1_us = median_plan_us(lambda: d1.plan(pre.kv_indptr, pre.kv_last_page_len, pre.qo_indptr))
     outs = [(torch.empty((N, H, 512), dtype=torch.bfloat16, device=dev),
              torch.empty((N, H), dtype=torch.float32, device=dev)) for _ in sets]
     tables = [tree_suffix_compact(s["mask"], s["r2t"], s["plen"], W) for s in sets]
@@ -555,9 +647,7 @@ def bench_tree_verify(args):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_s, warm_steps = warm_until_steady(torch, stream, step, args.warmup)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
@@ -613,6 +703,7 @@ def bench_tree_verify(args):
         "tokens_per_s": round(N / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "unique_latent_bytes": unique_bytes,
+        "warmup_run": {"steps": warm_steps, "seconds": round(warm_s, 2)},
         "plan_us": round(plan1_us, 1),
         "phases_us": {"compaction": round(compact_us, 2), "single_pass": round(single_us, 2),
                       "two_pass_prefix": round(prefix_us, 2),

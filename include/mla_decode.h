@@ -245,8 +245,12 @@ int32_t mla_decode_plan(const mla_decode_params* params, int32_t batch, const in
  *   sm_scale   softmax scale applied to the raw scores; finite and > 0.
  *   out_d      [N, H, 512] contiguous, out_dtype.
  *   lse_d      float [N, H] contiguous (natural log), or NULL.
- * The library never reads cache rows past a request's length, nor pool rows
- * outside its page list. Returns MLA_OK, MLA_ERR_INVALID_ARG,
+ * Reads: for each request, the cache rows of its tokens below its length,
+ * at the pages its kv_indices entries name, and nothing else of the cache.
+ * The library takes no pool size: it does not check those page numbers
+ * against the pool, and an entry outside it is an out-of-bounds device read.
+ * Callers that cannot vouch for their page tables check them on the host with
+ * mla_decode_validate_batch before the call. Returns MLA_OK, MLA_ERR_INVALID_ARG,
  * MLA_ERR_UNSUPPORTED, MLA_ERR_PLAN_MISMATCH, MLA_ERR_WORKSPACE_TOO_SMALL or
  * MLA_ERR_HIP.
  */
@@ -454,6 +458,46 @@ int32_t mla_project_output(const void* x_d, int64_t x_stride_n, int64_t x_stride
                            int64_t w_uv_stride_h, int64_t w_uv_stride_d, void* o_d,
                            int64_t o_stride_n, int64_t o_stride_h, int32_t num_rows,
                            int32_t num_heads, int32_t head_dim, void* stream);
+
+/*
+ * Host checks of a batch's index arrays against the pool, for callers that
+ * cannot vouch for them (the decode entry points take no pool size and read
+ * whatever rows the entries name). They read host copies only, enqueue
+ * nothing and need no device. Graph padding in the PR 49477 analysis
+ * (section 1) pins padded rows to offset 0 for exactly this reason: an index
+ * past the pool is an out-of-bounds read on the device.
+ *
+ * mla_decode_validate_batch: kv_indptr_h [batch+1] (and qo_indptr_h, when not
+ * NULL) start at 0 and never decrease; every entry kv_indices_h[e],
+ * e < kv_indptr_h[batch], is a page of the pool, 0 <= page < num_pool_pages;
+ * kv_last_page_len_h (when not NULL) is in [1, page_size] for every request
+ * with pages.
+ *
+ * mla_tree_validate_inputs: the inputs of mla_tree_suffix_compact. For every
+ * request r < num_requests, 0 <= prefix_lens_h[r] and prefix_lens_h[r] + width
+ * <= req_stride (the compaction reads req_to_token at columns
+ * [prefix_len, prefix_len + width)), and each of those draft slots is a pool
+ * row, 0 <= slot < num_pool_rows. req_to_token_h [num_requests, req_stride].
+ *
+ * mla_tree_validate_suffix: what mla_decode_tree_verify reads of the compacted
+ * table. For every row n < num_rows, suffix_lens_h[n] >= 0 and the entries
+ * suffix_table_h[n*suffix_stride + j], j < min(suffix_lens_h[n],
+ * suffix_tokens), are pool rows, 0 <= slot < num_pool_rows.
+ *
+ * Each returns MLA_OK, or MLA_ERR_INVALID_ARG for malformed arguments or the
+ * first entry out of range; *bad_entry (when not NULL) receives that entry's
+ * index in its array, or -1 when no single entry is at fault.
+ */
+int32_t mla_decode_validate_batch(int32_t page_size, int32_t batch, const int32_t* qo_indptr_h,
+                                  const int32_t* kv_indptr_h, const int32_t* kv_indices_h,
+                                  const int32_t* kv_last_page_len_h, int64_t num_pool_pages,
+                                  int64_t* bad_entry);
+int32_t mla_tree_validate_inputs(const int32_t* req_to_token_h, int64_t req_stride,
+                                 int32_t num_requests, const int32_t* prefix_lens_h, int32_t width,
+                                 int64_t num_pool_rows, int64_t* bad_entry);
+int32_t mla_tree_validate_suffix(const int32_t* suffix_table_h, int64_t suffix_stride,
+                                 const int32_t* suffix_lens_h, int32_t num_rows,
+                                 int32_t suffix_tokens, int64_t num_pool_rows, int64_t* bad_entry);
 
 /*
  * Name of the decode kernel instantiation these parameters select (static

@@ -70,6 +70,8 @@ def _load():
             lib.oracle_decode_elements.argtypes = [i32, p, i64, p]
             lib.oracle_num_threads.restype = i32
             lib.oracle_num_threads.argtypes = []
+            lib.oracle_set_num_threads.restype = None
+            lib.oracle_set_num_threads.argtypes = [i32]
             _lib = lib
     return _lib
 
@@ -80,6 +82,11 @@ def _ptr(a):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the next oracle calls; n <= 0 restores the default (all cores)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def bf16_to_double(bits) -> np.ndarray:

@@ -97,6 +97,18 @@ int32_t oracle_num_threads(void) {
 #endif
 }
 
+/* Threads the next calls use (the CPU baseline times one core as well as all
+ * of them). n <= 0 restores the OpenMP default. */
+void oracle_set_num_threads(int32_t n) {
+#ifdef _OPENMP
+    static int32_t dflt = 0;
+    if (dflt == 0) dflt = (int32_t)omp_get_max_threads();
+    omp_set_num_threads(n > 0 ? n : dflt);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Absorbed-MLA decode.
  *

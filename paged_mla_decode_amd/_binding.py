@@ -117,12 +117,21 @@ _lib.mla_tree_suffix_compact.argtypes = [_p, _i64, _p, _i64, _p, _i32, _i32, _i3
 for _fn in (_lib.mla_absorb_query, _lib.mla_project_output):
     _fn.restype = _i32
     _fn.argtypes = [_p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i32, _i32, _i32, _p]
+_PI64 = ctypes.POINTER(_i64)
+_lib.mla_decode_validate_batch.restype = _i32
+_lib.mla_decode_validate_batch.argtypes = [_i32, _i32, _p, _p, _p, _p, _i64, _PI64]
+_lib.mla_tree_validate_inputs.restype = _i32
+_lib.mla_tree_validate_inputs.argtypes = [_p, _i64, _i32, _p, _i32, _i64, _PI64]
+_lib.mla_tree_validate_suffix.restype = _i32
+_lib.mla_tree_validate_suffix.argtypes = [_p, _i64, _p, _i32, _i32, _i64, _PI64]
 
 EXPORTED_SYMBOLS = ("mla_status_string", "mla_decode_variant", "mla_decode_workspace_size",
                     "mla_decode_plan", "mla_decode", "mla_decode_append", "mla_decode_suffix_merge",
                     "mla_decode_tree_verify",
                     "mla_merge_states",
-                    "mla_tree_suffix_compact", "mla_absorb_query", "mla_project_output")
+                    "mla_tree_suffix_compact", "mla_absorb_query", "mla_project_output",
+                    "mla_decode_validate_batch", "mla_tree_validate_inputs",
+                    "mla_tree_validate_suffix")
 
 
 class MlaError(RuntimeError):
@@ -291,3 +300,35 @@ def read_plan(plan_h):
     workers = (ctypes.c_int32 * (h.num_workers + 1)).from_buffer_copy(
         ctypes.string_at(base + h.workers_offset, (h.num_workers + 1) * 4))
     return h, list(items), list(merges), list(workers)
+
+
+# ---- host checks of index arrays against the pool ----
+# Each takes host arrays (numpy int32, C-contiguous) and returns
+# (status, bad_entry): the first offending entry's index, or -1.
+
+def mla_decode_validate_batch(page_size, batch, qo_indptr_h, kv_indptr_h, kv_indices_h,
+                              kv_last_page_len_h, num_pool_pages):
+    bad = _i64(-1)
+    st = _lib.mla_decode_validate_batch(int(page_size), int(batch), _ptr(qo_indptr_h),
+                                        _ptr(kv_indptr_h), _ptr(kv_indices_h),
+                                        _ptr(kv_last_page_len_h), int(num_pool_pages),
+                                        ctypes.byref(bad))
+    return st, bad.value
+
+
+def mla_tree_validate_inputs(req_to_token_h, req_stride, num_requests, prefix_lens_h, width,
+                             num_pool_rows):
+    bad = _i64(-1)
+    st = _lib.mla_tree_validate_inputs(_ptr(req_to_token_h), int(req_stride), int(num_requests),
+                                       _ptr(prefix_lens_h), int(width), int(num_pool_rows),
+                                       ctypes.byref(bad))
+    return st, bad.value
+
+
+def mla_tree_validate_suffix(suffix_table_h, suffix_stride, suffix_lens_h, num_rows, suffix_tokens,
+                             num_pool_rows):
+    bad = _i64(-1)
+    st = _lib.mla_tree_validate_suffix(_ptr(suffix_table_h), int(suffix_stride), _ptr(suffix_lens_h),
+                                       int(num_rows), int(suffix_tokens), int(num_pool_rows),
+                                       ctypes.byref(bad))
+    return st, bad.value

@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         // features 64 v + 16 gq + [0, 16) and 64 v + 32 + 16 gq + [0, 16), which
         // are the bytes the step's two tile reads give this lane, and the head's
         // exponent (19 loads).
-        constexpr int kQLoads = QF8 ? 19 : kSteps;
+        constexpr int kQLoads = kSteps;  // the bf16 query's vector loads
         prologue_idx();
         bf16x8 q[QF8 ? 1 : kSteps];
         u32x8 q8[QF8 ? 9 : 1];
@@ -212,7 +212,15 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                 q[u] = u < 32 ? load_bf16x8(qn + f) : load_bf16x8(qr + (f - kLatent));
             }
         }
-        wait_vmcnt<kQLoads>();  // the page indices
+        // The page indices: the bf16 query is 36 vector loads issued after them,
+        // which the wait leaves in flight (tests/test_isa_waits.py checks the
+        // compiled kernels for at least kQLoads loads between the last index load
+        // and this wait). The fp8-score instantiation waits for everything: its
+        // query loads share the stretch with spill traffic the compiler places.
+        if constexpr (QF8)
+            wait_vmcnt<0>();
+        else
+            wait_vmcnt_query<kQLoads>();
         if (MODE == kModeAppend && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
             // Fused append: the request's new row goes to the cache before any
             // wave loads a tile that holds it.

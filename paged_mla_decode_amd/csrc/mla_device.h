@@ -42,6 +42,18 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// The wait that follows an item's page-index loads and its query loads: at
+// most N vector memory operations outstanding. Loads retire in issue order, so
+// when at least N loads were issued after the page-index loads, the indices
+// have landed while the last N (query) loads may still be in flight. The
+// trailing assembly comment tags it, so that a host test can check that
+// invariant in the compiler's output (at least N vector loads between the
+// last page-index load and this wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_query() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0) ; mla-query-wait" ::"n"(N) : "memory");
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");

@@ -45,6 +45,22 @@ def test_shapes(dev, H, ps):
 
 
 @pytest.mark.parametrize("H", [16, 128])
+@pytest.mark.parametrize("ps", [3, 48])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
+def test_odd_page_sizes(dev, H, ps, kv):
+    """Page sizes that are not powers of two take the kernels' division and
+    remainder branch of the address generation (token -> page, in-page row);
+    tiles then straddle pages at arbitrary tokens."""
+    batch = workloads.random_decode_batch(300 + H + ps, LENS, num_heads=H, page_size=ps, cache_dtype=kv)
+    say(f"odd page size H={H} ps={ps} kv={kv}")
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    for splits in (1, 0):
+        out, lse, dec = run_decode(batch, dev, "bf16", max_splits=splits, num_cus=8)
+        h = dec.header()
+        compare(out, lse, ref_out, ref_lse, False, f"H={H} ps={ps} kv={kv} merges={h.num_merges}")
+
+
+@pytest.mark.parametrize("H", [16, 128])
 def test_fp32_mode_with_splits(dev, H):
     batch = workloads.random_decode_batch(7 + H, [5, 300, 1000, 77], num_heads=H, page_size=16)
     say(f"fp32 H={H}")

@@ -12,7 +12,11 @@ max_t sum_k |code_q,k * 2^e * code_c,tk| for a row and head. Scores off by at
 most D move the lse by at most D and every probability by a factor within
 e^(+-2D), so each output element moves by at most (e^(2D) - 1) * max_t |v_t|.
 Both terms are added to the bf16-output tolerances of the other decode tests,
-which cover the rest of the arithmetic (identical to the fp8-cache path)."""
+which cover the rest of the arithmetic (identical to the fp8-cache path).
+The 2^-12 figure is a measurement of the matrix core, not a derivation (its
+internal summation order and rounding are not documented), so every check
+also asserts the plain bf16 gates (max-abs 2e-2, relative L2 5e-3, lse 1e-3)
+against the oracle with the dequantised query."""
 import numpy as np
 import pytest
 import torch
@@ -21,7 +25,6 @@ import oracle
 import workloads
 from gpu_util import (TOL_BF16_MAX_ABS, TOL_BF16_REL_L2, TOL_LSE_MAX_ABS, batch_to_device,
                       require_gpu, say)
-from test_gpu_configs import sampled_requests
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +89,11 @@ def check(out, lse, ref_out, ref_lse, D, M, what):
     assert (lse_err <= lse_tol).all(), f"{what}: lse beyond bound"
     assert (err <= TOL_BF16_MAX_ABS + slack).all(), f"{what}: output beyond bound"
     assert rel <= rel_tol, f"{what}: rel_l2 {rel}"
+    # The plain gates of the bf16 path hold as well: the derived slack above only
+    # widens them by the fp8 matrix core's measured internal rounding.
+    assert float(err.max()) <= TOL_BF16_MAX_ABS, f"{what}: max_abs {float(err.max())} (plain gate)"
+    assert rel <= TOL_BF16_REL_L2, f"{what}: rel_l2 {rel} (plain gate)"
+    assert float(lse_err.max(initial=0.0)) <= TOL_LSE_MAX_ABS, f"{what}: lse (plain gate)"
 
 
 def reference(batch):
@@ -172,15 +180,12 @@ def test_fp8_score_graph_safe_plan_with_fewer_rows(dev):
     check(out, lse, ref_out, ref_lse, D, M, "fp8 score graph-safe")
 
 
-def test_fp8_score_skewed_batch_sampled_rows(dev):
+def test_fp8_score_skewed_batch_all_rows(dev):
     """The skewed fp8 workload at full size (a 131,072-token request split
-    across the chip beside 31 short ones), sampled requests against the oracle."""
+    across the chip beside 31 short ones), every row against the oracle."""
     batch = workloads.skewed_fp8()
     say(f"fp8 score, skewed fp8: tokens={int(batch.seq_lens.sum())}")
     out, lse, _, h = run_qf8(batch, dev)
-    reqs = sampled_requests(batch, 3, seed=13)
-    sub = batch.subset(reqs)
-    ref_out, ref_lse, D, M = reference(sub)
-    say(f"  plan: items={h.num_items} merges={h.num_merges}; sampled {reqs.tolist()} "
-        f"(lengths {batch.seq_lens[reqs].tolist()})")
-    check(out[reqs], lse[reqs], ref_out, ref_lse, D, M, "fp8 score skewed sampled")
+    ref_out, ref_lse, D, M = reference(batch)
+    say(f"  plan: items={h.num_items} merges={h.num_merges}; all {batch.num_rows} rows")
+    check(out, lse, ref_out, ref_lse, D, M, "fp8 score skewed, all rows")

@@ -1,14 +1,18 @@
 """Graph-safe decode (MLA_DECODE_GRAPH_SAFE): one call captured in a HIP graph,
 replayed after each new plan is built into the same workspace, must give what
-an eager call on that plan gives, bit for bit. Between replays the test does
-eager work of its own and synchronises, and every replay is checked. Plans
-with fewer query rows leave the output rows past them untouched (padding)."""
+an eager call on that plan gives, bit for bit, and what the oracle gives
+within the tolerances. Between replays the test does eager work of its own and
+synchronises, and every replay is checked. Plans with fewer query rows leave
+the output rows past them untouched (padding)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
-from gpu_util import bf16_to_device, require_gpu, say
+from gpu_util import bf16_to_device, compare, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +48,28 @@ def test_graph_replay_follows_the_plan(dev, H, fp8_score):
         return indptr, indices, last
 
     batches = [csr(lens, 100 + k) for k, lens in enumerate(lens_set)]
+
+    def oracle_batch(k):
+        """Batch k over the shared pool, as a DecodeBatch for the oracle."""
+        indptr, indices, last = batches[k]
+        n = len(lens_set[k])
+        return dataclasses.replace(
+            pool, qo_indptr=np.arange(n + 1, dtype=np.int32), kv_indptr=indptr, kv_indices=indices,
+            kv_last_page_len=last, seq_lens=np.asarray(lens_set[k], np.int32),
+            q_nope=np.ascontiguousarray(q_all[:n, :, :512]), q_rope=np.ascontiguousarray(q_all[:n, :, 512:]))
+
+    def check_oracle(k, o, l, what):
+        b = oracle_batch(k)
+        n = b.num_rows
+        o = o[:n].float().cpu().numpy().astype(np.float64)
+        l = l[:n].cpu().numpy().astype(np.float64)
+        if fp8_score:
+            from test_gpu_fp8_score import check, reference
+            ref_out, ref_lse, D, M = reference(b)
+            check(o, l, ref_out, ref_lse, D, M, what)
+        else:
+            ref_out, ref_lse = oracle.decode_batch(b)
+            compare(o, l, ref_out, ref_lse, False, what)
     max_idx = max(len(b[1]) for b in batches)
     idx = torch.zeros(max_idx, dtype=torch.int32, device=dev)  # fixed buffer the graph reads
     dec = PagedMlaDecoder(H, ps, max_batch=B, num_cus=16, device=dev, graph_safe=True, kv_dtype=kv,
@@ -60,6 +86,7 @@ def test_graph_replay_follows_the_plan(dev, H, fp8_score):
     assert h0.num_merges > 0
     dec.run(qn, qr, cache, idx, pool.sm_scale, pool.kv_scale, out=out, lse=lse)  # warm up outside the capture
     torch.cuda.synchronize()
+    check_oracle(0, out, lse, f"H={H} fp8_score={fp8_score} graph-safe eager call vs oracle")
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -81,6 +108,7 @@ def test_graph_replay_follows_the_plan(dev, H, fp8_score):
         say(f"H={H} fp8_score={fp8_score} replay {rep}: batch {k} rows={rows} merges={h.num_merges} wide={h.num_wide_merges}")
         assert torch.equal(out[:rows], ref_out[:rows]) and torch.equal(lse[:rows], ref_lse[:rows]), \
             f"replay {rep} (batch {k}) differs from the eager call"
+        check_oracle(k, out, lse, f"replay {rep} vs oracle")
         assert torch.equal(out[rows:], sentinel_out) and torch.equal(lse[rows:], sentinel_lse), \
             "padding rows were written"
         out[:rows].zero_()  # eager work between replays
@@ -99,10 +127,12 @@ def test_tree_verify_step_replays_from_one_graph(dev):
     rows_pad = N + 16  # graph padding rows: the compaction zeroes them, the decode never plans them
     base = trees[0].prefix
     cache = bf16_to_device(base.cache, dev)  # one pool; every tree's slots hold values in it
+    pool_h = base.cache.reshape(-1, 576).copy()  # the same pool on the host, for the oracle
     for t in trees[1:]:
         used = np.unique(t.req_to_token)
         cache.view(-1, 576)[torch.from_numpy(used.astype(np.int64)).to(dev)] = \
             bf16_to_device(t.prefix.cache.reshape(-1, 576)[used], dev)
+        pool_h[used] = t.prefix.cache.reshape(-1, 576)[used]
     qn = torch.zeros((rows_pad, H, 512), dtype=torch.bfloat16, device=dev)
     qr = torch.zeros((rows_pad, H, 64), dtype=torch.bfloat16, device=dev)
     mask = torch.zeros((N, W), dtype=torch.uint8, device=dev)
@@ -150,4 +180,19 @@ def test_tree_verify_step_replays_from_one_graph(dev):
         torch.cuda.synchronize()
         say(f"tree replay {rep}: tree {k}, prefix {int(trees[k].prefix_lens[0])}")
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {rep} differs"
+        # Every row against the oracle: its prefix, then its visible drafts.
+        t = trees[k]
+        p = t.prefix
+        kv_indptr, kv_indices = [0], []
+        for r in range(N):
+            req, pl = r // W, int(t.prefix_lens[r // W])
+            vis = np.nonzero(t.tree_mask[r])[0]
+            kv_indices.append(np.concatenate([t.req_to_token[req, :pl], t.req_to_token[req, pl + vis]]))
+            kv_indptr.append(kv_indptr[-1] + len(kv_indices[-1]))
+        ref_out, ref_lse = oracle.mla_decode(
+            p.q_nope, p.q_rope, pool_h.reshape(-1, 1, 576), np.asarray(kv_indptr, np.int32),
+            np.concatenate(kv_indices).astype(np.int32), 1, base.sm_scale,
+            kv_last_page_len=np.ones(N, np.int32))
+        compare(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+                ref_out, ref_lse, False, f"tree replay {rep} vs oracle")
         out.zero_()

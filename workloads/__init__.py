@@ -195,7 +195,10 @@ def quantize_e4m3fn(cache_bf16: np.ndarray, rows: np.ndarray):
 
 
 def make_decode_batch(name, seed, seq_lens_fn, num_heads, page_size, pool_pages_fn,
-                      cache_dtype="bf16", rows_per_request=1) -> DecodeBatch:
+                      cache_dtype="bf16", rows_per_request=1, layout_only=False) -> DecodeBatch:
+    """layout_only: draw the lengths and the page layout only (the same arrays
+    as the full batch, since they come first in the draw order); the queries
+    and the cache are then empty arrays ([N, H, 0] and [pool_pages, ps, 0])."""
     rng = np.random.Generator(np.random.PCG64(seed))
     seq_lens = np.asarray(seq_lens_fn(rng), dtype=np.int64)
     npages = (seq_lens + page_size - 1) // page_size
@@ -203,6 +206,15 @@ def make_decode_batch(name, seed, seq_lens_fn, num_heads, page_size, pool_pages_
     kv_indptr, kv_indices, last = layout_from_lengths(seq_lens, page_size, pool_pages, rng)
     B = len(seq_lens)
     N = B * rows_per_request
+    if layout_only:
+        return DecodeBatch(
+            name=name, num_heads=num_heads, page_size=page_size,
+            qo_indptr=(np.arange(B + 1, dtype=np.int32) * rows_per_request),
+            kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last,
+            seq_lens=seq_lens.astype(np.int32), q_nope=np.zeros((N, num_heads, 0), np.uint16),
+            q_rope=np.zeros((N, num_heads, 0), np.uint16),
+            cache=np.zeros((pool_pages, page_size, 0), np.uint16 if cache_dtype == "bf16" else np.uint8),
+            cache_dtype=cache_dtype, seed=seed)
     q_nope = _draw_bf16(rng, (N, num_heads, KV_LORA_RANK))
     q_rope = _draw_bf16(rng, (N, num_heads, ROPE_DIM))
     rows = token_rows(kv_indptr, kv_indices, seq_lens, page_size)
@@ -224,19 +236,20 @@ def make_decode_batch(name, seed, seq_lens_fn, num_heads, page_size, pool_pages_
 # The five workloads. Each returns a fresh, fully seeded batch.
 # ---------------------------------------------------------------------------
 
-def tiny(seed: int = 1) -> DecodeBatch:
+def tiny(seed: int = 1, layout_only: bool = False) -> DecodeBatch:
     """B=2 with 7 and 33 tokens, H=16, page size 1, a pool of 64 slots."""
     return make_decode_batch(
         "tiny", seed, lambda rng: np.array([7, 33]), num_heads=16, page_size=1,
-        pool_pages_fn=lambda need: 64)
+        pool_pages_fn=lambda need: 64, layout_only=layout_only)
 
 
-def v2_lite(seed: int = 2, batch: int = 64) -> DecodeBatch:
+def v2_lite(seed: int = 2, batch: int = 64, layout_only: bool = False) -> DecodeBatch:
     """DeepSeek-V2-Lite-shaped decode: H=16, page size 1, L ~ U{512..4096},
     slots scattered over a pool of 300,000."""
     return make_decode_batch(
         "v2_lite", seed, lambda rng: rng.integers(512, 4096, size=batch, endpoint=True),
-        num_heads=16, page_size=1, pool_pages_fn=lambda need: max(300_000, need))
+        num_heads=16, page_size=1, pool_pages_fn=lambda need: max(300_000, need),
+        layout_only=layout_only)
 
 
 def lognormal_lengths(rng, batch, median=2048.0, sigma=0.8, lo=16, hi=16384):
@@ -244,16 +257,16 @@ def lognormal_lengths(rng, batch, median=2048.0, sigma=0.8, lo=16, hi=16384):
     return np.clip(np.rint(np.exp(math.log(median) + sigma * z)), lo, hi).astype(np.int64)
 
 
-def v3(seed: int = 3, batch: int = 128) -> DecodeBatch:
+def v3(seed: int = 3, batch: int = 128, layout_only: bool = False) -> DecodeBatch:
     """DeepSeek-V3-shaped decode: H=128, page size 64, lognormal lengths
     (median 2048, sigma 0.8, clipped to [16, 16384]), pages permuted."""
     return make_decode_batch(
         "v3", seed, lambda rng: lognormal_lengths(rng, batch), num_heads=128, page_size=64,
-        pool_pages_fn=lambda need: max(8192, need))
+        pool_pages_fn=lambda need: max(8192, need), layout_only=layout_only)
 
 
 def skewed_fp8(seed: int = 5, short_len: int = 1024, long_len: int = 131072,
-               batch: int = 32) -> DecodeBatch:
+               batch: int = 32, layout_only: bool = False) -> DecodeBatch:
     """One very long request among short ones, H=128, page size 64, fp8 cache."""
     def lens(rng):
         L = np.full(batch, short_len, dtype=np.int64)
@@ -261,7 +274,7 @@ def skewed_fp8(seed: int = 5, short_len: int = 1024, long_len: int = 131072,
         return L
     return make_decode_batch(
         "skewed_fp8", seed, lens, num_heads=128, page_size=64,
-        pool_pages_fn=lambda need: 2 * need, cache_dtype="fp8_e4m3fn")
+        pool_pages_fn=lambda need: 2 * need, cache_dtype="fp8_e4m3fn", layout_only=layout_only)
 
 
 @dataclasses.dataclass
