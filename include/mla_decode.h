@@ -262,6 +262,33 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
                    void* out_d, float* lse_d, void* stream);
 
 /*
+ * mla_decode_noalloc - mla_decode without a workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. The plan (built by mla_decode_plan
+ * with workspace_d = NULL) is copied by this call into a scratch array the
+ * library keeps in device memory (64 MiB per GPU, held until the process
+ * ends), which also holds the split-KV partials; the call allocates nothing.
+ * plan_h must stay unchanged until that asynchronous copy has run.
+ *
+ * Every call on one GPU shares that GPU's scratch and leaves its contents
+ * there: calls that overlap on one GPU (different streams, or different
+ * threads without ordering) race and give wrong results. Everything the
+ * kernels need zeroed comes with the plan copy of each call.
+ *
+ * Arguments and results as for mla_decode (without workspace_d and
+ * workspace_bytes). Returns those of mla_decode, and
+ * MLA_ERR_WORKSPACE_TOO_SMALL when the plan needs more than the 64 MiB
+ * scratch (mla_decode_workspace_size reports the bytes; at 128 heads a
+ * bf16 partial is 128 KiB, so about 500 split-KV pieces fit).
+ */
+int32_t mla_decode_noalloc(const mla_decode_params* params, const void* plan_h,
+                           const void* q_nope_d, int64_t q_nope_stride_n, int64_t q_nope_stride_h,
+                           const void* q_rope_d, int64_t q_rope_stride_n, int64_t q_rope_stride_h,
+                           const void* kv_cache_d, float kv_scale, const int32_t* kv_indices_d,
+                           const int32_t* kv_lens_d, float sm_scale, void* out_d, float* lse_d,
+                           void* stream);
+
+/*
  * mla_decode_append - mla_decode with the new token's cache row written in the
  * same launch (the fused KV-cache update of the tpu-inference V2 MLA kernel,
  * sglang-jax MLA gap page, section 2.4; the nope and rope parts are written

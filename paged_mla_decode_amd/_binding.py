@@ -100,6 +100,9 @@ _lib.mla_decode_plan.argtypes = [_PARAMS, _i32, _p, _p, _p, _p, _sz, _p, _sz, _p
 _lib.mla_decode.restype = _i32
 _lib.mla_decode.argtypes = [_PARAMS, _p, _p, _sz, _p, _i64, _i64, _p, _i64, _i64, _p, _f32, _p,
                             _p, _f32, _p, _p, _p]
+_lib.mla_decode_noalloc.restype = _i32
+_lib.mla_decode_noalloc.argtypes = [_PARAMS, _p, _p, _i64, _i64, _p, _i64, _i64, _p, _f32, _p, _p, _f32,
+                                    _p, _p, _p]
 _lib.mla_decode_append.restype = _i32
 _lib.mla_decode_append.argtypes = [_PARAMS, _p, _p, _sz, _p, _i64, _i64, _p, _i64, _i64, _p, _f32,
                                    _p, _p, _i64, _p, _i64, _f32, _p, _p, _p]
@@ -131,7 +134,7 @@ EXPORTED_SYMBOLS = ("mla_status_string", "mla_decode_variant", "mla_decode_works
                     "mla_merge_states",
                     "mla_tree_suffix_compact", "mla_absorb_query", "mla_project_output",
                     "mla_decode_validate_batch", "mla_tree_validate_inputs",
-                    "mla_tree_validate_suffix")
+                    "mla_tree_validate_suffix", "mla_decode_noalloc")
 
 
 class MlaError(RuntimeError):
@@ -216,6 +219,16 @@ def mla_decode(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_st
                            int(q_rope_stride_h), _ptr(kv_cache_d), float(kv_scale),
                            _ptr(kv_indices_d), _ptr(kv_lens_d), float(sm_scale), _ptr(out_d),
                            _ptr(lse_d), _stream(stream))
+
+
+def mla_decode_noalloc(params, plan_h, q_nope_d, q_nope_stride_n, q_nope_stride_h, q_rope_d,
+                       q_rope_stride_n, q_rope_stride_h, kv_cache_d, kv_scale, kv_indices_d,
+                       kv_lens_d, sm_scale, out_d, lse_d, stream=None):
+    return _lib.mla_decode_noalloc(ctypes.byref(params), _ptr(plan_h), _ptr(q_nope_d),
+                                   int(q_nope_stride_n), int(q_nope_stride_h), _ptr(q_rope_d),
+                                   int(q_rope_stride_n), int(q_rope_stride_h), _ptr(kv_cache_d),
+                                   float(kv_scale), _ptr(kv_indices_d), _ptr(kv_lens_d),
+                                   float(sm_scale), _ptr(out_d), _ptr(lse_d), _stream(stream))
 
 
 def mla_decode_append(params, plan_h, workspace_d, workspace_bytes, q_nope_d, q_nope_stride_n,

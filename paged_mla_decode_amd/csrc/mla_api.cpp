@@ -147,7 +147,7 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
                     int64_t q_rope_stride_h, const void* kv_cache_d, float kv_scale,
                     const int32_t* kv_indices_d, const int32_t* kv_lens_d, const AppendIn* app,
                     const PrefixIn* pre, const TreeIn* tree, float sm_scale, void* out_d, float* lse_d,
-                    void* stream) {
+                    void* stream, bool copy_plan = false) {
     if (!params || !plan_h || !workspace_d) return MLA_ERR_INVALID_ARG;
     Variant v;
     if (!select_variant(params, &v)) return MLA_ERR_UNSUPPORTED;
@@ -236,6 +236,10 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
         a.sfx_lens = tree->lens;
         a.sfx_max = params->suffix_tokens;
     }
+    // mla_decode_noalloc: the plan goes to the library's scratch first.
+    if (copy_plan && hipMemcpyAsync(const_cast<void*>(workspace_d), plan_h, (size_t)h->plan_bytes,
+                                    hipMemcpyHostToDevice, (hipStream_t)stream) != hipSuccess)
+        return MLA_ERR_HIP;
     if (qf8) {
         QuantQueryArgs q{};
         q.q_nope = a.q_nope;
@@ -299,6 +303,29 @@ int32_t mla_decode(const mla_decode_params* params, const void* plan_h, const vo
                        q_nope_stride_h, q_rope_d, q_rope_stride_n, q_rope_stride_h, kv_cache_d,
                        kv_scale, kv_indices_d, kv_lens_d, nullptr, nullptr, nullptr, sm_scale, out_d,
                        lse_d, stream);
+}
+
+int32_t mla_decode_noalloc(const mla_decode_params* params, const void* plan_h,
+                           const void* q_nope_d, int64_t q_nope_stride_n, int64_t q_nope_stride_h,
+                           const void* q_rope_d, int64_t q_rope_stride_n, int64_t q_rope_stride_h,
+                           const void* kv_cache_d, float kv_scale, const int32_t* kv_indices_d,
+                           const int32_t* kv_lens_d, float sm_scale, void* out_d, float* lse_d,
+                           void* stream) {
+    if (!params || !plan_h) return MLA_ERR_INVALID_ARG;
+    const mla_plan_header* h = static_cast<const mla_plan_header*>(plan_h);
+    if (h->magic != MLA_PLAN_MAGIC || h->version != MLA_PLAN_VERSION) return MLA_ERR_INVALID_ARG;
+    // The plan and everything it places in the workspace must fit the scratch.
+    if (h->workspace_bytes < h->plan_bytes || (size_t)h->workspace_bytes > kNoAllocScratchBytes)
+        return MLA_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    const int32_t st = noalloc_scratch(&ws);
+    if (st != MLA_OK) return st;
+    // decode_impl copies the plan to the start of the scratch (as mla_decode_plan
+    // puts it at the start of a workspace) after its argument checks.
+    return decode_impl(params, plan_h, ws, kNoAllocScratchBytes, q_nope_d, q_nope_stride_n, q_nope_stride_h,
+                       q_rope_d, q_rope_stride_n, q_rope_stride_h, kv_cache_d, kv_scale, kv_indices_d,
+                       kv_lens_d, nullptr, nullptr, nullptr, sm_scale, out_d, lse_d, stream,
+                       /*copy_plan=*/true);
 }
 
 int32_t mla_decode_tree_verify(const mla_decode_params* params, const void* plan_h,

@@ -28,6 +28,12 @@ struct Variant {
 bool select_variant(const mla_decode_params* p, Variant* v);
 const char* variant_name(const mla_decode_params* p);
 
+// mla_decode_noalloc: the library's static device scratch (plan copy,
+// partials, quantised query), 64 MiB per GPU, and its address on the current
+// device (mla_noalloc.hip).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+int32_t noalloc_scratch(void** ptr);
+
 // Host planner (pure host code, no HIP calls).
 int32_t plan_bounds(const mla_decode_params* p, int32_t num_cus, int32_t batch, int32_t num_rows,
                     size_t* plan_bytes, size_t* workspace_bytes);

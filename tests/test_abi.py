@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     lib = ctypes.CDLL(m.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -309,3 +309,24 @@ def test_fp8_score_rejected_by_the_fused_variants():
     # A plan built without the flag does not serve a call with it, nor the reverse.
     plain = m.make_params(128, 64, kv_dtype=m.MLA_DTYPE_FP8_E4M3FN, num_cus=256)
     assert m.mla_decode(**{**common, "params": plain}, kv_lens_d=None) == m.MLA_ERR_PLAN_MISMATCH
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    """mla_decode_noalloc checks the plan's workspace needs against its fixed
+    64 MiB scratch before touching the device (so this runs on the CPU)."""
+    p = B.make_params(128, 64, num_cus=2048)
+    lens = np.full(16, 200_000, np.int64)
+    npages = (lens + 63) // 64
+    indptr = np.concatenate([[0], np.cumsum(npages)]).astype(np.int32)
+    last = (lens - 64 * (npages - 1)).astype(np.int32)
+    pb, wb = B.mla_decode_workspace_size(p, 16, 16)
+    plan = np.zeros(pb, np.uint8)
+    assert B.mla_decode_plan(p, 16, None, indptr, last, plan, pb) == B.MLA_OK
+    h = B.read_plan(plan)[0]
+    assert h.workspace_bytes > 64 << 20
+    st = B.mla_decode_noalloc(p, plan, 16, 0, 0, 16, 0, 0, 16, 1.0, 16, None, 0.07, 16, None)
+    assert st == B.MLA_ERR_WORKSPACE_TOO_SMALL
+    bad = plan.copy()
+    bad[:4] = 0  # not a plan
+    st = B.mla_decode_noalloc(p, bad, 16, 0, 0, 16, 0, 0, 16, 1.0, 16, None, 0.07, 16, None)
+    assert st == B.MLA_ERR_INVALID_ARG
