@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "mla_append.h"
 #include "mla_device.h"
@@ -144,14 +145,18 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
             const int tau = min(kv_begin + tile * kTile + L::block_token(tb, lane), kv_end - 1);
             const int page = idx_ring[slot][w][lane / L::kCG];
             const int row = a.page_shift >= 0 ? (tau & (ps - 1)) : tau % ps;
-            const uint8_t* rowp = a.cache + ((int64_t)page * ps + row) * L::kRowBytes + dma_lane_off;
-            LDS_AS char* buf = (LDS_AS char*)smem + slot * L::kTileBytes;
-#pragma unroll
-            for (int i = 0; i < kLoadsMax; ++i) {
-                const int b = w + HS * i;
-                if (L::kNB % HS != 0 && b >= L::kNB) break;
-                dma16(rowp + (b / L::kNTB) * L::kCG * 16, buf + b * 1024);
-            }
+            // Load i of this wave is block b = w + HS i, chunk group
+            // b / kNTB = w / kNTB + (HS / kNTB) i: a per-wave base plus 128 i
+            // bytes in the row (both layouts), and 1 KiB block b in LDS.
+            static_assert(HS % L::kNTB == 0 && (HS / L::kNTB) * L::kCG * 16 == 128, "immediate step");
+            const uint8_t* rowp = a.cache + ((int64_t)page * ps + row) * L::kRowBytes + dma_lane_off +
+                                  (w / L::kNTB) * L::kCG * 16;
+            const uint32_t lds0 = (uint32_t)(uintptr_t)((LDS_AS char*)smem + slot * L::kTileBytes + w * 1024);
+            [&]<int... I>(std::integer_sequence<int, I...>) {
+                ((L::kNB % HS == 0 || w + HS * I < L::kNB ? dma16_imm<128 * I, 1024 * HS * I>(rowp, lds0)
+                                                          : (void)0),
+                 ...);
+            }(std::make_integer_sequence<int, kLoadsMax>{});
         };
         auto wrap = [](int x) { return x >= kStages ? x - kStages : x; };
         // Tile t and its page indices live in slot t % kStages.

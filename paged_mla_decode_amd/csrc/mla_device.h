@@ -79,21 +79,26 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 16-byte direct global->LDS load: lane l's 16 bytes land at lds + 16 l.
-// Issued as inline assembly so that the compiler's wait-count model never sees
-// these LDS writes (it would otherwise drain every load before each LDS read);
-// wait_vmcnt_barrier() orders them instead. M0 holds the wave-uniform LDS
-// address; one wait state separates its write from the load.
-__device__ __forceinline__ void dma16(const void* src, LDS_AS void* dst) {
-    const uint32_t lds = (uint32_t)(uintptr_t)dst;
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+// 16-byte direct global->LDS load: lane l's 16 bytes of src + kOff land at
+// lds_base + kLdsAdd + 16 l. Issued as inline assembly so that the compiler's
+// wait-count model never sees these LDS writes (it would otherwise drain every
+// load before each LDS read); wait_vmcnt_barrier() orders them instead. M0
+// holds the wave-uniform LDS address; one wait state separates its write from
+// the load. kOff is the load's immediate offset and kLdsAdd a constant added to
+// M0: one SALU write of M0 and no address arithmetic per load. The immediate offset moves the LDS
+// destination too (lane l's 16 bytes land at M0 + offset + 16 l), so M0 gets
+// kLdsAdd - kOff. A wave's blocks of one tile differ by such constants.
+template <int kOff, int kLdsAdd>
+__device__ __forceinline__ void dma16_imm(const void* src, uint32_t lds_base) {
+    static_assert(kOff >= 0 && kOff < 4096, "13-bit signed immediate offset");
+    asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%3"
                  :
-                 : "s"(lds), "v"(src)
+                 : "s"(lds_base), "v"(src), "n"(kLdsAdd - kOff), "n"(kOff)
                  : "memory", "m0");
 }
 
 // 4-byte direct global->LDS load: lane l's dword lands at lds + 4 l. Same
-// ordering rules as dma16.
+// ordering rules as dma16_imm.
 __device__ __forceinline__ void dma4(const void* src, LDS_AS void* dst) {
     const uint32_t lds = (uint32_t)(uintptr_t)dst;
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"

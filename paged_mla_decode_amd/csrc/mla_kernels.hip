@@ -29,6 +29,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "mla_append.h"
 #include "mla_device.h"
@@ -173,15 +174,23 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
                 rowp[k] = a.cache + ((int64_t)page * ps + row) * L::kRowBytes + dma_lane_off;
             }
         };
+        // Load i of this wave is block b = w + HS i: token row k = i % kKs of the
+        // wave, chunk group b / kNTB. With one row per wave (HS a multiple of
+        // kNTB) that group is w / kNTB + (HS / kNTB) i; with kKs rows it is
+        // i / kKs (w + HS k < kNTB). Either way a per-row base plus a
+        // compile-time byte offset, and 1 KiB block b in LDS.
         auto issue_tile = [&](LDS_AS char* base, const uint8_t* const* rowp) {
-#pragma unroll
-            for (int i = 0; i < kLoadsMax; ++i) {
-                const int b = w + HS * i;
-                if (L::kNB % HS != 0 && b >= L::kNB) break;
-                const int k = HS >= L::kNTB ? 0 : i % (L::kNTB / HS);
-                const int cg = b / L::kNTB;
-                dma16(rowp[k] + cg * L::kCG * 16, base + b * 1024);
-            }
+            constexpr int kKs = HS >= L::kNTB ? 1 : L::kNTB / HS;
+            static_assert(kKs == 1 ? HS % L::kNTB == 0 : HS * kKs == L::kNTB, "block geometry");
+            const int wave_off = kKs == 1 ? (w / L::kNTB) * L::kCG * 16 : 0;
+            const uint32_t lds0 = (uint32_t)(uintptr_t)(base + w * 1024);
+            [&]<int... I>(std::integer_sequence<int, I...>) {
+                ((L::kNB % HS == 0 || w + HS * I < L::kNB
+                      ? dma16_imm<(kKs == 1 ? (HS / L::kNTB) * I : I / kKs) * L::kCG * 16, 1024 * HS * I>(
+                            rowp[I % kKs] + wave_off, lds0)
+                      : (void)0),
+                 ...);
+            }(std::make_integer_sequence<int, kLoadsMax>{});
         };
 
         // ---- accumulators ----

@@ -31,6 +31,26 @@ void check_dma() {
     CHECK((int)seen.size() == L::kTile * L::kCPT, "dma coverage kv8=%d", KV8);
 }
 
+// The kernels issue load i of wave w (block b = w + HS i) as a per-row base
+// plus a compile-time byte offset: with one token row per wave (HS a multiple
+// of kNTB) the chunk group is w / kNTB + (HS / kNTB) i; with kKs = kNTB / HS
+// rows, row k = i % kKs is token block w + HS k and the chunk group is i / kKs.
+template <bool KV8>
+void check_dma_immediates(int HS) {
+    using L = TileLayout<KV8>;
+    const int kKs = HS >= L::kNTB ? 1 : L::kNTB / HS;
+    for (int w = 0; w < HS; ++w)
+        for (int i = 0; w + HS * i < L::kNB; ++i) {
+            const int b = w + HS * i;
+            const int tb_expect = kKs == 1 ? w % L::kNTB : w + HS * (i % kKs);
+            const int cg_expect = kKs == 1 ? w / L::kNTB + (HS / L::kNTB) * i : i / kKs;
+            CHECK(b % L::kNTB == tb_expect, "dma imm token block kv8=%d HS=%d w=%d i=%d", KV8, HS, w, i);
+            CHECK(b / L::kNTB == cg_expect, "dma imm chunk group kv8=%d HS=%d w=%d i=%d", KV8, HS, w, i);
+            const int off = (kKs == 1 ? (HS / L::kNTB) * i : i / kKs) * L::kCG * 16;
+            CHECK(off >= 0 && off < 4096, "dma imm offset range");
+        }
+}
+
 template <int HW, bool KV8>
 void check_score() {
     using S = ScoreAddr<HW, KV8>;
@@ -202,6 +222,10 @@ void check_pbuf() {
 int main() {
     check_dma<false>();
     check_dma<true>();
+    for (int HS : {2, 4}) {
+        check_dma_immediates<false>(HS);
+        check_dma_immediates<true>(HS);
+    }
     check_score<32, false>();
     check_score<32, true>();
     check_score<16, false>();
