@@ -141,21 +141,31 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
             if (MODE == kModeTree && tok >= lb) src = sfx_row + (tok - lb);
             dma4(src, (LDS_AS int*)&idx_ring[slot][w][0]);
         };
-        auto issue_tile = [&](int tile, int slot) {
+        // A tile's loads: the address of this lane's 16 bytes in load 0 and
+        // this wave's LDS base, then the loads themselves (issue_load<i>).
+        // Load i of this wave is block b = w + HS i, chunk group
+        // b / kNTB = w / kNTB + (HS / kNTB) i: a per-wave base plus 128 i bytes
+        // in the row (both layouts), and 1 KiB block b in LDS.
+        static_assert(HS % L::kNTB == 0 && (HS / L::kNTB) * L::kCG * 16 == 128, "immediate step");
+        struct TileAddr {
+            const uint8_t* rowp;
+            uint32_t lds0;
+        };
+        auto tile_addr = [&](int tile, int slot) {
             const int tau = min(kv_begin + tile * kTile + L::block_token(tb, lane), kv_end - 1);
             const int page = idx_ring[slot][w][lane / L::kCG];
             const int row = a.page_shift >= 0 ? (tau & (ps - 1)) : tau % ps;
-            // Load i of this wave is block b = w + HS i, chunk group
-            // b / kNTB = w / kNTB + (HS / kNTB) i: a per-wave base plus 128 i
-            // bytes in the row (both layouts), and 1 KiB block b in LDS.
-            static_assert(HS % L::kNTB == 0 && (HS / L::kNTB) * L::kCG * 16 == 128, "immediate step");
-            const uint8_t* rowp = a.cache + ((int64_t)page * ps + row) * L::kRowBytes + dma_lane_off +
-                                  (w / L::kNTB) * L::kCG * 16;
-            const uint32_t lds0 = (uint32_t)(uintptr_t)((LDS_AS char*)smem + slot * L::kTileBytes + w * 1024);
+            return TileAddr{a.cache + ((int64_t)page * ps + row) * L::kRowBytes + dma_lane_off + (w / L::kNTB) * L::kCG * 16,
+                            (uint32_t)(uintptr_t)((LDS_AS char*)smem + slot * L::kTileBytes + w * 1024)};
+        };
+        auto issue_load = [&](auto ic, const TileAddr& t) {
+            constexpr int i = decltype(ic)::value;
+            if (L::kNB % HS == 0 || w + HS * i < L::kNB) dma16_imm<128 * i, 1024 * HS * i>(t.rowp, t.lds0);
+        };
+        auto issue_tile = [&](int tile, int slot) {
+            const TileAddr t = tile_addr(tile, slot);
             [&]<int... I>(std::integer_sequence<int, I...>) {
-                ((L::kNB % HS == 0 || w + HS * I < L::kNB ? dma16_imm<128 * I, 1024 * HS * I>(rowp, lds0)
-                                                          : (void)0),
-                 ...);
+                (issue_load(std::integral_constant<int, I>{}, t), ...);
             }(std::make_integer_sequence<int, kLoadsMax>{});
         };
         auto wrap = [](int x) { return x >= kStages ? x - kStages : x; };
@@ -285,7 +295,20 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                     else
                         lds_barrier();
                     if (j + kIdxAhead < ntiles) issue_idx(j + kIdxAhead, wrap(cur + kIdxAhead % kStages));
-                    if (j + kAhead < ntiles) issue_tile(j + kAhead, wrap(cur + kAhead));
+                    // The data of tile j + kAhead. Issuing a tile's loads stalls each
+                    // wave about 550 cycles (per-phase timestamps, V3). With an fp8
+                    // cache they go out spread between this iteration's MFMAs below
+                    // (skewed fp8: 74 -> 70 us per call); with bf16 the spread was
+                    // slower (V3: 134.5 -> 137 us) and they go out here, together.
+                    constexpr bool kSpreadLoads = KV8;
+                    const bool do_dma = j + kAhead < ntiles;
+                    TileAddr dma{};
+                    if (do_dma) {
+                        if constexpr (kSpreadLoads)
+                            dma = tile_addr(j + kAhead, wrap(cur + kAhead));
+                        else
+                            issue_tile(j + kAhead, wrap(cur + kAhead));
+                    }
 
                     const LDS_AS char* Ts = (const LDS_AS char*)smem + cur * L::kTileBytes;
                     const LDS_AS char* Tp = (const LDS_AS char*)smem + prv * L::kTileBytes;
@@ -397,13 +420,24 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                     };
 
                     int si = 0, pi = 0;
-#pragma unroll
-                    for (int g = 0; g < kSM + kMix; ++g) {
-                        // Bresenham spread: slot g is a score MFMA when it advances the
-                        // score's share of the slots.
-                        if ((g + 1) * kSM / (kSM + kMix) != g * kSM / (kSM + kMix)) score_mfma(si++);
-                        else product_mfma(pi++);
-                    }
+                    // Slot g: a score MFMA when it advances the score's share of the
+                    // slots (Bresenham spread), else a product MFMA; after every
+                    // kDmaEvery-th slot one of the next tile's loads.
+                    constexpr int kSlots = kSM + kMix;
+                    constexpr int kDmaEvery = kSlots / kLoadsMax;
+                    auto mix_slot = [&](auto gc) {
+                        constexpr int g = decltype(gc)::value;
+                        if constexpr ((g + 1) * kSM / kSlots != g * kSM / kSlots)
+                            score_mfma(si++);
+                        else
+                            product_mfma(pi++);
+                        if constexpr (kSpreadLoads && g % kDmaEvery == kDmaEvery / 2 && g / kDmaEvery < kLoadsMax) {
+                            if (do_dma) issue_load(std::integral_constant<int, g / kDmaEvery>{}, dma);
+                        }
+                    };
+                    [&]<int... G>(std::integer_sequence<int, G...>) {
+                        (mix_slot(std::integral_constant<int, G>{}), ...);
+                    }(std::make_integer_sequence<int, kSlots>{});
                     settle_v(S);
 
                     // ---- softmax of tile j, in eight pieces between the last products ----
