@@ -99,6 +99,11 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Persistent worker: the plan's items [workers[w], workers[w+1]) in order.
     const int item_end = a.workers[blockIdx.x + 1];
+    // The bf16 query, held across items: the last iteration of an item (which
+    // only finishes the P . latent product) loads the next item's query, so that
+    // its transfer overlaps that product and the output stage (q_ready).
+    bf16x8 q[QF8 ? 1 : kSteps];
+    bool q_ready = false;
     for (int item = a.workers[blockIdx.x]; item < item_end; ++item) {
         // The thread index passes through an empty asm so that every per-lane
         // address is computed anew for each item: hoisted out of the item loop
@@ -126,6 +131,16 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + kTile - 1) / kTile : 0;
         const int hq = lane & 31, gq = lane >> 5;
         const int head = it.head_begin + 32 * w + hq;  // this lane's head in the score phase
+        // The bf16 query of this lane's head in query row `row`: 36 k-slices of 8 features.
+        auto load_query = [&](int row) {
+            const uint16_t* qn = a.q_nope + (int64_t)row * a.qn_sn + (int64_t)head * a.qn_sh;
+            const uint16_t* qr = a.q_rope + (int64_t)row * a.qr_sn + (int64_t)head * a.qr_sh;
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                const int f = L::q_feature(u, gq);
+                q[u] = u < 32 ? load_bf16x8(qn + f) : load_bf16x8(qr + (f - kLatent));
+            }
+        };
 
         // ---- tile loads ----
         // Wave w loads token block tb of every tile (kLoads 1 KiB blocks). Its
@@ -205,7 +220,6 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         // exponent (19 loads).
         constexpr int kQLoads = kSteps;  // the bf16 query's vector loads
         prologue_idx();
-        bf16x8 q[QF8 ? 1 : kSteps];
         u32x8 q8[QF8 ? 9 : 1];
         int q8e = 0;
         if constexpr (QF8) {
@@ -218,24 +232,19 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                 q8[v] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
             q8e = a.q8_exp[qrow];
-        } else {
-            const uint16_t* qn = a.q_nope + (int64_t)it.row * a.qn_sn + (int64_t)head * a.qn_sh;
-            const uint16_t* qr = a.q_rope + (int64_t)it.row * a.qr_sn + (int64_t)head * a.qr_sh;
-#pragma unroll
-            for (int u = 0; u < kSteps; ++u) {
-                const int f = L::q_feature(u, gq);
-                q[u] = u < 32 ? load_bf16x8(qn + f) : load_bf16x8(qr + (f - kLatent));
-            }
+        } else if (!q_ready) {
+            load_query(it.row);
         }
         // The page indices: the bf16 query is 36 vector loads issued after them,
         // which the wait leaves in flight (tests/test_isa_waits.py checks the
         // compiled kernels for at least kQLoads loads between the last index load
         // and this wait). The fp8-score instantiation waits for everything: its
         // query loads share the stretch with spill traffic the compiler places.
-        if constexpr (QF8)
-            wait_vmcnt<0>();
+        if (QF8 || q_ready)
+            wait_vmcnt<0>();  // (a prefetched query went out long before the indices)
         else
             wait_vmcnt_query<kQLoads>();
+        q_ready = false;
         if (MODE == kModeAppend && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
             // Fused append: the request's new row goes to the cache before any
             // wave loads a tile that holds it.
@@ -281,27 +290,43 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                     wait_vmcnt_barrier<0>();
                     start_tiles();
                 }
-                // Iterations j = 0 .. ntiles run one body: the score of tile j (slot
-                // cur) and the P . latent product of tile j-1 (slot prv). At j = 0
-                // the product reads a zeroed slot and a zeroed probability buffer and
-                // adds exact zeros; at j = ntiles every score is masked (no valid
-                // token) and the probabilities it writes are never read.
-                auto iteration = [&](int j, int cur) {
+                // Iterations j = 0 .. ntiles - 1 run one body: the score of tile j
+                // (slot cur) and the P . latent product of tile j-1 (slot prv). At
+                // j = 0 the product reads a zeroed slot and a zeroed probability
+                // buffer and adds exact zeros. The last iteration (kLast, j = ntiles)
+                // only finishes the product of tile ntiles - 1. With an fp8 cache and
+                // in the tree-verify pass it loads the next item's query meanwhile,
+                // unless this item reruns (every wave's rerun flag is written at the
+                // end of iteration ntiles - 1): skewed fp8 69.0 -> 66.7 us, tree
+                // verify 534 -> 529 us per call. The bf16 decode measured 1-2% slower
+                // with it (V3) and loads each query at its item's start.
+                constexpr bool kPrefetchQ = !QF8 && (KV8 || MODE == kModeTree);
+                auto iteration = [&](auto last_c, int j, int cur) {
+                    constexpr bool kLast = decltype(last_c)::value;
                     const int prv = cur == 0 ? kStages - 1 : cur - 1;
                     // Tile j has landed; every wave is past iteration j-1, so P(j-1)
                     // is visible and the slot of tile j-2 is free.
-                    if (j < ntiles)
+                    if constexpr (!kLast)
                         wait_tiles_barrier<kStages - 3, kLoadsMin>(min(kStages - 3, ntiles - 1 - j));
                     else
                         lds_barrier();
-                    if (j + kIdxAhead < ntiles) issue_idx(j + kIdxAhead, wrap(cur + kIdxAhead % kStages));
+                    if constexpr (kLast && kPrefetchQ) {
+                        int any = 0;
+#pragma unroll
+                        for (int k = 0; k < HS; ++k) any |= rerun_flag[k];
+                        if (!any && item + 1 < item_end) {
+                            load_query(a.items[item + 1].row);
+                            q_ready = true;
+                        }
+                    }
+                    if (!kLast && j + kIdxAhead < ntiles) issue_idx(j + kIdxAhead, wrap(cur + kIdxAhead % kStages));
                     // The data of tile j + kAhead. Issuing a tile's loads stalls each
                     // wave about 550 cycles (per-phase timestamps, V3). With an fp8
                     // cache they go out spread between this iteration's MFMAs below
                     // (skewed fp8: 74 -> 70 us per call); with bf16 the spread was
                     // slower (V3: 134.5 -> 137 us) and they go out here, together.
                     constexpr bool kSpreadLoads = KV8;
-                    const bool do_dma = j + kAhead < ntiles;
+                    const bool do_dma = !kLast && j + kAhead < ntiles;
                     TileAddr dma{};
                     if (do_dma) {
                         if constexpr (kSpreadLoads)
@@ -370,7 +395,8 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                         const u32x4 lo = sload(2 * v), hi = sload(2 * v + 1);
                         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                     };
-                    if constexpr (QF8) {
+                    if constexpr (kLast) {
+                    } else if constexpr (QF8) {
 #pragma unroll
                         for (int i = 0; i < kPipe8; ++i) sb8[i] = sload8(i);
                     } else {
@@ -420,6 +446,11 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                     };
 
                     int si = 0, pi = 0;
+                    if constexpr (kLast) {
+#pragma unroll
+                        for (int t = 0; t < kPM; ++t) product_mfma(pi++);
+                        return;
+                    }
                     // Slot g: a score MFMA when it advances the score's share of the
                     // slots (Bresenham spread), else a product MFMA; after every
                     // kDmaEvery-th slot one of the next tile's loads.
@@ -501,6 +532,13 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     l_part += ls0 + ls1;
+                    if constexpr (kPrefetchQ) {
+                        // The last tile's softmax is done: does any head need the rerun?
+                        if (j == ntiles - 1) {
+                            const bool over = __builtin_amdgcn_ballot_w64(m_true > m_ref + kOverflowSlack) != 0;
+                            if (lane == 0) rerun_flag[w] = over ? 1 : 0;
+                        }
+                    }
 
                     // Every wave is done reading P(j-1): the buffer takes P(j).
                     lds_barrier();
@@ -511,10 +549,11 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                     }
                 };
                 int cur = 0;
-                for (int j = 0; j <= ntiles; ++j) {
-                    iteration(j, cur);
+                for (int j = 0; j < ntiles; ++j) {
+                    iteration(std::false_type{}, j, cur);
                     cur = wrap(cur + 1);
                 }
+                iteration(std::true_type{}, ntiles, cur);
                 settle_o(O);
             }
             // Did any head outgrow its reference? All waves must agree (the tiles are
