@@ -117,6 +117,8 @@ def warm_until_steady(torch, stream, step, min_steps, min_s=1.5, max_s=5.0, batc
         step(done)
         done += 1
     torch.cuda.synchronize()
+    if min_s <= 0:
+        return time.perf_counter() - t0, done
     prev = None
     while True:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -217,6 +219,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warmup-seconds", type=float, default=1.5,
+                    help="after --warmup steps, keep warming until this many seconds have passed and "
+                         "two 25-step batches agree within 1%% (0: --warmup steps only, e.g. under a "
+                         "profiler)")
     ap.add_argument("--workload", default="v3",
                     choices=["v3", "v2_lite", "skewed_fp8", "projections", "tree_verify"])
     ap.add_argument("--append", action="store_true",
@@ -306,7 +312,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    warm_s, warm_steps = warm_until_steady(torch, stream, step, args.warmup)
+    warm_s, warm_steps = warm_until_steady(torch, stream, step, args.warmup, min_s=args.warmup_seconds)
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -466,7 +472,7 @@ def bench_projections(args):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    warm_s, warm_steps = warm_until_steady(torch, stream, step, args.warmup)
+    warm_s, warm_steps = warm_until_steady(torch, stream, step, args.warmup, min_s=args.warmup_seconds)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
@@ -647,7 +653,7 @@ def bench_tree_verify(args):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    warm_s, warm_steps = warm_until_steady(torch, stream, step, args.warmup)
+    warm_s, warm_steps = warm_until_steady(torch, stream, step, args.warmup, min_s=args.warmup_seconds)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
