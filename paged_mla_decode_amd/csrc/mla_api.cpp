@@ -218,6 +218,16 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
         if (params->page_size == (1 << b)) a.page_shift = b;
     a.scale_log2 = (float)((double)sm_scale * (double)kv_scale * 1.4426950408889634);
     a.out_scale = kv_scale;
+    // Tiles read once per launch (one query row per request) stream past the
+    // caches, which then keep the queries the pieces of a row share and the
+    // partials the merge reads back (A/B on one box: V3 133.1-133.6 -> 130.0-
+    // 130.5 us, V2-Lite 41.4 -> 37.9 us per call). Rows that share a request's
+    // tiles (qo_indptr, tree verify) keep the default policy, under which L2
+    // serves the repeats (the hint cost the tree-verify pass 531 -> 544 us),
+    // and so do fp8 tiles (rows of 576 bytes straddle cache lines; skewed fp8
+    // 67.3 -> 70.2 us with it). A graph-safe launch keeps the choice of the
+    // plan it was captured with.
+    a.stream_tiles = params->kv_dtype == MLA_DTYPE_BF16 && h->num_rows == h->batch && !tree;
     if (app) {
         a.c_new = static_cast<const uint16_t*>(app->c_new);
         a.c_new_sn = app->c_new_stride;

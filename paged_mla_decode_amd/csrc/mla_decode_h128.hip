@@ -68,9 +68,13 @@ __device__ __forceinline__ void settle_o(f32x16 (&O)[4][4]) {
 // comes as e4m3fn codes and a per-head exponent (quantize_query_kernel); the
 // score runs on the 32x32x64 fp8 MFMA, whose operands are the tile's fp8 bytes
 // as read, with no widening.
-template <bool KV8, bool OUT32, int MODE, bool QF8 = false>
+// NT: the tile loads carry the non-temporal hint (DecodeArgs::stream_tiles; a
+// parameter of its own, since a branch between the two forms in the loop cost
+// most of what the hint gains).
+template <bool KV8, bool OUT32, int MODE, bool QF8 = false, bool NT = false>
 __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
     static_assert(!QF8 || (KV8 && !OUT32 && MODE == kModePlain), "fp8 score: fp8 cache, bf16 output, plain decode");
+    static_assert(!NT || !KV8, "the hint is for bf16 tiles");
     constexpr int HS = 4;
     using L = H128Layout<KV8>;
     constexpr int kLoadsMax = (L::kNB + HS - 1) / HS;
@@ -173,14 +177,15 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
             return TileAddr{a.cache + ((int64_t)page * ps + row) * L::kRowBytes + dma_lane_off + (w / L::kNTB) * L::kCG * 16,
                             (uint32_t)(uintptr_t)((LDS_AS char*)smem + slot * L::kTileBytes + w * 1024)};
         };
-        auto issue_load = [&](auto ic, const TileAddr& t) {
+        auto issue_load = [&](auto ic, const TileAddr& t, auto nt_c) {
             constexpr int i = decltype(ic)::value;
-            if (L::kNB % HS == 0 || w + HS * i < L::kNB) dma16_imm<128 * i, 1024 * HS * i>(t.rowp, t.lds0);
+            if (L::kNB % HS == 0 || w + HS * i < L::kNB)
+                dma16_imm<128 * i, 1024 * HS * i, decltype(nt_c)::value>(t.rowp, t.lds0);
         };
         auto issue_tile = [&](int tile, int slot) {
             const TileAddr t = tile_addr(tile, slot);
             [&]<int... I>(std::integer_sequence<int, I...>) {
-                (issue_load(std::integral_constant<int, I>{}, t), ...);
+                (issue_load(std::integral_constant<int, I>{}, t, std::bool_constant<NT>{}), ...);
             }(std::make_integer_sequence<int, kLoadsMax>{});
         };
         auto wrap = [](int x) { return x >= kStages ? x - kStages : x; };
@@ -463,7 +468,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                         else
                             product_mfma(pi++);
                         if constexpr (kSpreadLoads && g % kDmaEvery == kDmaEvery / 2 && g / kDmaEvery < kLoadsMax) {
-                            if (do_dma) issue_load(std::integral_constant<int, g / kDmaEvery>{}, dma);
+                            if (do_dma) issue_load(std::integral_constant<int, g / kDmaEvery>{}, dma, std::false_type{});
                         }
                     };
                     [&]<int... G>(std::integer_sequence<int, G...>) {
@@ -697,14 +702,24 @@ int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num
     }
     auto go = [&](auto kv8_t, auto o32_t) {
         constexpr bool K = decltype(kv8_t)::value, O = decltype(o32_t)::value;
-        if (mode == kModeAppend)
-            decode_h128_kernel<K, O, kModeAppend><<<grid, block, 0, s>>>(a);
-        else if (mode == kModeTree)
+        // The streaming hint exists for the bf16 plain and append decodes (one
+        // query row per request); other modes share tiles among rows or do not
+        // stream (the suffix merge reads a few slots per row).
+        const bool nt = !K && a.stream_tiles;
+        if (mode == kModeAppend) {
+            if (nt)
+                decode_h128_kernel<false, O, kModeAppend, false, true><<<grid, block, 0, s>>>(a);
+            else
+                decode_h128_kernel<K, O, kModeAppend><<<grid, block, 0, s>>>(a);
+        } else if (mode == kModeTree) {
             decode_h128_kernel<K, O, kModeTree><<<grid, block, 0, s>>>(a);
-        else if (mode == kModeMerge)
+        } else if (mode == kModeMerge) {
             decode_h128_kernel<K, O, kModeMerge><<<grid, block, 0, s>>>(a);
-        else
+        } else if (nt) {
+            decode_h128_kernel<false, O, kModePlain, false, true><<<grid, block, 0, s>>>(a);
+        } else {
             decode_h128_kernel<K, O, kModePlain><<<grid, block, 0, s>>>(a);
+        }
     };
     using T = std::true_type;
     using F = std::false_type;

@@ -88,13 +88,22 @@ __device__ __forceinline__ void lds_barrier() {
 // M0: one SALU write of M0 and no address arithmetic per load. The immediate offset moves the LDS
 // destination too (lane l's 16 bytes land at M0 + offset + 16 l), so M0 gets
 // kLdsAdd - kOff. A wave's blocks of one tile differ by such constants.
-template <int kOff, int kLdsAdd>
+// kNT sets the non-temporal cache policy: for data read once per launch, so
+// that it does not push out of the caches what is read again (queries shared
+// by a row's pieces, partials the merge reads back).
+template <int kOff, int kLdsAdd, bool kNT = false>
 __device__ __forceinline__ void dma16_imm(const void* src, uint32_t lds_base) {
     static_assert(kOff >= 0 && kOff < 4096, "13-bit signed immediate offset");
-    asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%3"
-                 :
-                 : "s"(lds_base), "v"(src), "n"(kLdsAdd - kOff), "n"(kOff)
-                 : "memory", "m0");
+    if constexpr (kNT)
+        asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%3 nt"
+                     :
+                     : "s"(lds_base), "v"(src), "n"(kLdsAdd - kOff), "n"(kOff)
+                     : "memory", "m0");
+    else
+        asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%3"
+                     :
+                     : "s"(lds_base), "v"(src), "n"(kLdsAdd - kOff), "n"(kOff)
+                     : "memory", "m0");
 }
 
 // 4-byte direct global->LDS load: lane l's dword lands at lds + 4 l. Same

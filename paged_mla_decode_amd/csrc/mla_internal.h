@@ -60,6 +60,9 @@ struct DecodeArgs {
     int32_t page_shift;  // log2(page_size) when it is a power of two, else -1
     float scale_log2;    // sm_scale * kv_scale * log2(e)
     float out_scale;   // kv_scale (fp8 cache) or 1
+    // 1: the bf16 tile loads carry the non-temporal hint (every request has one
+    // query row, so each tile is read once per launch).
+    int32_t stream_tiles;
     // Fused append (null c_new: none). The item flagged MLA_ITEM_LAST_CHUNK writes
     // its request's row L-1 from c_new/k_pe_new (bf16, row it.row) into cache_w
     // (the same memory as cache) before any of its tile loads.

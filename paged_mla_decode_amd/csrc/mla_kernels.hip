@@ -184,13 +184,19 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
             static_assert(kKs == 1 ? HS % L::kNTB == 0 : HS * kKs == L::kNTB, "block geometry");
             const int wave_off = kKs == 1 ? (w / L::kNTB) * L::kCG * 16 : 0;
             const uint32_t lds0 = (uint32_t)(uintptr_t)(base + w * 1024);
-            [&]<int... I>(std::integer_sequence<int, I...>) {
-                ((L::kNB % HS == 0 || w + HS * I < L::kNB
-                      ? dma16_imm<(kKs == 1 ? (HS / L::kNTB) * I : I / kKs) * L::kCG * 16, 1024 * HS * I>(
-                            rowp[I % kKs] + wave_off, lds0)
-                      : (void)0),
-                 ...);
-            }(std::make_integer_sequence<int, kLoadsMax>{});
+            auto all = [&](auto nt_c) {
+                [&]<int... I>(std::integer_sequence<int, I...>) {
+                    ((L::kNB % HS == 0 || w + HS * I < L::kNB
+                          ? dma16_imm<(kKs == 1 ? (HS / L::kNTB) * I : I / kKs) * L::kCG * 16, 1024 * HS * I,
+                                      decltype(nt_c)::value>(rowp[I % kKs] + wave_off, lds0)
+                          : (void)0),
+                     ...);
+                }(std::make_integer_sequence<int, kLoadsMax>{});
+            };
+            if (!KV8 && a.stream_tiles)
+                all(std::true_type{});
+            else
+                all(std::false_type{});
         };
 
         // ---- accumulators ----
