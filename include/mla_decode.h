@@ -110,6 +110,21 @@ typedef struct {
  */
 #define MLA_DECODE_FP8_SCORE 2
 
+/*
+ * Shared rows (16 or 32 heads): the query rows of one request (qo_indptr) are
+ * planned together, up to 64 / num_heads rows per work item, so that each
+ * latent tile the item loads serves all of them: the mixed (q_len > 1)
+ * launch the sglang-jax MLA gap page keeps beside the q_len = 1 decode
+ * (section 2.4), for MTP and speculative decoding, where a request's draft
+ * rows read the same tokens (the PR 49477 analysis, introduction: the prefix
+ * that every draft of a request shares). Each row still attends to all of its
+ * request's tokens, as without the flag, and the results are the same up to
+ * rounding order. The item runs the 64-head kernel with one row's heads per
+ * wave (16 heads) or per two waves (32 heads). With 64 or 128 heads one row
+ * already fills a work item's accumulators and the flag changes nothing.
+ */
+#define MLA_DECODE_SHARED_ROWS 4
+
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(int32_t status);
 
@@ -118,7 +133,7 @@ const char* mla_status_string(int32_t status);
  * of the device workspace. It is plain data: tests may read it.
  */
 #define MLA_PLAN_MAGIC 0x504C4D41u /* "AMLP" */
-#define MLA_PLAN_VERSION 6
+#define MLA_PLAN_VERSION 7
 
 typedef struct {
     uint32_t magic;
@@ -137,7 +152,8 @@ typedef struct {
     int32_t num_wide_merges; /* the leading merges, those of at least 16 partials */
     int32_t flags;          /* the params' flags the plan was built with */
     int32_t suffix_tokens;  /* the params' suffix_tokens: each row is planned that much longer */
-    int32_t reserved;
+    int32_t tiles_read_once; /* 1: no two items read the same tokens of a request (every
+                                request's rows are one item, or one planned unit) */
     int64_t num_page_entries; /* kv_indptr[batch]: entries of kv_indices the batch uses */
     int64_t items_offset;   /* byte offset of mla_work_item[num_items] */
     int64_t merges_offset;  /* byte offset of mla_merge_item[num_merges] */
@@ -154,14 +170,18 @@ typedef struct {
 } mla_plan_header;
 
 typedef struct {
-    int32_t row;       /* query row n */
+    int32_t row;       /* query row n (the first of num_rows consecutive rows) */
     int32_t request;   /* request b */
     int32_t page_base; /* kv_indptr[b]: first entry of b's page list in kv_indices */
     int32_t kv_begin;  /* first token of the chunk */
     int32_t kv_end;    /* one past the last token (the request's length for the last chunk) */
-    int32_t partial;   /* -1: write out/lse directly; else the partial slot */
+    int32_t partial;   /* -1: write out/lse directly; else the partial slot of row `row`
+                          (row + r uses slot partial + r) */
     int32_t head_begin;
     uint32_t flags;    /* MLA_ITEM_* bits */
+    int32_t num_rows;  /* query rows row .. row + num_rows - 1 of request b (1 unless
+                          MLA_DECODE_SHARED_ROWS) */
+    int32_t reserved;
 } mla_work_item;
 
 /* The item's chunk ends at its request's planned length (kv_end == L >= 1): the
@@ -169,10 +189,10 @@ typedef struct {
 #define MLA_ITEM_LAST_CHUNK 1u
 
 typedef struct {
-    int32_t row;           /* query row n */
-    int32_t partial_begin; /* its chunks are partial slots [partial_begin, +num_partials) */
-    int32_t num_partials;
-    int32_t reserved;
+    int32_t row;            /* query row n */
+    int32_t partial_begin;  /* its chunks are partial slots partial_begin + k * partial_stride, */
+    int32_t num_partials;   /*   k < num_partials, in token order */
+    int32_t partial_stride; /* 1, or the rows of its shared-rows items */
 } mla_merge_item;
 
 /*

@@ -14,7 +14,7 @@ fallback implementation.
 _BINDING = (
     "EXPORTED_SYMBOLS", "LIB_PATH", "MLA_DTYPE_BF16", "MLA_DTYPE_FP8_E4M3FN", "MLA_DTYPE_FP32",
     "MLA_ERR_HIP", "MLA_ERR_INVALID_ARG", "MLA_ERR_PLAN_MISMATCH", "MLA_ERR_UNSUPPORTED",
-    "MLA_ERR_WORKSPACE_TOO_SMALL", "MLA_ITEM_LAST_CHUNK", "MLA_DECODE_GRAPH_SAFE", "MLA_DECODE_FP8_SCORE", "MLA_OK",
+    "MLA_ERR_WORKSPACE_TOO_SMALL", "MLA_ITEM_LAST_CHUNK", "MLA_DECODE_GRAPH_SAFE", "MLA_DECODE_FP8_SCORE", "MLA_DECODE_SHARED_ROWS", "MLA_OK",
     "MLA_PLAN_VERSION", "MlaError",
     "make_params", "mla_absorb_query", "mla_decode", "mla_decode_append", "mla_decode_plan",
     "mla_decode_suffix_merge", "mla_decode_tree_verify", "mla_decode_variant",

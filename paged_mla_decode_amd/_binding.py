@@ -41,9 +41,10 @@ MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP32 = 1
 MLA_DTYPE_FP8_E4M3FN = 2
 MLA_PLAN_MAGIC = 0x504C4D41
-MLA_PLAN_VERSION = 6
+MLA_PLAN_VERSION = 7
 MLA_DECODE_GRAPH_SAFE = 1
 MLA_DECODE_FP8_SCORE = 2
+MLA_DECODE_SHARED_ROWS = 4
 MLA_ITEM_LAST_CHUNK = 1
 
 
@@ -65,7 +66,7 @@ class mla_plan_header(ctypes.Structure):
                 ("num_partials", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
                 ("num_workers", ctypes.c_int32), ("max_merge_partials", ctypes.c_int32),
                 ("num_wide_merges", ctypes.c_int32), ("flags", ctypes.c_int32),
-                ("suffix_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("suffix_tokens", ctypes.c_int32), ("tiles_read_once", ctypes.c_int32),
                 ("num_page_entries", ctypes.c_int64), ("items_offset", ctypes.c_int64),
                 ("merges_offset", ctypes.c_int64), ("workers_offset", ctypes.c_int64),
                 ("plan_bytes", ctypes.c_int64),
@@ -77,11 +78,11 @@ class mla_plan_header(ctypes.Structure):
 class mla_work_item(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("row", "request", "page_base", "kv_begin", "kv_end", "partial", "head_begin")] + \
-        [("flags", ctypes.c_uint32)]
+        [("flags", ctypes.c_uint32), ("num_rows", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class mla_merge_item(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("row", "partial_begin", "num_partials", "reserved")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("row", "partial_begin", "num_partials", "partial_stride")]
 
 
 _p = ctypes.c_void_p

@@ -218,7 +218,7 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
         if (params->page_size == (1 << b)) a.page_shift = b;
     a.scale_log2 = (float)((double)sm_scale * (double)kv_scale * 1.4426950408889634);
     a.out_scale = kv_scale;
-    // Tiles read once per launch (one query row per request) stream past the
+    // Tiles read once per launch (one planned unit of rows per request) stream past the
     // caches, which then keep the queries the pieces of a row share and the
     // partials the merge reads back (A/B on one box: V3 133.1-133.6 -> 130.0-
     // 130.5 us, V2-Lite 41.4 -> 37.9 us per call). Rows that share a request's
@@ -227,7 +227,7 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
     // and so do fp8 tiles (rows of 576 bytes straddle cache lines; skewed fp8
     // 67.3 -> 70.2 us with it). A graph-safe launch keeps the choice of the
     // plan it was captured with.
-    a.stream_tiles = params->kv_dtype == MLA_DTYPE_BF16 && h->num_rows == h->batch && !tree;
+    a.stream_tiles = params->kv_dtype == MLA_DTYPE_BF16 && h->tiles_read_once && !tree;
     if (app) {
         a.c_new = static_cast<const uint16_t*>(app->c_new);
         a.c_new_sn = app->c_new_stride;
@@ -289,9 +289,10 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
             const mla_plan_header* hd = reinterpret_cast<const mla_plan_header*>(ws);
             m.dev_num_merges = &hd->num_merges;
             m.dev_num_wide = &hd->num_wide_merges;
+            // With shared rows each split unit holds up to rows_per_item rows.
             const int g = h->num_workers;
-            num_merges = std::max(1, g - 1);
-            num_wide = std::max(1, (g - 1 + kWideMergePartials - 2) / (kWideMergePartials - 1));
+            num_merges = std::max(1, g - 1) * v.rows_per_item;
+            num_wide = std::max(1, (g - 1 + kWideMergePartials - 2) / (kWideMergePartials - 1)) * v.rows_per_item;
         }
         err = launch_merge_partials(params->out_dtype, m, num_merges, num_wide, stream);
         if (err != 0) return MLA_ERR_HIP;

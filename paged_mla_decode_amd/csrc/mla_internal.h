@@ -21,6 +21,7 @@ struct Variant {
     int hs;
     int wgs_per_cu;
     int item_cost;  // fixed cost of one work item, in 32-token tiles (measured)
+    int rows_per_item = 1;  // MLA_DECODE_SHARED_ROWS: query rows of a request per item
 };
 
 // Selects the kernel instantiation for these parameters. Returns false when the

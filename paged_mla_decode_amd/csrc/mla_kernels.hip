@@ -109,18 +109,23 @@ __global__ __launch_bounds__(64 * HS) void decode_kernel(const DecodeArgs a) {
         // Lane roles. hq: head (MFMA N index); gq: lane group along the K dim.
         const int hq = HW == 32 ? (lane & 31) : (lane & 15);
         const int gq = HW == 32 ? (lane >> 5) : (lane >> 4);
+        // This lane's head, counted over the item's rows: rows it.row + r hold heads
+        // r H .. r H + H - 1 (one row unless MLA_DECODE_SHARED_ROWS). Outputs,
+        // partials and lse of consecutive rows are consecutive [H] blocks, so
+        // it.row * H + head (it.partial * H + head) addresses them all.
         const int head = it.head_begin + w * HW + hq;
-        // A wave whose heads lie past num_heads only loads tiles: with 16 heads the
-        // second wave halves the first one's loads per tile, which lets the vmcnt
-        // budget cover twice the stages.
-        const bool active = w * HW < a.num_heads;
+        // A wave whose heads lie past the item's only loads tiles: with 16 heads
+        // the second wave halves the first one's loads per tile, which lets the
+        // vmcnt budget cover twice the stages.
+        const bool active = w * HW < it.num_rows * a.num_heads;
 
         // ---- absorbed query -> registers (B operand of the score MFMA) ----
         // Loaded with the first page-table entries (below), under one wait.
         bf16x8 q[kSteps];
         auto load_query = [&] {
-            const uint16_t* qn = a.q_nope + (int64_t)it.row * a.qn_sn + (int64_t)head * a.qn_sh;
-            const uint16_t* qr = a.q_rope + (int64_t)it.row * a.qr_sn + (int64_t)head * a.qr_sh;
+            const int qrow = it.row + head / a.num_heads, qhead = head % a.num_heads;
+            const uint16_t* qn = a.q_nope + (int64_t)qrow * a.qn_sn + (int64_t)qhead * a.qn_sh;
+            const uint16_t* qr = a.q_rope + (int64_t)qrow * a.qr_sn + (int64_t)qhead * a.qr_sh;
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
                 const int k0 = (HW == 32 ? 16 : 32) * s + 8 * gq;
@@ -522,7 +527,7 @@ __device__ __forceinline__ void merge_batch(const MergePartialsArgs& a, const ml
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
         if (k < nb) {
-            const int64_t slot = (int64_t)(mi.partial_begin + p0 + k) * nh + h;
+            const int64_t slot = (int64_t)(mi.partial_begin + (p0 + k) * mi.partial_stride) * nh + h;
             l[k] = a.part_lse[slot];
             v[k] = *(reinterpret_cast<const V*>(a.part_out) + slot * (kLatent / 8) + lane);
         }

@@ -41,7 +41,8 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 }  // namespace
 
 bool select_variant(const mla_decode_params* p, Variant* v) {
-    if (!p || (p->flags & ~(MLA_DECODE_GRAPH_SAFE | MLA_DECODE_FP8_SCORE)) != 0) return false;
+    if (!p || (p->flags & ~(MLA_DECODE_GRAPH_SAFE | MLA_DECODE_FP8_SCORE | MLA_DECODE_SHARED_ROWS)) != 0)
+        return false;
     // The fp8 score: the 128-head kernel over an e4m3fn cache, bf16 output, plain decode.
     if ((p->flags & MLA_DECODE_FP8_SCORE) &&
         (p->num_heads != 128 || p->kv_dtype != MLA_DTYPE_FP8_E4M3FN || p->out_dtype != MLA_DTYPE_BF16 ||
@@ -53,6 +54,11 @@ bool select_variant(const mla_decode_params* p, Variant* v) {
     if (p->kv_lora_rank != kLatent || p->qk_rope_head_dim != kRope || p->page_size < 1) return false;
     if (p->kv_dtype != MLA_DTYPE_BF16 && p->kv_dtype != MLA_DTYPE_FP8_E4M3FN) return false;
     if (p->out_dtype != MLA_DTYPE_BF16 && p->out_dtype != MLA_DTYPE_FP32) return false;
+    // Shared rows: 64 / H rows of 16 or 32 heads per item, on the 64-head kernel.
+    if ((p->flags & MLA_DECODE_SHARED_ROWS) && (p->num_heads == 16 || p->num_heads == 32)) {
+        *v = Variant{16, 4, 1, 4, 64 / p->num_heads};
+        return true;
+    }
     switch (p->num_heads) {
         // The 128-head kernel loads a 144 KiB query and stores a 128 KiB output
         // per item, about as long as 8 tiles of its main loop; the smaller
@@ -127,7 +133,8 @@ int32_t plan_bounds(const mla_decode_params* p, int32_t num_cus, int32_t batch, 
         num_rows = std::max(num_rows, p->max_rows);
     }
     const int64_t items = (int64_t)num_rows + G + 1;
-    const int64_t partials = std::min<int64_t>(items, 2 * G + 2);
+    // A split item writes one partial per query row it holds.
+    const int64_t partials = std::min<int64_t>(items, 2 * G + 2) * v.rows_per_item;
     mla_plan_header h{};
     layout((int32_t)items, num_rows, (int32_t)G, (int32_t)partials, p->num_heads, partial_elem_bytes(p),
            query_rows(p, num_rows), &h);
@@ -176,16 +183,21 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
     int64_t min_piece = item_cost;
     const int64_t sfx = p->suffix_tokens;
 
+    // The planned units: a query row, or with shared rows up to rows_per_item
+    // consecutive rows of one request (they read the same tokens).
     struct Row {
         int32_t row, request;
         int64_t len, tiles;
+        int32_t nrows;
     };
+    const int64_t R = v.rows_per_item;
     std::vector<Row> rows;
     rows.reserve((size_t)num_rows);
     for (int32_t b = 0; b < batch; ++b) {
         const int64_t r0 = qo_indptr ? qo_indptr[b] : b;
         const int64_t r1 = qo_indptr ? qo_indptr[b + 1] : b + 1;
-        for (int64_t r = r0; r < r1; ++r) rows.push_back(Row{(int32_t)r, b, len[b], (len[b] + kTile - 1) / kTile});
+        for (int64_t r = r0; r < r1; r += R)
+            rows.push_back(Row{(int32_t)r, b, len[b], (len[b] + kTile - 1) / kTile, (int32_t)std::min(R, r1 - r)});
     }
     std::stable_sort(rows.begin(), rows.end(), [](const Row& x, const Row& y) { return x.tiles > y.tiles; });
 
@@ -263,7 +275,9 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
     std::vector<Piece> pieces;
     if (!fill(hi, &pieces)) return MLA_ERR_UNSUPPORTED;  // unreachable: hi is feasible
 
-    // Partial slots: the pieces of a split row take consecutive slots.
+    // Partial slots: the pieces of a split unit take consecutive runs of slots,
+    // one slot per row (piece c of a unit of n rows: slots first + c n + r), so
+    // that row r's partials are first + r + k n, k < pieces.
     std::vector<int32_t> npieces(rows.size(), 0), first_slot(rows.size(), -1);
     for (const Piece& pc : pieces) ++npieces[pc.row_index];
     std::vector<mla_merge_item> merges;
@@ -271,8 +285,9 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
     for (size_t i = 0; i < rows.size(); ++i)
         if (npieces[i] > 1) {
             first_slot[i] = num_partials;
-            merges.push_back(mla_merge_item{rows[i].row, num_partials, npieces[i], 0});
-            num_partials += npieces[i];
+            for (int32_t r = 0; r < rows[i].nrows; ++r)
+                merges.push_back(mla_merge_item{rows[i].row + r, num_partials + r, npieces[i], rows[i].nrows});
+            num_partials += npieces[i] * rows[i].nrows;
         }
     // Rows with the most partials first: the launch merges the leading ones
     // (at least kWideMergePartials each) with the wide kernel.
@@ -291,8 +306,13 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
         it.page_base = kv_indptr[r.request];
         it.kv_begin = (int32_t)(pc.t0 * kTile);
         it.kv_end = (int32_t)std::min<int64_t>(r.len, pc.t1 * kTile);
-        it.partial = npieces[pc.row_index] > 1 ? next_slot[pc.row_index]++ : -1;
+        it.partial = -1;
+        if (npieces[pc.row_index] > 1) {
+            it.partial = next_slot[pc.row_index];
+            next_slot[pc.row_index] += r.nrows;
+        }
         it.head_begin = 0;
+        it.num_rows = r.nrows;
         it.flags = (r.len > 0 && it.kv_end == r.len) ? MLA_ITEM_LAST_CHUNK : 0u;
         per_worker[(size_t)pc.worker].push_back(it);
     }
@@ -340,14 +360,20 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
     }
     h.flags = p->flags;
     h.suffix_tokens = p->suffix_tokens;
+    // Tiles are read once per launch when no request has more rows than one
+    // planned unit holds (pieces of one unit read disjoint tokens).
+    h.tiles_read_once = 1;
+    for (int32_t b = 0; qo_indptr && b < batch; ++b)
+        if ((int64_t)qo_indptr[b + 1] - qo_indptr[b] > R) h.tiles_read_once = 0;
     h.num_page_entries = kv_indptr[batch];
     if (p->flags & MLA_DECODE_GRAPH_SAFE) {
         // The layout of plan_bounds for max_rows rows: the same offsets for every
         // plan of these params, so that captured launches find each array.
         if (p->max_rows < 1 || num_rows > p->max_rows) return MLA_ERR_INVALID_ARG;
         const int64_t cap_items = (int64_t)p->max_rows + G + 1;
-        layout((int32_t)cap_items, p->max_rows, (int32_t)G, (int32_t)std::min<int64_t>(cap_items, 2 * G + 2),
-               p->num_heads, partial_elem_bytes(p), query_rows(p, p->max_rows), &h);
+        layout((int32_t)cap_items, p->max_rows, (int32_t)G,
+               (int32_t)(std::min<int64_t>(cap_items, 2 * G + 2) * R), p->num_heads, partial_elem_bytes(p),
+               query_rows(p, p->max_rows), &h);
     } else {
         layout(h.num_items, h.num_merges, num_workers, num_partials, p->num_heads, partial_elem_bytes(p),
                query_rows(p, h.num_rows), &h);

@@ -19,12 +19,14 @@ class PagedMlaDecoder:
     def __init__(self, num_heads: int, page_size: int, max_batch: int, max_rows: int | None = None,
                  kv_dtype: str = "bf16", out_dtype: str = "bf16", num_cus: int = 0,
                  max_splits: int = 0, device="cuda", graph_safe: bool = False,
-                 suffix_tokens: int = 0, fp8_score: bool = False):
+                 suffix_tokens: int = 0, fp8_score: bool = False, shared_rows: bool = False):
         self.device = torch.device(device)
         max_rows = max_batch if max_rows is None else max_rows
         # Graph-safe: launches and workspace addresses fixed for up to max_rows rows.
         # fp8_score: the score on the fp8 matrix core with an e4m3fn-quantised query.
-        flags = (B.MLA_DECODE_GRAPH_SAFE if graph_safe else 0) | (B.MLA_DECODE_FP8_SCORE if fp8_score else 0)
+        # shared_rows: a request's query rows share each tile (16 and 32 heads).
+        flags = ((B.MLA_DECODE_GRAPH_SAFE if graph_safe else 0) | (B.MLA_DECODE_FP8_SCORE if fp8_score else 0)
+                 | (B.MLA_DECODE_SHARED_ROWS if shared_rows else 0))
         self.params = B.make_params(num_heads, page_size, _DTYPES[kv_dtype], _DTYPES[out_dtype],
                                     num_cus, max_splits,
                                     flags=flags,

@@ -40,14 +40,14 @@ def batch_to_device(batch, dev):
 
 
 def run_decode(batch, dev, out_dtype="bf16", max_splits=0, kv_lens=None, num_cus=0,
-               q_pair=None):
+               q_pair=None, shared_rows=False):
     from paged_mla_decode_amd.decoder import PagedMlaDecoder
     qn, qr, cache, idx = batch_to_device(batch, dev)
     if q_pair is not None:
         qn, qr = q_pair
     dec = PagedMlaDecoder(batch.num_heads, batch.page_size, max_batch=batch.batch,
                           max_rows=batch.num_rows, kv_dtype=batch.cache_dtype, out_dtype=out_dtype,
-                          num_cus=num_cus, max_splits=max_splits, device=dev)
+                          num_cus=num_cus, max_splits=max_splits, device=dev, shared_rows=shared_rows)
     rows_per_req = np.diff(batch.qo_indptr)
     qo = None if np.all(rows_per_req == 1) else batch.qo_indptr
     dec.plan(batch.kv_indptr, batch.kv_last_page_len, qo)

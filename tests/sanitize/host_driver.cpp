@@ -83,7 +83,7 @@ int plan_one(const Batch& b, mla_decode_params p, int32_t cus) {
 int run_batch(const Batch& b) {
     int bad = 0;
     for (int32_t cus : {256, 13, 1}) {
-        for (int variant = 0; variant < 6; ++variant) {
+        for (int variant = 0; variant < 8; ++variant) {
             mla_decode_params p{};
             p.num_heads = b.heads;
             p.kv_lora_rank = 512;
@@ -105,6 +105,14 @@ int run_batch(const Batch& b) {
                 if (b.heads != 128 || b.suffix) continue;
                 p.kv_dtype = MLA_DTYPE_FP8_E4M3FN;
                 p.flags = MLA_DECODE_FP8_SCORE | MLA_DECODE_GRAPH_SAFE;
+            }
+            if (variant == 6) {
+                if (b.suffix) continue;
+                p.flags = MLA_DECODE_SHARED_ROWS;
+            }
+            if (variant == 7) {
+                if (b.suffix) continue;
+                p.flags = MLA_DECODE_SHARED_ROWS | MLA_DECODE_GRAPH_SAFE;
             }
             const int st = plan_one(b, p, cus);
             if (st != MLA_OK) {

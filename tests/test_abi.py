@@ -265,7 +265,7 @@ def test_fp8_score_only_for_the_128_head_fp8_bf16_plain_decode():
     for bad in (dict(num_heads=16), dict(num_heads=64), dict(kv_dtype=m.MLA_DTYPE_BF16),
                 dict(out_dtype=m.MLA_DTYPE_FP32), dict(page_size=1, suffix_tokens=8)):
         assert m.mla_decode_variant(_qf8_params(**bad)) is None, bad
-    assert m.mla_decode_variant(_qf8_params(flags=4)) is None  # an unknown flag
+    assert m.mla_decode_variant(_qf8_params(flags=8)) is None  # an unknown flag
 
 
 @pytest.mark.parametrize("graph", [False, True])

@@ -27,6 +27,13 @@ def item_cost(num_heads):
     return 8 if num_heads == 128 else 4
 
 
+def rows_per_item(p):
+    """Query rows of one request a work item holds."""
+    if p.flags & m.MLA_DECODE_SHARED_ROWS and p.num_heads in (16, 32):
+        return 64 // p.num_heads
+    return 1
+
+
 def worker_loads(items, workers, cost):
     return [sum(-(-(it.kv_end - it.kv_begin) // TILE) + cost for it in items[workers[w]:workers[w + 1]])
             for w in range(len(workers) - 1)]
@@ -40,9 +47,15 @@ def check_invariants(p, batch, h, items, merges, workers):
     row_req = np.repeat(np.arange(batch.batch), np.diff(batch.qo_indptr))
     covered = {}
     partial_of = {}
+    R = rows_per_item(p)
+    per_req = np.diff(batch.qo_indptr)
+    assert h.tiles_read_once == int(per_req.max(initial=0) <= R)
     for it in items:
-        assert 0 <= it.row < batch.num_rows
-        assert it.request == row_req[it.row]
+        # an item holds rows it.row .. it.row + num_rows - 1 of one request
+        assert 1 <= it.num_rows <= R
+        rows = range(it.row, it.row + it.num_rows)
+        assert 0 <= it.row and it.row + it.num_rows <= batch.num_rows
+        assert all(row_req[r] == it.request for r in rows)
         assert it.page_base == batch.kv_indptr[it.request]
         assert 0 <= it.kv_begin <= it.kv_end <= lens[it.row]
         assert it.kv_begin % TILE == 0
@@ -50,10 +63,11 @@ def check_invariants(p, batch, h, items, merges, workers):
         # The last-chunk flag marks exactly the item that ends at a non-empty row's length.
         assert bool(it.flags & m.MLA_ITEM_LAST_CHUNK) == (lens[it.row] > 0 and it.kv_end == lens[it.row])
         assert it.flags & ~m.MLA_ITEM_LAST_CHUNK == 0
-        covered.setdefault(it.row, []).append((it.kv_begin, it.kv_end))
-        if it.partial >= 0:
-            assert it.partial not in partial_of
-            partial_of[it.partial] = it
+        for k, r in enumerate(rows):
+            covered.setdefault(r, []).append((it.kv_begin, it.kv_end))
+            if it.partial >= 0:  # row it.row + k writes slot it.partial + k
+                assert it.partial + k not in partial_of
+                partial_of[it.partial + k] = (it, r)
     # exact cover of every row's tokens
     for r in range(batch.num_rows):
         segs = sorted(covered[r])
@@ -65,10 +79,10 @@ def check_invariants(p, batch, h, items, merges, workers):
     merged_rows = set()
     for mi in merges:
         merged_rows.add(mi.row)
-        assert mi.num_partials >= 2
-        chunks = [partial_of[mi.partial_begin + k] for k in range(mi.num_partials)]
-        assert all(c.row == mi.row for c in chunks)
-        assert sorted((c.kv_begin, c.kv_end) for c in chunks) == sorted(covered[mi.row])
+        assert mi.num_partials >= 2 and mi.partial_stride >= 1
+        chunks = [partial_of[mi.partial_begin + k * mi.partial_stride] for k in range(mi.num_partials)]
+        assert all(r == mi.row for _, r in chunks)
+        assert [(c.kv_begin, c.kv_end) for c, _ in chunks] == sorted(covered[mi.row]), "token order"
     for r, segs in covered.items():
         assert (len(segs) > 1) == (r in merged_rows)
     assert h.num_merges == len(merges)
@@ -112,6 +126,43 @@ def test_plan_invariants(make, H, ps):
         check_invariants(p, batch, h, items, merges, workers)
         if splits == 1:
             assert h.num_merges == 0 and h.num_partials == 0
+
+
+@pytest.mark.parametrize("H", [16, 32, 64, 128])
+@pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, [0, 4, 1, 9, 2, 0, 3]])
+def test_shared_rows_plan_invariants(H, rows):
+    """MLA_DECODE_SHARED_ROWS: up to 64 / H consecutive rows of a request per
+    item (16 and 32 heads; one row otherwise), each row's pieces in its own
+    partial slots, a merge per split row over strided slots."""
+    lens = [0, 40, 300, 1, 2048, 64, 5000]
+    nb = len(lens)
+    batch = workloads.random_decode_batch(5, lens, H, 16, rows_per_request=rows)
+    for cus, splits in ((256, 0), (64, 0), (80, 3), (1, 0)):
+        p = m.make_params(H, 16, num_cus=cus, max_splits=splits, flags=m.MLA_DECODE_SHARED_ROWS)
+        h, items, merges, workers = build(p, batch)
+        check_invariants(p, batch, h, items, merges, workers)
+        R = rows_per_item(p)
+        per_req = np.diff(batch.qo_indptr)
+        # every request's rows form ceil(rows / R) units, each planned like one row
+        units = sum(-(-int(n) // R) for n in per_req)
+        firsts = {(it.request, it.row) for it in items}
+        assert len(firsts) == units, (len(firsts), units)
+    assert nb == batch.batch
+
+
+def test_shared_rows_graph_safe_layout_holds_every_plan():
+    """Graph-safe shared-rows plans keep one layout, with room for a partial per
+    row of every split unit."""
+    p = m.make_params(16, 1, num_cus=256, flags=m.MLA_DECODE_SHARED_ROWS | m.MLA_DECODE_GRAPH_SAFE, max_rows=64)
+    offs = set()
+    for rows in (1, 4, [4, 3, 2, 1] * 4):
+        batch = workloads.random_decode_batch(6, [3000] * 16, 16, 1, rows_per_request=rows)
+        h, items, merges, workers = build(p, batch)
+        check_invariants(p, batch, h, items, merges, workers)
+        assert h.num_partials * 16 * 512 * 2 <= h.partial_lse_offset - h.partial_out_offset
+        offs.add((h.items_offset, h.merges_offset, h.workers_offset, h.partial_out_offset,
+                  h.partial_lse_offset, h.workspace_bytes))
+    assert len(offs) == 1
 
 
 def test_skewed_batch_splits_the_long_request_across_the_chip():

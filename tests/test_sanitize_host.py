@@ -1,8 +1,8 @@
 """Host code under AddressSanitizer and UndefinedBehaviorSanitizer.
 
 The planner (every params variant: plain, graph-safe, never split, fp32
-output, the fp8 score, tree-verify suffix tokens; several compute-unit
-counts), the host index checks and the C oracle are compiled with g++/gcc and
+output, the fp8 score, shared rows, tree-verify suffix tokens; several
+compute-unit counts), the host index checks and the C oracle are compiled with g++/gcc and
 -fsanitize=address,undefined into one host program (tests/sanitize/
 host_driver.cpp), which plans the page layouts of every workload plus empty
 and degenerate batches. Any sanitizer report aborts the program and fails the
@@ -72,6 +72,11 @@ def test_planner_validation_and_oracle_are_clean(driver):
     add("zero_lengths", workloads.random_decode_batch(2, [0, 0, 0], num_heads=128, page_size=64))
     add("one_token", workloads.random_decode_batch(3, [1], num_heads=128, page_size=64))
     add("odd_pages", workloads.random_decode_batch(4, [0, 1, 47, 48, 49, 1000], num_heads=16, page_size=48))
+    # several query rows per request (shared-rows units of up to 4 rows at 16 heads, 2 at 32)
+    add("rows16", workloads.random_decode_batch(7, [0, 40, 3000, 9000, 1], num_heads=16, page_size=16,
+                                                rows_per_request=[3, 4, 9, 1, 2]))
+    add("rows32", workloads.random_decode_batch(8, [5000, 2, 700], num_heads=32, page_size=1,
+                                                rows_per_request=[5, 2, 0]))
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
     res = subprocess.run([str(exe), *cases], capture_output=True, text=True, env=env, timeout=600)

@@ -205,11 +205,14 @@ def make_decode_batch(name, seed, seq_lens_fn, num_heads, page_size, pool_pages_
     pool_pages = int(pool_pages_fn(int(npages.sum())))
     kv_indptr, kv_indices, last = layout_from_lengths(seq_lens, page_size, pool_pages, rng)
     B = len(seq_lens)
-    N = B * rows_per_request
+    # Query rows per request: one count for all, or one per request.
+    rpr = np.broadcast_to(np.asarray(rows_per_request, dtype=np.int64), (B,))
+    qo_indptr = np.concatenate([[0], np.cumsum(rpr)]).astype(np.int32)
+    N = int(qo_indptr[-1])
     if layout_only:
         return DecodeBatch(
             name=name, num_heads=num_heads, page_size=page_size,
-            qo_indptr=(np.arange(B + 1, dtype=np.int32) * rows_per_request),
+            qo_indptr=qo_indptr,
             kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last,
             seq_lens=seq_lens.astype(np.int32), q_nope=np.zeros((N, num_heads, 0), np.uint16),
             q_rope=np.zeros((N, num_heads, 0), np.uint16),
@@ -226,7 +229,7 @@ def make_decode_batch(name, seed, seq_lens_fn, num_heads, page_size, pool_pages_
         raise ValueError(cache_dtype)
     return DecodeBatch(
         name=name, num_heads=num_heads, page_size=page_size,
-        qo_indptr=(np.arange(B + 1, dtype=np.int32) * rows_per_request),
+        qo_indptr=qo_indptr,
         kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last,
         seq_lens=seq_lens.astype(np.int32), q_nope=q_nope, q_rope=q_rope, cache=cache,
         cache_dtype=cache_dtype, kv_scale=kv_scale, seed=seed)
@@ -243,13 +246,16 @@ def tiny(seed: int = 1, layout_only: bool = False) -> DecodeBatch:
         pool_pages_fn=lambda need: 64, layout_only=layout_only)
 
 
-def v2_lite(seed: int = 2, batch: int = 64, layout_only: bool = False) -> DecodeBatch:
+def v2_lite(seed: int = 2, batch: int = 64, layout_only: bool = False, rows_per_request: int = 1) -> DecodeBatch:
     """DeepSeek-V2-Lite-shaped decode: H=16, page size 1, L ~ U{512..4096},
-    slots scattered over a pool of 300,000."""
+    slots scattered over a pool of 300,000. rows_per_request > 1: that many
+    query rows per request over the same tokens (multi-token prediction or
+    speculative decoding), drawn after the layout and before the cache."""
+    name = "v2_lite" if rows_per_request == 1 else f"v2_lite_rows{rows_per_request}"
     return make_decode_batch(
-        "v2_lite", seed, lambda rng: rng.integers(512, 4096, size=batch, endpoint=True),
+        name, seed, lambda rng: rng.integers(512, 4096, size=batch, endpoint=True),
         num_heads=16, page_size=1, pool_pages_fn=lambda need: max(300_000, need),
-        layout_only=layout_only)
+        layout_only=layout_only, rows_per_request=rows_per_request)
 
 
 def lognormal_lengths(rng, batch, median=2048.0, sigma=0.8, lo=16, hi=16384):
@@ -347,8 +353,10 @@ def tree_verify(seed: int = 4, batch: int = 16, prefix_len: int = 2048, width: i
 
 def random_decode_batch(seed: int, seq_lens, num_heads: int, page_size: int,
                         pool_pages: Optional[int] = None, cache_dtype: str = "bf16",
-                        rows_per_request: int = 1) -> DecodeBatch:
-    """A small batch with explicit lengths, for parity and edge cases."""
+                        rows_per_request=1) -> DecodeBatch:
+    """A small batch with explicit lengths, for parity and edge cases.
+    rows_per_request: query rows of every request, or a list with one count per
+    request (0 allowed)."""
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     return make_decode_batch(
         f"random(seed={seed})", seed, lambda rng: seq_lens, num_heads=num_heads,
