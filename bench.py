@@ -231,6 +231,10 @@ def main():
     ap.add_argument("--fp8-score", action="store_true",
                     help="skewed_fp8: the score on the fp8 matrix core with an e4m3fn-quantised "
                          "query (MLA_DECODE_FP8_SCORE)")
+    ap.add_argument("--rows-per-request", type=int, default=1,
+                    help="v2_lite: this many query rows per request over the same tokens (multi-token "
+                         "prediction, speculative decoding), planned with MLA_DECODE_SHARED_ROWS; the "
+                         "JSON also gives the time with one work item per row")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -243,6 +247,10 @@ def main():
 
     if args.fp8_score and (args.workload != "skewed_fp8" or args.append):
         print("--fp8-score applies to the skewed_fp8 workload's mla_decode only", file=sys.stderr)
+        sys.exit(2)
+    if args.rows_per_request < 1 or (args.rows_per_request > 1 and
+                                     (args.workload != "v2_lite" or args.append or args.fp8_score)):
+        print("--rows-per-request applies to the v2_lite workload's mla_decode only", file=sys.stderr)
         sys.exit(2)
     if args.workload == "projections":
         return bench_projections(args)
@@ -257,7 +265,9 @@ def main():
     dev = torch.device("cuda:0")
     make = {"v3": workloads.v3, "v2_lite": workloads.v2_lite, "skewed_fp8": workloads.skewed_fp8}
     t0 = time.perf_counter()
-    batch = make[args.workload]()
+    R = args.rows_per_request
+    batch = make[args.workload]() if R == 1 else workloads.v2_lite(rows_per_request=R)
+    qo = None if R == 1 else batch.qo_indptr
     log(f"workload {batch.name}: B={batch.batch} H={batch.num_heads} ps={batch.page_size} "
         f"tokens={int(batch.seq_lens.sum())} gen {time.perf_counter() - t0:.1f}s")
 
@@ -275,9 +285,9 @@ def main():
 
     dec = PagedMlaDecoder(batch.num_heads, batch.page_size, max_batch=batch.batch,
                           max_rows=batch.num_rows, kv_dtype=batch.cache_dtype, out_dtype="bf16",
-                          device=dev, fp8_score=args.fp8_score)
-    h = dec.plan(batch.kv_indptr, batch.kv_last_page_len)
-    plan_us = median_plan_us(lambda: dec.plan(batch.kv_indptr, batch.kv_last_page_len))
+                          device=dev, fp8_score=args.fp8_score, shared_rows=R > 1)
+    h = dec.plan(batch.kv_indptr, batch.kv_last_page_len, qo)
+    plan_us = median_plan_us(lambda: dec.plan(batch.kv_indptr, batch.kv_last_page_len, qo))
     torch.cuda.synchronize()
     outs = [torch.empty((batch.num_rows, batch.num_heads, 512), dtype=torch.bfloat16, device=dev)
             for _ in sets]
@@ -323,11 +333,35 @@ def main():
     elapsed = time.perf_counter() - t0
     launch_ms = np.array([a.elapsed_time(b) for a, b in events])
 
-    profile_key = f"mla_decode_{args.workload}" + ("_fp8_score" if args.fp8_score else "")
+    profile_key = (f"mla_decode_{args.workload}" + ("_fp8_score" if args.fp8_score else "") +
+                   (f"_rows{R}" if R > 1 else ""))
     tokens = int(batch.seq_lens.sum())
     latent_bytes = costs.mla_decode_latent_bytes(tokens, 1 if batch.cache_dtype != "bf16" else 2)
     assert latent_bytes == tokens * batch.cache_bytes_per_token
-    flops = float(costs.mla_decode_flops(tokens, batch.num_heads))
+    # Every query row attends to all of its request's tokens.
+    flops = float(costs.mla_decode_flops(tokens, batch.num_heads)) * R
+    per_row = None
+    if R > 1:
+        # The same batch with one work item per query row, for comparison.
+        dec1 = PagedMlaDecoder(batch.num_heads, batch.page_size, max_batch=batch.batch,
+                               max_rows=batch.num_rows, device=dev)
+        h1 = dec1.plan(batch.kv_indptr, batch.kv_last_page_len, qo)
+
+        def step1(i, ev=None):
+            s = sets[i % 2]
+            dec1.run(s[0], s[1], s[2], s[3], batch.sm_scale, batch.kv_scale, out=outs[i % 2],
+                     lse=lses[i % 2], stream=stream)
+
+        warm_until_steady(torch, stream, step1, args.warmup, min_s=args.warmup_seconds)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            step1(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_row = {"us_per_call": round(e0.elapsed_time(e1) * 1e3 / args.steps, 2),
+                   "items": h1.num_items, "merges": h1.num_merges}
+        log(f"one item per row: {per_row['us_per_call']:.1f} us per call ({h1.num_items} items)")
     ms_per_step = elapsed * 1e3 / args.steps
     gbs = latent_bytes / (ms_per_step * 1e-3) / 1e9
     launch_avg_ms = float(launch_ms.mean())
@@ -361,6 +395,7 @@ def main():
             "qk_rope_head_dim": 64, "page_size": batch.page_size, "kv_tokens": tokens,
             "query_rows": batch.num_rows, "parallelism": "single GPU",
             "fused_append": bool(args.append), "fp8_score": bool(args.fp8_score),
+            "rows_per_request": R, "shared_rows": R > 1,
         },
         "tokens_per_s": round(batch.num_rows / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -391,6 +426,8 @@ def main():
     res["copy_gbs"] = round(copy_gbs, 1)
     res["frac_of_copy_bandwidth"] = round(achieved / copy_gbs, 4)
     res["launch_us_p10_p50_p90"] = [round(float(np.percentile(launch_ms, q)) * 1e3, 2) for q in (10, 50, 90)]
+    if per_row is not None:
+        res["one_item_per_row"] = per_row
     mfma = None if args.append else measured_traffic(profile_key, "mfma_util_percent_decode")
     res["roofline"]["mfma_busy_counter"] = None if mfma is None else round(mfma / 100.0, 4)
     if not args.no_cpu_baseline:
