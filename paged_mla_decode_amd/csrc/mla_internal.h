@@ -128,11 +128,16 @@ struct MergePartialsArgs {
     int32_t num_heads;
     const void* prefix_out;  // fused prefix merge, or null
     const float* prefix_lse;
-    // Graph-safe launches: the counts in the plan's device copy (null otherwise).
-    // The narrow kernel then takes merges [*num_wide + blockIdx.x] while below
-    // *num_merges, the wide kernel merges [blockIdx.x] below *num_wide.
+    // Graph-safe launches: the counts in the plan's device copy (null otherwise),
+    // read by merge_partials_mixed_kernel.
     const int32_t* dev_num_merges;
     const int32_t* dev_num_wide;
+    // merge_partials_mixed_kernel: its first wide_bound * H workgroups take the
+    // wide merges; num_wide and num_merges are the counts when the device ones
+    // are null (set by launch_merge_partials).
+    int32_t wide_bound;
+    int32_t num_wide;
+    int32_t num_merges;
 };
 
 // Kernel launchers (device code lives in mla_kernels.hip). Return hipError_t as int.

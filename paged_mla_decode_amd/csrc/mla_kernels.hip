@@ -604,16 +604,13 @@ __device__ __forceinline__ void merge_store(const MergePartialsArgs& a, const ml
     if (a.lse && lane == 0) a.lse[orow] = empty ? -INFINITY : st.m + __logf(st.wsum);
 }
 
-// Few partials per row: one wave per (row, head) folds them all.
+// Few partials per row: one wave per (row, head) folds them all. For plans
+// without wide merges (graph-safe launches and plans with wide merges take
+// merge_partials_mixed_kernel).
 template <bool OUT32>
 __global__ __launch_bounds__(256) void merge_partials_kernel(const MergePartialsArgs a) {
     constexpr int kBatch = 8;
-    int m = blockIdx.x;
-    if (a.dev_num_merges) {  // graph-safe launch: a fixed grid, the counts from the plan
-        m += *a.dev_num_wide;
-        if (m >= *a.dev_num_merges) return;
-    }
-    const mla_merge_item mi = a.merges[m];
+    const mla_merge_item mi = a.merges[blockIdx.x];
     const int lane = threadIdx.x & 63;
     for (int h = blockIdx.y * 4 + (threadIdx.x >> 6); h < a.num_heads; h += gridDim.y * 4) {
         MergeState st;
@@ -627,14 +624,34 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(const MergePartials
 // Many partials per row (a very long request cut into hundreds of pieces): a
 // workgroup of kWaves waves per (row, head), each folding its own batches, the
 // wave states combined through LDS. One wave alone would wait out hundreds of
-// dependent memory round trips.
+// dependent memory round trips. The same launch merges the narrow rows that
+// follow the wide ones in the plan (kWaves heads per workgroup, one wave per
+// head, as merge_partials_kernel does), so that a plan with both kinds costs
+// one merge launch: workgroups [0, wide_bound * H) take (wide merge, head),
+// the rest (narrow merge, 16 heads).
 template <bool OUT32>
-__global__ __launch_bounds__(1024) void merge_partials_wide_kernel(const MergePartialsArgs a) {
+__global__ __launch_bounds__(1024) void merge_partials_mixed_kernel(const MergePartialsArgs a) {
     constexpr int kWaves = 16, kBatch = 8;
-    if (a.dev_num_merges && (int)blockIdx.x >= *a.dev_num_wide) return;  // graph-safe launch
-    const mla_merge_item mi = a.merges[blockIdx.x];
-    const int h = blockIdx.y;
+    const int nh = a.num_heads;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int num_wide = a.dev_num_wide ? *a.dev_num_wide : a.num_wide;
+    const int num_merges = a.dev_num_merges ? *a.dev_num_merges : a.num_merges;
+    const int wide_blocks = a.wide_bound * nh;
+    if ((int)blockIdx.x >= wide_blocks) {
+        const int b = blockIdx.x - wide_blocks, per = (nh + kWaves - 1) / kWaves;
+        const int m = num_wide + b / per, h = (b % per) * kWaves + wv;
+        if (m >= num_merges || h >= nh) return;
+        const mla_merge_item mi = a.merges[m];
+        MergeState st;
+        for (int p0 = 0; p0 < mi.num_partials; p0 += kBatch)
+            merge_batch<OUT32, kBatch>(a, mi, h, lane, p0, min(kBatch, mi.num_partials - p0), st);
+        if (a.prefix_lse) merge_prefix<OUT32>(a, mi.row, h, lane, st);
+        merge_store<OUT32>(a, mi, h, lane, st);
+        return;
+    }
+    const int m = blockIdx.x / nh, h = blockIdx.x % nh;
+    if (m >= num_wide) return;  // graph-safe launch: past this plan's wide merges
+    const mla_merge_item mi = a.merges[m];
     MergeState st;
     for (int p0 = wv * kBatch; p0 < mi.num_partials; p0 += kWaves * kBatch)
         merge_batch<OUT32, kBatch>(a, mi, h, lane, p0, min(kBatch, mi.num_partials - p0), st);
@@ -842,37 +859,30 @@ int launch_merge_partials(int out_dtype, const MergePartialsArgs& a, int num_mer
                           void* stream) {
     hipStream_t s = (hipStream_t)stream;
     const bool o32 = out_dtype == MLA_DTYPE_FP32;
-    if (a.dev_num_merges) {
-        // Graph-safe: num_merges and num_wide bound the plan's counts (which the
-        // kernels read from its device copy); both grids are launched.
-        const dim3 gw(num_wide, a.num_heads), bw(1024);
-        const dim3 gn(num_merges, (a.num_heads + 3) / 4), bn(256);
-        if (o32) {
-            merge_partials_wide_kernel<true><<<gw, bw, 0, s>>>(a);
-            merge_partials_kernel<true><<<gn, bn, 0, s>>>(a);
-        } else {
-            merge_partials_wide_kernel<false><<<gw, bw, 0, s>>>(a);
-            merge_partials_kernel<false><<<gn, bn, 0, s>>>(a);
-        }
+    const int nh = a.num_heads;
+    if (!a.dev_num_merges && num_merges <= 0) return 0;
+    if (a.dev_num_merges || num_wide > 0) {
+        // One launch for the wide merges and the narrow ones after them.
+        // Graph-safe: num_merges and num_wide bound the plan's counts, which the
+        // kernel reads from its device copy; any of the merges may be narrow.
+        MergePartialsArgs m = a;
+        m.wide_bound = num_wide;
+        m.num_wide = num_wide;
+        m.num_merges = num_merges;
+        const int narrow = a.dev_num_merges ? num_merges : num_merges - num_wide;
+        const int blocks = num_wide * nh + narrow * ((nh + 15) / 16);
+        if (blocks <= 0) return 0;
+        if (o32)
+            merge_partials_mixed_kernel<true><<<blocks, 1024, 0, s>>>(m);
+        else
+            merge_partials_mixed_kernel<false><<<blocks, 1024, 0, s>>>(m);
         return (int)hipGetLastError();
     }
-    if (num_merges <= 0) return 0;
-    if (num_wide > 0) {
-        const dim3 grid(num_wide, a.num_heads), block(1024);
-        if (o32)
-            merge_partials_wide_kernel<true><<<grid, block, 0, s>>>(a);
-        else
-            merge_partials_wide_kernel<false><<<grid, block, 0, s>>>(a);
-    }
-    if (num_merges > num_wide) {
-        MergePartialsArgs rest = a;
-        rest.merges = a.merges + num_wide;
-        const dim3 grid(num_merges - num_wide, (a.num_heads + 3) / 4), block(256);
-        if (o32)
-            merge_partials_kernel<true><<<grid, block, 0, s>>>(rest);
-        else
-            merge_partials_kernel<false><<<grid, block, 0, s>>>(rest);
-    }
+    const dim3 grid(num_merges, (nh + 3) / 4), block(256);
+    if (o32)
+        merge_partials_kernel<true><<<grid, block, 0, s>>>(a);
+    else
+        merge_partials_kernel<false><<<grid, block, 0, s>>>(a);
     return (int)hipGetLastError();
 }
 
