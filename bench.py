@@ -521,6 +521,11 @@ def bench_projections(args):
     # instead over `steps` back-to-back launches on the same rotating sets, with
     # one pair of HIP events on the launch stream around them.
     def launch_avg_us(fn):
+        # A few untimed calls first: the first launch of a kernel the step does
+        # not use loads its code.
+        for i in range(10):
+            fn(i)
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(args.steps):
@@ -698,6 +703,11 @@ def bench_tree_verify(args):
     elapsed = time.perf_counter() - t0
 
     def launch_avg_us(fn):
+        # A few untimed calls first: the first launch of a kernel the step does
+        # not use loads its code.
+        for i in range(10):
+            fn(i)
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(args.steps):
