@@ -233,8 +233,10 @@ def main():
                          "query (MLA_DECODE_FP8_SCORE)")
     ap.add_argument("--rows-per-request", type=int, default=1,
                     help="v2_lite: this many query rows per request over the same tokens (multi-token "
-                         "prediction, speculative decoding), planned with MLA_DECODE_SHARED_ROWS; the "
-                         "JSON also gives the time with one work item per row")
+                         "prediction, speculative decoding), planned with MLA_DECODE_SHARED_ROWS")
+    ap.add_argument("--compare-per-row", action="store_true",
+                    help="with --rows-per-request: also time the batch with one work item per query row "
+                         "(one_item_per_row in the JSON)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -341,7 +343,7 @@ def main():
     # Every query row attends to all of its request's tokens.
     flops = float(costs.mla_decode_flops(tokens, batch.num_heads)) * R
     per_row = None
-    if R > 1:
+    if R > 1 and args.compare_per_row:
         # The same batch with one work item per query row, for comparison.
         dec1 = PagedMlaDecoder(batch.num_heads, batch.page_size, max_batch=batch.batch,
                                max_rows=batch.num_rows, device=dev)

@@ -196,3 +196,87 @@ def test_tree_verify_step_replays_from_one_graph(dev):
         compare(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
                 ref_out, ref_lse, False, f"tree replay {rep} vs oracle")
         out.zero_()
+
+
+@pytest.mark.parametrize("H", [16, 32])
+def test_graph_replay_with_shared_rows(dev, H):
+    """Graph-safe plans with MLA_DECODE_SHARED_ROWS: batches with different row
+    counts per request through one captured call; each replay equals an eager
+    call on its plan bit for bit and the oracle within the tolerances, and rows
+    past the plan's are left as they were."""
+    from paged_mla_decode_amd.decoder import PagedMlaDecoder
+    ps = 16
+    cases = [([3000, 40, 1, 700], [4, 1, 2, 3]), ([10, 5000, 300], [1, 5, 2]), ([900, 900], [2, 2])]
+    max_rows = max(sum(r) for _, r in cases)
+    max_batch = max(len(lens) for lens, _ in cases)
+    pool = workloads.random_decode_batch(95 + H, [12000], num_heads=H, page_size=ps)
+    cache = bf16_to_device(pool.cache, dev)
+    rng = np.random.Generator(np.random.PCG64(96))
+    q_all = workloads.f32_to_bf16_bits(rng.standard_normal((max_rows, H, 576), dtype=np.float32) * np.float32(0.5))
+    q = bf16_to_device(q_all, dev)
+    qn, qr = q[:, :, :512], q[:, :, 512:]
+    filled = pool.kv_indices
+
+    def csr(lens, rows, seed):
+        r = np.random.Generator(np.random.PCG64(seed))
+        npages = [(L + ps - 1) // ps for L in lens]
+        indptr = np.concatenate([[0], np.cumsum(npages)]).astype(np.int32)
+        indices = filled[r.permutation(len(filled))[:indptr[-1]]].astype(np.int32)
+        last = np.array([L - ps * (n - 1) if L > 0 else 0 for L, n in zip(lens, npages)], np.int32)
+        qo = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+        return indptr, indices, last, qo
+
+    batches = [csr(lens, rows, 200 + k) for k, (lens, rows) in enumerate(cases)]
+
+    def check_oracle(k, o, l, what):
+        indptr, indices, last, qo = batches[k]
+        n = int(qo[-1])
+        b = dataclasses.replace(
+            pool, qo_indptr=qo, kv_indptr=indptr, kv_indices=indices, kv_last_page_len=last,
+            seq_lens=np.asarray(cases[k][0], np.int32),
+            q_nope=np.ascontiguousarray(q_all[:n, :, :512]), q_rope=np.ascontiguousarray(q_all[:n, :, 512:]))
+        ref_out, ref_lse = oracle.decode_batch(b)
+        compare(o[:n].float().cpu().numpy().astype(np.float64), l[:n].cpu().numpy().astype(np.float64),
+                ref_out, ref_lse, False, what)
+
+    max_idx = max(len(b[1]) for b in batches)
+    idx = torch.zeros(max_idx, dtype=torch.int32, device=dev)
+    dec = PagedMlaDecoder(H, ps, max_batch=max_batch, max_rows=max_rows, num_cus=16, device=dev,
+                          graph_safe=True, shared_rows=True)
+    out = torch.zeros((max_rows, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros((max_rows, H), dtype=torch.float32, device=dev)
+
+    def load(k):
+        indptr, indices, last, qo = batches[k]
+        idx[:len(indices)].copy_(torch.from_numpy(indices))
+        return dec.plan(indptr, last, qo)
+
+    h0 = load(0)
+    assert h0.num_merges > 0
+    dec.run(qn, qr, cache, idx, pool.sm_scale, pool.kv_scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    check_oracle(0, out, lse, f"H={H} shared rows graph-safe eager call vs oracle")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s), torch.cuda.graph(g, stream=s):
+        dec.run(qn, qr, cache, idx, pool.sm_scale, pool.kv_scale, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep, k in enumerate([1, 2, 0, 2, 1]):
+        h = load(k)
+        rows = h.num_rows
+        sentinel_out = out[rows:].clone()
+        sentinel_lse = lse[rows:].clone()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = dec.run(qn, qr, cache, idx, pool.sm_scale, pool.kv_scale)
+        torch.cuda.synchronize()
+        say(f"H={H} shared rows replay {rep}: batch {k} rows={rows} items={h.num_items} merges={h.num_merges}")
+        assert torch.equal(out[:rows], ref_out[:rows]) and torch.equal(lse[:rows], ref_lse[:rows]), \
+            f"replay {rep} (batch {k}) differs from the eager call"
+        check_oracle(k, out, lse, f"replay {rep} vs oracle")
+        assert torch.equal(out[rows:], sentinel_out) and torch.equal(lse[rows:], sentinel_lse), \
+            "padding rows were written"
+        out[:rows].zero_()
