@@ -146,10 +146,10 @@ int launch_decode(const Variant& v, int kv_dtype, int out_dtype, const DecodeArg
 // The 128-head kernel (latent columns split across the waves), mla_decode_h128.hip.
 int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num_workers,
                        void* stream);
-// Rows with at least kWideMergePartials partials take the wide merge kernel
-// (one workgroup per row and head), the others one wave per row and head. The
-// plan lists merges by partial count, most first; the first num_wide of them
-// are wide.
+// Rows with at least kWideMergePartials partials are merged by a workgroup per
+// row and head, the others by one wave per row and head (in the same launch
+// when a plan has both kinds). The plan lists merges by partial count, most
+// first; the first num_wide of them are wide.
 constexpr int kWideMergePartials = 16;
 int launch_merge_partials(int out_dtype, const MergePartialsArgs& a, int num_merges, int num_wide,
                           void* stream);

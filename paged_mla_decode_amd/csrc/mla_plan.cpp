@@ -289,8 +289,8 @@ int32_t plan_build(const mla_decode_params* p, int32_t num_cus, int32_t batch,
                 merges.push_back(mla_merge_item{rows[i].row + r, num_partials + r, npieces[i], rows[i].nrows});
             num_partials += npieces[i] * rows[i].nrows;
         }
-    // Rows with the most partials first: the launch merges the leading ones
-    // (at least kWideMergePartials each) with the wide kernel.
+    // Rows with the most partials first: the merge launch takes the leading ones
+    // (at least kWideMergePartials each) with a workgroup per row and head.
     std::stable_sort(merges.begin(), merges.end(),
                      [](const mla_merge_item& x, const mla_merge_item& y) { return x.num_partials > y.num_partials; });
     std::vector<int32_t> next_slot(first_slot);

@@ -188,9 +188,9 @@ def test_one_worker_runs_every_item(dev, cache_dtype):
 @pytest.mark.parametrize("H", [16, 128])
 @pytest.mark.parametrize("out_dtype", ["bf16", "fp32"])
 def test_many_partials_take_the_wide_merge(dev, H, out_dtype):
-    """A long request cut into dozens of pieces: its partials are merged by the
-    wide merge kernel (a workgroup per row and head), the short rows' by the
-    one-wave kernel in the same launch."""
+    """A long request cut into dozens of pieces: its partials are merged by a
+    workgroup per row and head, the short rows' by one wave per row and head,
+    in the same merge launch."""
     batch = workloads.random_decode_batch(41 + H, [20000, 300, 5, 2600], num_heads=H, page_size=16)
     say(f"wide merge H={H} out={out_dtype}")
     ref_out, ref_lse = oracle.decode_batch(batch)
