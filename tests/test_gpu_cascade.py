@@ -75,3 +75,39 @@ def test_suffix_merge_validates_aliasing(dev):
     big = torch.zeros((3, 16, 512), dtype=torch.bfloat16, device=dev)
     with pytest.raises(B.MlaError):  # out overlaps the prefix without being it
         d.run_suffix_merge(qn, qr, cache, idx, batch.sm_scale, big[:2], pl, out=big[1:])
+
+
+def test_tree_verify_single_pass_at_the_suffix_maximum(dev):
+    """mla_decode_tree_verify with suffix_tokens at its maximum (256): rows with
+    0, 1, 31-33, 255 and 256 visible suffix slots (whole tiles of suffix, and a
+    table row stride above S), each against the oracle over its request's
+    prefix and then its suffix slots."""
+    from paged_mla_decode_amd.decoder import PagedMlaDecoder
+    S, stride = 256, 260
+    counts = [0, 1, 31, 32, 33, 255, 256, 100]
+    batch = workloads.random_decode_batch(61, [37, 700], num_heads=128, page_size=1, rows_per_request=4)
+    N = batch.num_rows
+    rng = np.random.Generator(np.random.PCG64(62))
+    valid = batch.kv_indices[:int(batch.kv_indptr[-1])]  # pool rows that hold values
+    table = np.zeros((N, stride), np.int32)
+    for r in range(N):
+        table[r, :counts[r]] = rng.choice(valid, size=counts[r], replace=True)
+    qn, qr, cache, idx = batch_to_device(batch, dev)
+    d = PagedMlaDecoder(128, 1, max_batch=batch.batch, max_rows=N, device=dev, suffix_tokens=S)
+    d.plan(batch.kv_indptr, batch.kv_last_page_len, batch.qo_indptr)
+    out, lse = d.run_tree_verify(qn, qr, cache, idx, torch.from_numpy(table).to(dev),
+                                 torch.from_numpy(np.asarray(counts, np.int32)).to(dev), batch.sm_scale)
+    torch.cuda.synchronize()
+    row_req = np.repeat(np.arange(batch.batch), np.diff(batch.qo_indptr))
+    indptr, indices = [0], []
+    for r in range(N):
+        b = row_req[r]
+        slots = np.concatenate([batch.kv_indices[batch.kv_indptr[b]:batch.kv_indptr[b + 1]], table[r, :counts[r]]])
+        indices.append(slots)
+        indptr.append(indptr[-1] + len(slots))
+    ref_out, ref_lse = oracle.mla_decode(batch.q_nope, batch.q_rope, batch.cache, np.asarray(indptr, np.int32),
+                                         np.concatenate(indices).astype(np.int32), 1, batch.sm_scale,
+                                         kv_last_page_len=np.ones(N, np.int32))
+    say(f"tree verify at S={S}: suffix counts {counts}")
+    compare(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+            ref_out, ref_lse, False, "tree verify S=256")

@@ -197,3 +197,19 @@ def test_many_partials_take_the_wide_merge(dev, H, out_dtype):
     out, lse, dec = run_decode(batch, dev, out_dtype, num_cus=64)
     assert dec.header().max_merge_partials >= 16
     compare(out, lse, ref_out, ref_lse, out_dtype == "fp32", f"wide merge H={H} out={out_dtype}")
+
+
+@pytest.mark.parametrize("H", [16, 128])
+@pytest.mark.parametrize("ps", [128, 1024])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
+def test_large_page_sizes(dev, H, ps, kv):
+    """Pages larger than a tile (a 1024-token page holds 32 tiles): the shift
+    branch of the address generation with many tiles per page, partial last
+    pages, and requests shorter than one page."""
+    lens = [1, ps - 1, ps, ps + 1, 3 * ps + 17, 2000]
+    batch = workloads.random_decode_batch(330 + H + ps, lens, num_heads=H, page_size=ps, cache_dtype=kv)
+    say(f"large page size H={H} ps={ps} kv={kv}")
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    for splits in (1, 0):
+        out, lse, dec = run_decode(batch, dev, "bf16", max_splits=splits, num_cus=8)
+        compare(out, lse, ref_out, ref_lse, False, f"H={H} ps={ps} kv={kv} merges={dec.header().num_merges}")
