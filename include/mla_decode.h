@@ -257,7 +257,9 @@ int32_t mla_decode_plan(const mla_decode_params* params, int32_t batch, const in
  *              (latent 512, then rope 64); 16-byte aligned.
  *   kv_scale   fp8 dequantisation scale (cache value = code * kv_scale); must be
  *              1 for bf16 caches.
- *   kv_indices_d  int32 page numbers, the CSR column array of the plan's batch.
+ *   kv_indices_d  int32 page numbers, the CSR column array of the plan's batch;
+ *              may be NULL when the batch has no page entries (every request
+ *              empty: each row's out is 0 and its lse -inf).
  *   kv_lens_d  int32 [batch] token counts known only on the device, or NULL.
  *              Request b then attends to min(kv_lens_d[b], planned length)
  *              tokens. This is how the tree-verify suffix uses the compacted

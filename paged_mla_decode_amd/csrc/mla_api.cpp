@@ -165,7 +165,9 @@ int32_t decode_impl(const mla_decode_params* params, const void* plan_h, const v
     // A graph-safe call launches whatever this plan holds: a later plan may not be empty.
     const bool graph = (params->flags & MLA_DECODE_GRAPH_SAFE) != 0;
     if (h->num_items == 0 && !graph) return MLA_OK;
-    if (!q_nope_d || !q_rope_d || !kv_cache_d || !kv_indices_d || !out_d) return MLA_ERR_INVALID_ARG;
+    // A batch of empty requests has no page entries, and its page array may be NULL.
+    if (!q_nope_d || !q_rope_d || !kv_cache_d || (!kv_indices_d && h->num_page_entries > 0) || !out_d)
+        return MLA_ERR_INVALID_ARG;
     if (!aligned16(q_nope_d) || !aligned16(q_rope_d) || !aligned16(kv_cache_d) || !aligned16(out_d) ||
         !aligned16(workspace_d))
         return MLA_ERR_INVALID_ARG;

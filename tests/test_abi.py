@@ -140,6 +140,7 @@ def test_decode_validates_before_launch():
 
     assert call(q_nope_d=None) == m.MLA_ERR_INVALID_ARG
     assert call(kv_cache_d=None) == m.MLA_ERR_INVALID_ARG
+    assert call(kv_indices_d=None) == m.MLA_ERR_INVALID_ARG  # the batch has page entries
     assert call(out_d=FAKE + 8) == m.MLA_ERR_INVALID_ARG  # misaligned
     assert call(q_nope_stride_h=500) == m.MLA_ERR_INVALID_ARG
     assert call(sm_scale=float("nan")) == m.MLA_ERR_INVALID_ARG

@@ -99,6 +99,9 @@ def check_invariants(p, batch, h, items, merges, workers):
         assert h.num_workers == G
         pour = sorted((w % 8) * (G // 8) + w // 8 for w in busy)
         assert pour == list(range(len(busy))), "busy workers are a prefix of the pour"
+    elif p.flags & m.MLA_DECODE_GRAPH_SAFE:
+        # graph-safe plans list all G workers; the busy ones come first
+        assert h.num_workers == G and busy == list(range(len(busy)))
     else:
         assert busy == list(range(h.num_workers)), "every worker has an item"
     assert h.num_workers <= G

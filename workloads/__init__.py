@@ -353,16 +353,16 @@ def tree_verify(seed: int = 4, batch: int = 16, prefix_len: int = 2048, width: i
 
 def random_decode_batch(seed: int, seq_lens, num_heads: int, page_size: int,
                         pool_pages: Optional[int] = None, cache_dtype: str = "bf16",
-                        rows_per_request=1) -> DecodeBatch:
+                        rows_per_request=1, layout_only: bool = False) -> DecodeBatch:
     """A small batch with explicit lengths, for parity and edge cases.
     rows_per_request: query rows of every request, or a list with one count per
-    request (0 allowed)."""
+    request (0 allowed). layout_only: the lengths and page layout only."""
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     return make_decode_batch(
         f"random(seed={seed})", seed, lambda rng: seq_lens, num_heads=num_heads,
         page_size=page_size,
         pool_pages_fn=lambda need: pool_pages if pool_pages is not None else 2 * need + 3,
-        cache_dtype=cache_dtype, rows_per_request=rows_per_request)
+        cache_dtype=cache_dtype, rows_per_request=rows_per_request, layout_only=layout_only)
 
 
 @dataclasses.dataclass
