@@ -17,7 +17,7 @@ def dev():
     return require_gpu()
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_batch_against_the_oracle(dev, seed):
     rng = np.random.Generator(np.random.PCG64(1000 + seed))
     B = int(rng.integers(1, 7))
