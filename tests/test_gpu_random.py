@@ -1,7 +1,9 @@
-"""Seeded random small batches through the whole decode path against the
+"""Seeded random small batches through the decode entry points against the
 oracle: head counts, page sizes (powers of two and not), bf16 and fp8 caches,
 bf16 and fp32 outputs, several query rows per request with and without shared
-rows, CU counts and split caps drawn per case."""
+rows, CU counts and split caps drawn per case; the fused append (outputs, and
+the cache bit for bit) and the fused prefix merge (in place and not) on random
+batches of their own."""
 import numpy as np
 import pytest
 
@@ -38,3 +40,65 @@ def test_random_batch_against_the_oracle(dev, seed):
     ref_out, ref_lse = oracle.decode_batch(batch)
     out, lse, dec = run_decode(batch, dev, out_dtype, max_splits=splits, num_cus=cus, shared_rows=shared)
     compare(out, lse, ref_out, ref_lse, out_dtype == "fp32", what)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_append_against_the_oracle(dev, seed):
+    """mla_decode_append on random batches: outputs within the tolerances and
+    the whole cache after the call bit for bit against write-then-decode."""
+    from test_gpu_append import new_rows, run_append
+    rng = np.random.Generator(np.random.PCG64(3000 + seed))
+    B = int(rng.integers(1, 7))
+    lens = [int(x) for x in rng.choice([1, 2, 31, 32, 33, 200, 1500, 3000], size=B)]
+    ps = int(rng.choice([1, 3, 16, 64, 128]))
+    H = int(rng.choice([16, 32, 64, 128]))
+    kv = str(rng.choice(["bf16", "fp8_e4m3fn"]))
+    out_dtype = str(rng.choice(["bf16", "fp32"]))
+    cus = int(rng.choice([1, 7, 32, 256]))
+    batch = workloads.random_decode_batch(4000 + seed, lens, num_heads=H, page_size=ps, cache_dtype=kv)
+    c, r = new_rows(5000 + seed, B)
+    what = f"append seed={seed} lens={lens} ps={ps} H={H} kv={kv} out={out_dtype} cus={cus}"
+    say(what)
+    ref_out, ref_lse, ref_cache = oracle.append_then_decode(
+        batch.q_nope, batch.q_rope, batch.cache, batch.kv_indptr, batch.kv_indices,
+        batch.kv_last_page_len, batch.page_size, batch.sm_scale, c, r, batch.kv_scale)
+    out, lse, cache, _ = run_append(batch, dev, c, r, out_dtype=out_dtype, num_cus=cus)
+    assert np.array_equal(cache, ref_cache), f"{what}: cache differs from write-then-decode"
+    compare(out, lse, ref_out, ref_lse, out_dtype == "fp32", what)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_suffix_merge_against_the_oracle(dev, seed):
+    """mla_decode_suffix_merge on random prefix / suffix splits (page size 1):
+    the merged state equals the oracle's attention over the union."""
+    import torch
+    from test_gpu_cascade import split_csr
+    from gpu_util import batch_to_device
+    from paged_mla_decode_amd.decoder import PagedMlaDecoder
+    rng = np.random.Generator(np.random.PCG64(6000 + seed))
+    B = int(rng.integers(1, 7))
+    prefix = [int(x) for x in rng.choice([0, 1, 5, 33, 300, 1500], size=B)]
+    suffix = [int(x) for x in rng.choice([0, 1, 7, 32, 200, 1500], size=B)]
+    H = int(rng.choice([16, 32, 64, 128]))
+    out_dtype = str(rng.choice(["bf16", "fp32"]))
+    inplace = bool(rng.random() < 0.5)
+    cus = int(rng.choice([1, 7, 32, 256]))
+    batch = workloads.random_decode_batch(7000 + seed, [p + s for p, s in zip(prefix, suffix)],
+                                          num_heads=H, page_size=1)
+    (pi, pidx, plast), (si, sidx, slast) = split_csr(batch, prefix)
+    what = f"suffix merge seed={seed} prefix={prefix} suffix={suffix} H={H} out={out_dtype} inplace={inplace} cus={cus}"
+    say(what)
+    qn, qr, cache, _ = batch_to_device(batch, dev)
+    dp = PagedMlaDecoder(H, 1, max_batch=B, out_dtype=out_dtype, num_cus=cus, device=dev)
+    dp.plan(pi, plast)
+    pidx_d = torch.from_numpy(pidx).to(dev) if len(pidx) else torch.zeros(1, dtype=torch.int32, device=dev)
+    sidx_d = torch.from_numpy(sidx).to(dev) if len(sidx) else torch.zeros(1, dtype=torch.int32, device=dev)
+    out_p, lse_p = dp.run(qn, qr, cache, pidx_d, batch.sm_scale)
+    ds = PagedMlaDecoder(H, 1, max_batch=B, out_dtype=out_dtype, num_cus=cus, device=dev)
+    ds.plan(si, slast)
+    kw = dict(out=out_p, lse=lse_p) if inplace else {}
+    out, lse = ds.run_suffix_merge(qn, qr, cache, sidx_d, batch.sm_scale, out_p, lse_p, **kw)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.decode_batch(batch)
+    compare(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+            ref_out, ref_lse, out_dtype == "fp32", what)
