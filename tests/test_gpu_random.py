@@ -102,3 +102,38 @@ def test_random_suffix_merge_against_the_oracle(dev, seed):
     ref_out, ref_lse = oracle.decode_batch(batch)
     compare(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
             ref_out, ref_lse, out_dtype == "fp32", what)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_fp8_score_against_the_oracle(dev, seed):
+    """MLA_DECODE_FP8_SCORE on random e4m3fn batches (128 heads, bf16 output,
+    several rows per request at times): within the bound derived for the fp8
+    matrix core and within the plain bf16 gates, against the oracle with the
+    dequantised query."""
+    from test_gpu_fp8_score import check, reference
+    rng = np.random.Generator(np.random.PCG64(8000 + seed))
+    B = int(rng.integers(1, 7))
+    lens = [int(x) for x in rng.choice([0, 1, 5, 31, 32, 33, 200, 777, 1500, 3000], size=B)]
+    ps = int(rng.choice([1, 3, 16, 64, 128]))
+    rows = [int(x) for x in rng.integers(0, 4, size=B)] if rng.random() < 0.5 else 1
+    if rows != 1 and sum(rows) == 0:
+        rows[0] = 1
+    cus = int(rng.choice([1, 7, 32, 256]))
+    splits = int(rng.choice([0, 0, 1, 3]))
+    batch = workloads.random_decode_batch(9000 + seed, lens, num_heads=128, page_size=ps,
+                                          cache_dtype="fp8_e4m3fn", rows_per_request=rows)
+    what = f"fp8 score seed={seed} lens={lens} ps={ps} rows={rows} cus={cus} splits={splits}"
+    say(what)
+    import torch
+    from gpu_util import batch_to_device
+    from paged_mla_decode_amd.decoder import PagedMlaDecoder
+    qn, qr, cache, idx = batch_to_device(batch, dev)
+    dec = PagedMlaDecoder(128, ps, max_batch=B, max_rows=max(1, batch.num_rows), kv_dtype="fp8_e4m3fn",
+                          num_cus=cus, max_splits=splits, device=dev, fp8_score=True)
+    qo = None if np.all(np.diff(batch.qo_indptr) == 1) else batch.qo_indptr
+    dec.plan(batch.kv_indptr, batch.kv_last_page_len, qo)
+    out, lse = dec.run(qn, qr, cache, idx, batch.sm_scale, batch.kv_scale)
+    torch.cuda.synchronize()
+    ref_out, ref_lse, D, M = reference(batch)
+    check(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+          ref_out, ref_lse, D, M, what)
