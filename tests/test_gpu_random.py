@@ -2,8 +2,8 @@
 oracle: head counts, page sizes (powers of two and not), bf16 and fp8 caches,
 bf16 and fp32 outputs, several query rows per request with and without shared
 rows, CU counts and split caps drawn per case; the fused append (outputs, and
-the cache bit for bit) and the fused prefix merge (in place and not) on random
-batches of their own."""
+the cache bit for bit), the fused prefix merge (in place and not), the fp8
+score and the single tree-verify pass on random batches of their own."""
 import numpy as np
 import pytest
 
@@ -137,3 +137,47 @@ def test_random_fp8_score_against_the_oracle(dev, seed):
     ref_out, ref_lse, D, M = reference(batch)
     check(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
           ref_out, ref_lse, D, M, what)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_tree_verify_against_the_oracle(dev, seed):
+    """mla_decode_tree_verify on random prefixes, row counts, suffix caps and
+    suffix tables: each row against the oracle over its request's prefix and
+    then its visible suffix slots."""
+    import torch
+    from gpu_util import batch_to_device
+    from paged_mla_decode_amd.decoder import PagedMlaDecoder
+    rng = np.random.Generator(np.random.PCG64(10000 + seed))
+    B = int(rng.integers(1, 5))
+    prefix = [int(x) for x in rng.choice([1, 5, 33, 300, 2048], size=B)]
+    rows = [int(x) for x in rng.integers(1, 6, size=B)]
+    S = int(rng.choice([1, 8, 64, 256]))
+    stride = S + int(rng.integers(0, 5))
+    cus = int(rng.choice([1, 7, 32, 256]))
+    batch = workloads.random_decode_batch(11000 + seed, prefix, num_heads=128, page_size=1, rows_per_request=rows)
+    N = batch.num_rows
+    counts = rng.integers(0, S + 1, size=N).astype(np.int32)
+    valid = batch.kv_indices[:int(batch.kv_indptr[-1])]
+    table = np.zeros((N, stride), np.int32)
+    for r in range(N):
+        table[r, :counts[r]] = rng.choice(valid, size=int(counts[r]), replace=True)
+    what = f"tree verify seed={seed} prefix={prefix} rows={rows} S={S} counts={counts.tolist()} cus={cus}"
+    say(what)
+    qn, qr, cache, idx = batch_to_device(batch, dev)
+    d = PagedMlaDecoder(128, 1, max_batch=B, max_rows=N, num_cus=cus, device=dev, suffix_tokens=S)
+    d.plan(batch.kv_indptr, batch.kv_last_page_len, batch.qo_indptr)
+    out, lse = d.run_tree_verify(qn, qr, cache, idx, torch.from_numpy(table).to(dev),
+                                 torch.from_numpy(counts).to(dev), batch.sm_scale)
+    torch.cuda.synchronize()
+    row_req = np.repeat(np.arange(B), np.diff(batch.qo_indptr))
+    indptr, indices = [0], []
+    for r in range(N):
+        b = row_req[r]
+        slots = np.concatenate([batch.kv_indices[batch.kv_indptr[b]:batch.kv_indptr[b + 1]], table[r, :counts[r]]])
+        indices.append(slots)
+        indptr.append(indptr[-1] + len(slots))
+    ref_out, ref_lse = oracle.mla_decode(batch.q_nope, batch.q_rope, batch.cache, np.asarray(indptr, np.int32),
+                                         np.concatenate(indices).astype(np.int32), 1, batch.sm_scale,
+                                         kv_last_page_len=np.ones(N, np.int32))
+    compare(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+            ref_out, ref_lse, False, what)
