@@ -104,6 +104,13 @@ def check_invariants(p, batch, h, items, merges, workers):
         assert h.num_workers == G and busy == list(range(len(busy)))
     else:
         assert busy == list(range(h.num_workers)), "every worker has an item"
+    if p.flags & m.MLA_DECODE_GRAPH_SAFE:
+        # The fixed merge grid of a graph-safe launch covers any plan: at most G - 1
+        # split units (each crosses a worker boundary), at most ceil((G - 1) / 15)
+        # of them wide, each of up to rows_per_item rows.
+        R = rows_per_item(p)
+        assert h.num_merges <= max(1, G - 1) * R
+        assert h.num_wide_merges <= max(1, (G - 1 + 14) // 15) * R
     assert h.num_workers <= G
     # no worker above the plan's capacity by more than a minimum piece, unless
     # a single item (or an unsplittable row) forces it
