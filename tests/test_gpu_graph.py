@@ -280,3 +280,76 @@ def test_graph_replay_with_shared_rows(dev, H):
         assert torch.equal(out[rows:], sentinel_out) and torch.equal(lse[rows:], sentinel_lse), \
             "padding rows were written"
         out[:rows].zero_()
+
+
+@pytest.mark.parametrize("H,shared", [(16, False), (32, True), (128, False)])
+def test_graph_replay_over_random_plans(dev, H, shared):
+    """One captured graph-safe call replayed over eight random plans (request
+    counts, lengths from empty to long, row counts, splits): each replay equal
+    to an eager call bit for bit and to the oracle within the tolerances."""
+    from paged_mla_decode_amd.decoder import PagedMlaDecoder
+    ps, max_batch, max_rows = 16, 8, 24
+    pool = workloads.random_decode_batch(120 + H, [50000], num_heads=H, page_size=ps)
+    cache = bf16_to_device(pool.cache, dev)
+    rng = np.random.Generator(np.random.PCG64(121 + H))
+    q_all = workloads.f32_to_bf16_bits(rng.standard_normal((max_rows, H, 576), dtype=np.float32) * np.float32(0.5))
+    q = bf16_to_device(q_all, dev)
+    qn, qr = q[:, :, :512], q[:, :, 512:]
+    filled = pool.kv_indices
+    cases = []
+    for k in range(8):
+        B = int(rng.integers(1, max_batch + 1))
+        lens = [int(x) for x in rng.choice([0, 1, 33, 300, 2000, 6000], size=B)]
+        rows = [int(x) for x in rng.integers(1, 4, size=B)]
+        while sum(rows) > max_rows:
+            rows[int(np.argmax(rows))] -= 1
+        npages = [(L + ps - 1) // ps for L in lens]
+        indptr = np.concatenate([[0], np.cumsum(npages)]).astype(np.int32)
+        assert indptr[-1] <= len(filled)  # distinct pages that hold values
+        indices = filled[rng.permutation(len(filled))[:indptr[-1]]].astype(np.int32)
+        last = np.array([L - ps * (n - 1) if L > 0 else 0 for L, n in zip(lens, npages)], np.int32)
+        qo = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+        cases.append((lens, indptr, indices, last, qo))
+    idx = torch.zeros(max(1, max(len(c[2]) for c in cases)), dtype=torch.int32, device=dev)
+    dec = PagedMlaDecoder(H, ps, max_batch=max_batch, max_rows=max_rows, num_cus=32, device=dev,
+                          graph_safe=True, shared_rows=shared)
+    out = torch.zeros((max_rows, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros((max_rows, H), dtype=torch.float32, device=dev)
+
+    def load(k):
+        lens, indptr, indices, last, qo = cases[k]
+        if len(indices):
+            idx[:len(indices)].copy_(torch.from_numpy(indices))
+        return dec.plan(indptr, last, qo)
+
+    load(0)
+    dec.run(qn, qr, cache, idx, pool.sm_scale, pool.kv_scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s), torch.cuda.graph(g, stream=s):
+        dec.run(qn, qr, cache, idx, pool.sm_scale, pool.kv_scale, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for k in range(len(cases)):
+        h = load(k)
+        rows = h.num_rows
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = dec.run(qn, qr, cache, idx, pool.sm_scale, pool.kv_scale)
+        torch.cuda.synchronize()
+        lens, indptr, indices, last, qo = cases[k]
+        say(f"H={H} shared={shared} random plan {k}: lens={lens} rows={np.diff(qo).tolist()} "
+            f"items={h.num_items} merges={h.num_merges} wide={h.num_wide_merges}")
+        assert torch.equal(out[:rows], ref_out[:rows]) and torch.equal(lse[:rows], ref_lse[:rows]), \
+            f"replay {k} differs from the eager call"
+        b = dataclasses.replace(
+            pool, qo_indptr=qo, kv_indptr=indptr, kv_indices=indices, kv_last_page_len=last,
+            seq_lens=np.asarray(lens, np.int32),
+            q_nope=np.ascontiguousarray(q_all[:rows, :, :512]), q_rope=np.ascontiguousarray(q_all[:rows, :, 512:]))
+        o_ref, l_ref = oracle.decode_batch(b)
+        compare(out[:rows].float().cpu().numpy().astype(np.float64), lse[:rows].cpu().numpy().astype(np.float64),
+                o_ref, l_ref, False, f"random plan {k} replay vs oracle")
+        out[:rows].zero_()
