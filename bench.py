@@ -325,14 +325,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     warm_s, warm_steps = warm_until_steady(torch, stream, step, args.warmup, min_s=args.warmup_seconds)
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # The timed region: K calls back to back, with no event between them (an
+    # event record is a packet of its own in the stream), bracketed by
+    # synchronisations; two events on the stream give its GPU time.
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    g0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gpu_step_us = g0.elapsed_time(g1) * 1e3 / args.steps
+    # Then the same K calls again, each between two events of its own, for the
+    # per-call times (average, p10/p50/p90) of the roofline.
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, events[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     launch_ms = np.array([a.elapsed_time(b) for a, b in events])
 
     profile_key = (f"mla_decode_{args.workload}" + ("_fp8_score" if args.fp8_score else "") +
@@ -428,6 +440,7 @@ def main():
     res["copy_gbs"] = round(copy_gbs, 1)
     res["frac_of_copy_bandwidth"] = round(achieved / copy_gbs, 4)
     res["launch_us_p10_p50_p90"] = [round(float(np.percentile(launch_ms, q)) * 1e3, 2) for q in (10, 50, 90)]
+    res["gpu_us_per_step"] = round(gpu_step_us, 2)
     if per_row is not None:
         res["one_item_per_row"] = per_row
     mfma = None if args.append else measured_traffic(profile_key, "mfma_util_percent_decode")
