@@ -345,7 +345,9 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                     const LDS_AS char* Pb = (const LDS_AS char*)pbuf;
 
                     // Score operand s (one or two k-slices): raw tile bytes; fp8 codes
-                    // are widened to bf16 next to their MFMA.
+                    // are widened to bf16 next to their MFMA. The bf16 operands of both
+                    // products come from LDS and the query from global memory, so their
+                    // MFMAs skip the wait states a VALU-written operand needs (<KV8>).
                     using SOp = std::conditional_t<KV8, u32x4, bf16x8>;
                     auto sload = [&](int s) {
                         return *(const LDS_AS SOp*)(Ts + sbase[L::score_base_index(s)] + L::score_delta(s));
@@ -428,8 +430,8 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                             bf16x8 A;
                             if constexpr (KV8) A = fp8x8_to_bf16(sb[s % kPipe][2 * h], sb[s % kPipe][2 * h + 1]);
                             else A = sb[s % kPipe];
-                            if (si == 0) mfma32_first_v(S, A, q[si]);
-                            else mfma32_acc_v(S, A, q[si]);
+                            if (si == 0) mfma32_first_v<KV8>(S, A, q[si]);
+                            else mfma32_acc_v<KV8>(S, A, q[si]);
                             if (h == kMPR - 1 && s + kPipe < kSR) sb[s % kPipe] = sload(s + kPipe);
                         }
                     };
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                             if (a + 2 < 8) ab[a & 1] = aload(a + 2);
                         }
                         const bf16x8 B = lo ? Bl[hb] : Bp[hb];
-                        mfma32_acc_a(O[md][hb], Acur, B);
+                        mfma32_acc_a<KV8>(O[md][hb], Acur, B);
                         // P of token half 1 replaces each operand after its last use in
                         // half 0.
                         if (kk == 0 && md == 3 && lo == (OUT32 ? 1 : 0)) {

@@ -187,23 +187,39 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // inserts none of their wait states, so:
 //   * each starts with two wait states (an operand written by a VALU
 //     instruction right before it is ready: the gfx950 VALU -> MFMA source
-//     requirement);
+//     requirement), unless kWait is false: for operands that come from memory
+//     (LDS or global loads), never from a VALU instruction. A host test
+//     (tests/test_isa_hazards.py) checks the compiled kernels: no VALU
+//     instruction writes a source of such an MFMA within four instructions
+//     before it;
 //   * back-to-back products accumulating into the same registers need none;
 //   * readers (and VALU writers) of a result wait through a settle statement, at least
 //     19 wait states after the last product that wrote it (an 8-pass XDL
 //     write followed by a VALU access needs 11).
+template <bool kWait = true>
 __device__ __forceinline__ void mfma32_first_v(f32x16& c, bf16x8 a, bf16x8 b) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+    if constexpr (kWait)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
 }
+template <bool kWait = true>
 __device__ __forceinline__ void mfma32_acc_v(f32x16& c, bf16x8 a, bf16x8 b) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+    if constexpr (kWait)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 // c = 0 through the matrix core (0 . 0 + 0), so no VALU instruction writes c.
 __device__ __forceinline__ void mfma32_zero_a(f32x16& c, bf16x8 z) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(c) : "v"(z));
 }
+template <bool kWait = true>
 __device__ __forceinline__ void mfma32_acc_a(f32x16& c, bf16x8 a, bf16x8 b) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    if constexpr (kWait)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 // The fp8 score: 32x32x64 e4m3fn x e4m3fn (16 passes), 32 bytes of k per lane.
 __device__ __forceinline__ void mfma32_f8_first_v(f32x16& c, u32x8 a, u32x8 b) {
