@@ -91,6 +91,9 @@ __device__ __forceinline__ void lds_barrier() {
 // kNT sets the non-temporal cache policy: for data read once per launch, so
 // that it does not push out of the caches what is read again (queries shared
 // by a row's pieces, partials the merge reads back).
+// s_add_u32 also writes SCC (its carry): the statement declares it clobbered,
+// or the compiler may keep a comparison's result in SCC across it and branch
+// on the carry (tests/test_isa_scc.py checks the compiled kernels).
 template <int kOff, int kLdsAdd, bool kNT = false>
 __device__ __forceinline__ void dma16_imm(const void* src, uint32_t lds_base) {
     static_assert(kOff >= 0 && kOff < 4096, "13-bit signed immediate offset");
@@ -98,12 +101,12 @@ __device__ __forceinline__ void dma16_imm(const void* src, uint32_t lds_base) {
         asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%3 nt"
                      :
                      : "s"(lds_base), "v"(src), "n"(kLdsAdd - kOff), "n"(kOff)
-                     : "memory", "m0");
+                     : "memory", "m0", "scc");
     else
         asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%3"
                      :
                      : "s"(lds_base), "v"(src), "n"(kLdsAdd - kOff), "n"(kOff)
-                     : "memory", "m0");
+                     : "memory", "m0", "scc");
 }
 
 // 4-byte direct global->LDS load: lane l's dword lands at lds + 4 l. Same
