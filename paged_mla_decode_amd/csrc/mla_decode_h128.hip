@@ -71,10 +71,15 @@ __device__ __forceinline__ void settle_o(f32x16 (&O)[4][4]) {
 // NT: the tile loads carry the non-temporal hint (DecodeArgs::stream_tiles; a
 // parameter of its own, since a branch between the two forms in the loop cost
 // most of what the hint gains).
-template <bool KV8, bool OUT32, int MODE, bool QF8 = false, bool NT = false>
+// PT: every tile lies in one page (page size a power of two of at least 32
+// tokens; chunks start on tile boundaries), plain decode. A tile's page number
+// is one scalar load and its address a wave-uniform base plus a fixed per-lane
+// offset, instead of per-lane page indices staged through LDS.
+template <bool KV8, bool OUT32, int MODE, bool QF8 = false, bool NT = false, bool PT = false>
 __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
     static_assert(!QF8 || (KV8 && !OUT32 && MODE == kModePlain), "fp8 score: fp8 cache, bf16 output, plain decode");
     static_assert(!NT || !KV8, "the hint is for bf16 tiles");
+    static_assert(!PT || MODE == kModePlain, "page-uniform tiles: plain decode");
     constexpr int HS = 4;
     using L = H128Layout<KV8>;
     constexpr int kLoadsMax = (L::kNB + HS - 1) / HS;
@@ -167,20 +172,36 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         // in the row (both layouts), and 1 KiB block b in LDS.
         static_assert(HS % L::kNTB == 0 && (HS / L::kNTB) * L::kCG * 16 == 128, "immediate step");
         struct TileAddr {
-            const uint8_t* rowp;
+            const uint8_t* rowp;  // PT: the wave-uniform base
             uint32_t lds0;
+            uint32_t off;  // PT: this lane's offset from rowp
         };
         auto tile_addr = [&](int tile, int slot) {
+            if constexpr (PT) {
+                // The tile's tokens [t0, t0 + 32) share page t0 >> page_shift; tail
+                // tokens are clamped to the last valid one, as below, and a tile
+                // past the chunk (never issued) to the last tile.
+                const int t0 = kv_begin + min(tile, ntiles - 1) * kTile;
+                const int page = ((const __attribute__((address_space(4))) int32_t*)page_table)[t0 >> a.page_shift];
+                const int tok = min(L::block_token(tb, lane), kv_end - 1 - t0);
+                return TileAddr{a.cache + ((int64_t)page * ps + (t0 & (ps - 1))) * L::kRowBytes + (w / L::kNTB) * L::kCG * 16,
+                                (uint32_t)(uintptr_t)((LDS_AS char*)smem + slot * L::kTileBytes + w * 1024),
+                                (uint32_t)(tok * L::kRowBytes + dma_lane_off)};
+            }
             const int tau = min(kv_begin + tile * kTile + L::block_token(tb, lane), kv_end - 1);
             const int page = idx_ring[slot][w][lane / L::kCG];
             const int row = a.page_shift >= 0 ? (tau & (ps - 1)) : tau % ps;
             return TileAddr{a.cache + ((int64_t)page * ps + row) * L::kRowBytes + dma_lane_off + (w / L::kNTB) * L::kCG * 16,
-                            (uint32_t)(uintptr_t)((LDS_AS char*)smem + slot * L::kTileBytes + w * 1024)};
+                            (uint32_t)(uintptr_t)((LDS_AS char*)smem + slot * L::kTileBytes + w * 1024), 0u};
         };
         auto issue_load = [&](auto ic, const TileAddr& t, auto nt_c) {
             constexpr int i = decltype(ic)::value;
-            if (L::kNB % HS == 0 || w + HS * i < L::kNB)
-                dma16_imm<128 * i, 1024 * HS * i, decltype(nt_c)::value>(t.rowp, t.lds0);
+            if (L::kNB % HS == 0 || w + HS * i < L::kNB) {
+                if constexpr (PT)
+                    dma16_imm_s<128 * i, 1024 * HS * i, decltype(nt_c)::value>(t.rowp, t.off, t.lds0);
+                else
+                    dma16_imm<128 * i, 1024 * HS * i, decltype(nt_c)::value>(t.rowp, t.lds0);
+            }
         };
         auto issue_tile = [&](int tile, int slot) {
             const TileAddr t = tile_addr(tile, slot);
@@ -191,9 +212,11 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         auto wrap = [](int x) { return x >= kStages ? x - kStages : x; };
         // Tile t and its page indices live in slot t % kStages.
         auto prologue_idx = [&] {
+            if constexpr (!PT) {
 #pragma unroll
-            for (int t = 0; t < kAhead; ++t)
-                if (t < ntiles) issue_idx(t, t);
+                for (int t = 0; t < kAhead; ++t)
+                    if (t < ntiles) issue_idx(t, t);
+            }
         };
         // The first tiles: the product at j = 0 reads slot kStages-1 (first
         // loaded at j = 1) and the probability buffer, both zeroed; then the data
@@ -209,7 +232,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
             }
 #pragma unroll
             for (int t = 0; t < kAhead; ++t) {
-                if (t + kAhead < ntiles) issue_idx(t + kAhead, wrap(t + kAhead));
+                if (!PT && t + kAhead < ntiles) issue_idx(t + kAhead, wrap(t + kAhead));
                 if (t < ntiles) issue_tile(t, t);
             }
         };
@@ -245,10 +268,13 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
         // compiled kernels for at least kQLoads loads between the last index load
         // and this wait). The fp8-score instantiation waits for everything: its
         // query loads share the stretch with spill traffic the compiler places.
-        if (QF8 || q_ready)
+        if constexpr (PT) {
+            // No page indices to wait for: the tiles go out behind the query.
+        } else if (QF8 || q_ready) {
             wait_vmcnt<0>();  // (a prefetched query went out long before the indices)
-        else
+        } else {
             wait_vmcnt_query<kQLoads>();
+        }
         q_ready = false;
         if (MODE == kModeAppend && __builtin_amdgcn_readfirstlane(it.flags) & MLA_ITEM_LAST_CHUNK) {
             // Fused append: the request's new row goes to the cache before any
@@ -324,7 +350,7 @@ __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
                             q_ready = true;
                         }
                     }
-                    if (!kLast && j + kIdxAhead < ntiles) issue_idx(j + kIdxAhead, wrap(cur + kIdxAhead % kStages));
+                    if (!PT && !kLast && j + kIdxAhead < ntiles) issue_idx(j + kIdxAhead, wrap(cur + kIdxAhead % kStages));
                     // The data of tile j + kAhead. Issuing a tile's loads stalls each
                     // wave about 550 cycles (per-phase timestamps, V3). With an fp8
                     // cache they go out spread between this iteration's MFMAs below
@@ -699,7 +725,10 @@ int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num
     const int mode = a.c_new ? kModeAppend : a.prefix_lse ? kModeMerge : a.sfx_table ? kModeTree : kModePlain;
     if (a.q8) {
         if (!kv8 || o32 || mode != kModePlain) return (int)hipErrorInvalidValue;
-        decode_h128_kernel<true, false, kModePlain, true><<<grid, block, 0, s>>>(a);
+        if (a.page_shift >= 5)
+            decode_h128_kernel<true, false, kModePlain, true, false, true><<<grid, block, 0, s>>>(a);
+        else
+            decode_h128_kernel<true, false, kModePlain, true><<<grid, block, 0, s>>>(a);
         return (int)hipGetLastError();
     }
     auto go = [&](auto kv8_t, auto o32_t) {
@@ -708,6 +737,8 @@ int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num
         // query row per request); other modes share tiles among rows or do not
         // stream (the suffix merge reads a few slots per row).
         const bool nt = !K && a.stream_tiles;
+        // Page-uniform tiles (plain decode): a power-of-two page of at least 32 tokens.
+        const bool pt = a.page_shift >= 5;
         if (mode == kModeAppend) {
             if (nt)
                 decode_h128_kernel<false, O, kModeAppend, false, true><<<grid, block, 0, s>>>(a);
@@ -718,7 +749,12 @@ int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num
         } else if (mode == kModeMerge) {
             decode_h128_kernel<K, O, kModeMerge><<<grid, block, 0, s>>>(a);
         } else if (nt) {
-            decode_h128_kernel<false, O, kModePlain, false, true><<<grid, block, 0, s>>>(a);
+            if (pt)
+                decode_h128_kernel<false, O, kModePlain, false, true, true><<<grid, block, 0, s>>>(a);
+            else
+                decode_h128_kernel<false, O, kModePlain, false, true><<<grid, block, 0, s>>>(a);
+        } else if (pt) {
+            decode_h128_kernel<K, O, kModePlain, false, false, true><<<grid, block, 0, s>>>(a);
         } else {
             decode_h128_kernel<K, O, kModePlain><<<grid, block, 0, s>>>(a);
         }

@@ -109,6 +109,25 @@ __device__ __forceinline__ void dma16_imm(const void* src, uint32_t lds_base) {
                      : "memory", "m0", "scc");
 }
 
+// dma16_imm with a wave-uniform base address in SGPRs and a 32-bit per-lane
+// offset: lane l's 16 bytes of base + off + kOff land at M0 + kOff + 16 l, as
+// above. For tiles whose tokens share one page, the page's address is uniform
+// and the per-lane part is fixed, so no vector address arithmetic is needed.
+template <int kOff, int kLdsAdd, bool kNT = false>
+__device__ __forceinline__ void dma16_imm_s(const void* base, uint32_t off, uint32_t lds_base) {
+    static_assert(kOff >= 0 && kOff < 4096, "13-bit signed immediate offset");
+    if constexpr (kNT)
+        asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%4 nt"
+                     :
+                     : "s"(lds_base), "v"(off), "s"(base), "n"(kLdsAdd - kOff), "n"(kOff)
+                     : "memory", "m0", "scc");
+    else
+        asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%4"
+                     :
+                     : "s"(lds_base), "v"(off), "s"(base), "n"(kLdsAdd - kOff), "n"(kOff)
+                     : "memory", "m0", "scc");
+}
+
 // 4-byte direct global->LDS load: lane l's dword lands at lds + 4 l. Same
 // ordering rules as dma16_imm.
 __device__ __forceinline__ void dma4(const void* src, LDS_AS void* dst) {

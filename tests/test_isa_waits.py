@@ -6,7 +6,9 @@ Loads retire in issue order, so that wait covers the page indices only if at
 least 36 loads were issued after the last index load. The loads are ordinary
 C++ loads, so their count and placement are the compiler's choice. This test
 compiles the kernel source for gfx950 to assembly (host only, no GPU) and
-checks the invariant at every tagged wait of every instantiation."""
+checks the invariant at every tagged wait of every instantiation. (Kernels whose
+tiles each lie in one page read a scalar page number per tile instead and have
+no such wait.)"""
 import os
 import re
 import subprocess
@@ -38,6 +40,7 @@ def h128_asm(tmp_path_factory):
 def test_query_wait_leaves_only_query_loads_in_flight(h128_asm):
     lines = h128_asm
     kernels, tagged = 0, 0
+    with_idx = set()
     current = None
     for i, line in enumerate(lines):
         m = re.match(r"^(_Z\w*decode_h128_kernel\w*):", line)
@@ -45,6 +48,8 @@ def test_query_wait_leaves_only_query_loads_in_flight(h128_asm):
             current = m.group(1)
             kernels += 1
             continue
+        if current and _IDX.match(line):
+            with_idx.add(current)
         t = _TAG.search(line)
         if not t:
             continue
@@ -62,5 +67,8 @@ def test_query_wait_leaves_only_query_loads_in_flight(h128_asm):
         assert loads >= need, (f"{current}: only {loads} vector loads between the last page-index "
                                f"load and 'vmcnt({need})' (line {i + 1})")
     assert kernels >= 8
-    # every instantiation but the fp8-score one has the tagged wait
-    assert tagged >= kernels - 1, (tagged, kernels)
+    # Every instantiation that stages page indices through LDS has the tagged
+    # wait, but the fp8-score one; those with page-uniform tiles (a scalar load
+    # of one page number per tile) load no page indices and have none.
+    assert len(with_idx) >= 8 and kernels > len(with_idx)
+    assert tagged >= len(with_idx) - 1, (tagged, len(with_idx), kernels)
