@@ -72,14 +72,14 @@ __device__ __forceinline__ void settle_o(f32x16 (&O)[4][4]) {
 // parameter of its own, since a branch between the two forms in the loop cost
 // most of what the hint gains).
 // PT: every tile lies in one page (page size a power of two of at least 32
-// tokens; chunks start on tile boundaries), plain decode. A tile's page number
+// tokens; chunks start on tile boundaries), plain and append decodes. A tile's page number
 // is one scalar load and its address a wave-uniform base plus a fixed per-lane
 // offset, instead of per-lane page indices staged through LDS.
 template <bool KV8, bool OUT32, int MODE, bool QF8 = false, bool NT = false, bool PT = false>
 __global__ __launch_bounds__(256) void decode_h128_kernel(const DecodeArgs a) {
     static_assert(!QF8 || (KV8 && !OUT32 && MODE == kModePlain), "fp8 score: fp8 cache, bf16 output, plain decode");
     static_assert(!NT || !KV8, "the hint is for bf16 tiles");
-    static_assert(!PT || MODE == kModePlain, "page-uniform tiles: plain decode");
+    static_assert(!PT || MODE == kModePlain || MODE == kModeAppend, "page-uniform tiles: plain and append decodes");
     constexpr int HS = 4;
     using L = H128Layout<KV8>;
     constexpr int kLoadsMax = (L::kNB + HS - 1) / HS;
@@ -737,11 +737,16 @@ int launch_decode_h128(int kv_dtype, int out_dtype, const DecodeArgs& a, int num
         // query row per request); other modes share tiles among rows or do not
         // stream (the suffix merge reads a few slots per row).
         const bool nt = !K && a.stream_tiles;
-        // Page-uniform tiles (plain decode): a power-of-two page of at least 32 tokens.
+        // Page-uniform tiles (plain and append decodes): a power-of-two page of at
+        // least 32 tokens.
         const bool pt = a.page_shift >= 5;
         if (mode == kModeAppend) {
-            if (nt)
+            if (nt && pt)
+                decode_h128_kernel<false, O, kModeAppend, false, true, true><<<grid, block, 0, s>>>(a);
+            else if (nt)
                 decode_h128_kernel<false, O, kModeAppend, false, true><<<grid, block, 0, s>>>(a);
+            else if (pt)
+                decode_h128_kernel<K, O, kModeAppend, false, false, true><<<grid, block, 0, s>>>(a);
             else
                 decode_h128_kernel<K, O, kModeAppend><<<grid, block, 0, s>>>(a);
         } else if (mode == kModeTree) {
