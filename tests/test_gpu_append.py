@@ -67,7 +67,7 @@ LENS = [1, 31, 32, 33, 300, 2000]
 
 
 @pytest.mark.parametrize("H", [16, 128])
-@pytest.mark.parametrize("ps", [1, 64])
+@pytest.mark.parametrize("ps", [1, 32, 64])
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
 def test_append_parity(dev, H, ps, kv):
     batch = workloads.random_decode_batch(500 + H + ps, LENS, num_heads=H, page_size=ps, cache_dtype=kv)

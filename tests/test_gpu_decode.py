@@ -200,12 +200,13 @@ def test_many_partials_take_the_wide_merge(dev, H, out_dtype):
 
 
 @pytest.mark.parametrize("H", [16, 128])
-@pytest.mark.parametrize("ps", [128, 1024])
+@pytest.mark.parametrize("ps", [32, 128, 1024])
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
 def test_large_page_sizes(dev, H, ps, kv):
-    """Pages larger than a tile (a 1024-token page holds 32 tiles): the shift
+    """Pages of one tile or larger (a 1024-token page holds 32 tiles): the shift
     branch of the address generation with many tiles per page, partial last
-    pages, and requests shorter than one page."""
+    pages, and requests shorter than one page. At 128 heads these take the
+    page-uniform tile path (one page number per tile), 32 being its smallest page."""
     lens = [1, ps - 1, ps, ps + 1, 3 * ps + 17, 2000]
     batch = workloads.random_decode_batch(330 + H + ps, lens, num_heads=H, page_size=ps, cache_dtype=kv)
     say(f"large page size H={H} ps={ps} kv={kv}")

@@ -136,7 +136,7 @@ def test_quantised_query_bit_exact(dev):
     assert e[0, 0] == 0 and e[1, 3] == 2
 
 
-@pytest.mark.parametrize("ps", [1, 64])
+@pytest.mark.parametrize("ps", [1, 32, 64])
 @pytest.mark.parametrize("num_cus", [4, 0])
 def test_fp8_score_parity(dev, ps, num_cus):
     batch = workloads.random_decode_batch(960 + ps + num_cus, LENS, num_heads=128, page_size=ps,
