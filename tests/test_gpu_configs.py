@@ -20,19 +20,6 @@ def dev():
     return require_gpu()
 
 
-def sampled_requests(batch, k, seed):
-    """The longest and the shortest request plus k-2 others, seeded."""
-    lens = batch.seq_lens
-    rng = np.random.Generator(np.random.PCG64(seed))
-    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
-    others = rng.permutation(batch.batch)
-    for b in others:
-        if len(pick) >= k:
-            break
-        pick.add(int(b))
-    return np.array(sorted(pick), dtype=np.int64)
-
-
 def run_full(batch, dev, out_dtype):
     from paged_mla_decode_amd.decoder import PagedMlaDecoder
     qn, qr, cache, idx = batch_to_device(batch, dev)
