@@ -28,7 +28,9 @@
 // data loads of a tile are issued, an earlier wait has already covered its
 // entries. The loop therefore has no scalar memory loads in flight while it
 // waits on LDS reads (the compiler would make every LDS wait a full wait on
-// them), and no load of its own the compiler could wait on.
+// them), and no load of its own the compiler could wait on. Where every tile
+// lies in one page (PT), a tile's page number is one scalar load at the top of
+// the iteration, consumed before the iteration's first LDS read.
 //
 // Output. After the last tile, the normalised outputs go through LDS (bf16:
 // all 512 columns at once where the ring holds them; fp32: four rounds of 128
