@@ -83,21 +83,25 @@ def test_fp8_cache(dev, H, ps, out_dtype):
     compare(out, lse, ref_out, ref_lse, out_dtype == "fp32", f"fp8 H={H} ps={ps}")
 
 
-def test_kv_lens_clips_on_device(dev):
-    batch = workloads.random_decode_batch(21, [40, 200, 333, 64], num_heads=128, page_size=16)
+@pytest.mark.parametrize("ps", [16, 64])
+def test_kv_lens_clips_on_device(dev, ps):
+    """Device lengths shorter than the plan's (a truncated cascade suffix): whole
+    chunks past the clip, chunks cut inside a tile, and a request clipped to 0.
+    At 64 tokens per page the 128-head kernel takes the page-uniform tiles."""
+    batch = workloads.random_decode_batch(21 + ps, [40, 200, 333, 64], num_heads=128, page_size=ps)
     clip = np.array([17, 200, 100, 0], np.int32)
-    say("kv_lens clip")
+    say(f"kv_lens clip ps={ps}")
     out, lse, _ = run_decode(batch, dev, "bf16", kv_lens=clip, num_cus=4)
     # oracle over the clipped lengths: same pages, fewer tokens
     L = clip
-    npages = (L + 15) // 16
+    npages = (L + ps - 1) // ps
     kv_indptr = np.concatenate([[0], np.cumsum(npages)]).astype(np.int32)
     kv_indices = np.concatenate([batch.kv_indices[batch.kv_indptr[b]:batch.kv_indptr[b] + npages[b]]
                                  for b in range(batch.batch)]).astype(np.int32)
-    last = np.where(L > 0, L - 16 * (npages - 1), 1).astype(np.int32)
+    last = np.where(L > 0, L - ps * (npages - 1), 1).astype(np.int32)
     ref_out, ref_lse = oracle.mla_decode(batch.q_nope, batch.q_rope, batch.cache, kv_indptr,
-                                         kv_indices, 16, batch.sm_scale, kv_last_page_len=last)
-    compare(out, lse, ref_out, ref_lse, False, "kv_lens")
+                                         kv_indices, ps, batch.sm_scale, kv_last_page_len=last)
+    compare(out, lse, ref_out, ref_lse, False, f"kv_lens ps={ps}")
 
 
 def test_empty_requests(dev):
